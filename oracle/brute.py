@@ -1,0 +1,83 @@
+"""Exact rational brute force for tiny inputs (test infrastructure only).
+
+Pure-Python ``fractions.Fraction`` arithmetic: no rounding anywhere.  Used by
+the tests to pin the C oracle's block exponent, FP4 rounding, dequantisation
+and logits on small cases.  It is written from the definitions, separately
+from ``fp4idx_oracle.c`` (decode by table lookup on reshaped pool views, dot
+products as exact rational sums).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+# e2m1 magnitudes by 3-bit code (OCP MX v1.0, FP4 E2M1)
+GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+        Fraction(6)]
+
+
+def exact(x) -> Fraction:
+    """Exact rational value of a finite float."""
+    return Fraction(float(x))
+
+
+def block_exponent(amax) -> int:
+    """Smallest integer e with 6 * 2^e >= amax, clamped to [-127, 127]."""
+    a = exact(amax)
+    if a == 0:
+        return -127
+    e = -127
+    while e < 127 and Fraction(6) * Fraction(2) ** e < a:
+        e += 1
+    return e
+
+
+def e2m1_code(z, e: int) -> int:
+    """Nearest grid magnitude to |z| / 2^e, ties to the even code; sign bit 3."""
+    v = abs(exact(z)) / Fraction(2) ** e
+    best, bd = 0, abs(v - GRID[0])
+    for c in range(1, 8):
+        d = abs(v - GRID[c])
+        if d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    neg = np.signbit(np.float32(z))
+    return best | (8 if neg else 0)
+
+
+def decode_vector(codes64: np.ndarray, scales4: np.ndarray):
+    """128 exact values from 64 packed bytes (low nibble = even element) and
+    4 UE8M0 scale bytes."""
+    out = []
+    for i in range(128):
+        b = int(codes64[i // 2])
+        c = (b >> 4) if (i & 1) else (b & 15)
+        m = GRID[c & 7]
+        if c & 8:
+            m = -m
+        out.append(m * Fraction(2) ** (int(scales4[i // 32]) - 127))
+    return out
+
+
+def pool_token(payload: np.ndarray, scale: np.ndarray, slot: int):
+    """Read one token's 64 + 4 bytes through the page shapes
+    payload [P, 1, 4, 64, 16] and scale [P, 1, 4, 64]."""
+    P = payload.size // 4096
+    pv = payload.reshape(P, 1, 4, 64, 16)
+    sv = scale.reshape(P, 1, 4, 64)
+    page, t = divmod(int(slot), 64)
+    codes = pv[page, 0, :, t, :].reshape(64)
+    sc = sv[page, 0, :, t]
+    return codes, sc
+
+
+def logit(qcodes, qscales, w, kcodes, kscales) -> Fraction:
+    """sum_h w_h * ReLU(qhat_h . khat), exactly.  qcodes [H,64], qscales [H,4]."""
+    kv = decode_vector(kcodes, kscales)
+    total = Fraction(0)
+    for h in range(qcodes.shape[0]):
+        qv = decode_vector(qcodes[h], qscales[h])
+        d = sum((a * b for a, b in zip(qv, kv)), Fraction(0))
+        if d > 0:
+            total += exact(w[h]) * d
+    return total
