@@ -1,0 +1,167 @@
+/*
+ * fp4idx: FP4 lightning-indexer hot path for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Sources, cited by page title and
+ * section:
+ *   [P1] "dsv4.1-amd: KV cache layouts, FP4 indexer, compressor and router
+ *        kernels" (sglang PR 41019)
+ *   [P2] "[AMD] Enable FP4 indexer for Deepseek V4" (sglang PR 37353)
+ *   [P3] "[AMD] DeepSeek-V4.1-Flash on MI350X (gfx950)" (sglang PR 39186)
+ *
+ * Common conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller (device
+ *     memory of the current HIP device).  The library allocates nothing and
+ *     keeps no state between calls apart from a per-device architecture check.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *     is asynchronous on that stream: no host synchronisation, no device reads
+ *     on the host, so calls can be captured in a HIP graph.
+ *   - Argument validation checks host scalars and pointer non-nullness only.
+ *     Values held in device memory (positions, slots, block-table entries,
+ *     context lengths) are the caller's contract: out-of-range device values
+ *     are undefined behaviour (they are documented per call).
+ *   - Return value: FP4IDX_OK (0), or a negative status; on a negative status
+ *     nothing was launched.  fp4idx_status_string() names the status.
+ *   - Sizes and offsets are 64-bit; pools larger than 2 GiB are supported.
+ *   - Fixed geometry: head dim 128, rotary dims = the first 64, 64 tokens per
+ *     page, one UE8M0 scale per 32 elements, e2m1 FP4 codes.
+ *   - Numerics: the two encoders (write_k, pack_q) are bit-exact encodings
+ *     whose fp32 operation order is fixed (see each call); logits are fp32
+ *     with fp32 accumulation; top-k is exact on the logits it is given.
+ */
+#ifndef FP4IDX_H
+#define FP4IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4IDX_OK 0
+#define FP4IDX_E_INVALID (-1)     /* null pointer, bad size, stride or count  */
+#define FP4IDX_E_UNSUPPORTED (-2) /* current device is not gfx950            */
+#define FP4IDX_E_LAUNCH (-3)      /* a HIP runtime call or launch failed      */
+#define FP4IDX_E_WORKSPACE (-4)   /* workspace missing or too small           */
+
+#define FP4IDX_HEAD_DIM 128
+#define FP4IDX_ROPE_DIM 64
+#define FP4IDX_PAGE_TOKENS 64
+#define FP4IDX_PAYLOAD_PAGE_BYTES 4096 /* [1, 4, 64, 16] */
+#define FP4IDX_SCALE_PAGE_BYTES 256    /* [1, 4, 64]     */
+#define FP4IDX_MAX_TOPK 2048
+
+/*
+ * Fused K writer.  [P2] Modifications / fp4_indexer_hip.py and compress.py:
+ * RMSNorm -> RoPE -> Hadamard -> FP4 quantisation -> paged write, fed with
+ * per-forward positions and cache slots, the BF16 RMSNorm weight and the
+ * model's BF16 RoPE cos/sin table; [P2] Motivation: split payload/scale pool.
+ *
+ *   k_bf16       [n_tokens, k_row_stride] bf16 bits; the first 128 of each row
+ *   pos          [n_tokens] int32 RoPE position, 0 <= pos < max_pos
+ *   slot         [n_tokens] int32 pool slot = page*64 + in-page index; a
+ *                negative slot skips the token (padding).  Slots must be
+ *                unique within one call and < num_pages*64.
+ *   norm_w_bf16  [128] bf16 RMSNorm weight g (plain g, not 1+g)
+ *   eps          RMSNorm epsilon (>= 0).  Inputs must keep every intermediate
+ *                finite: with eps = 0 an all-zero (or fully underflowing)
+ *                row divides by zero and its bytes are unspecified.
+ *   cos_sin_bf16 [max_pos, 64] bf16: cos(p*theta_j) in columns 0..31, sin in 32..63
+ *   payload      [num_pages, 1, 4, 64, 16] u8: byte b of block j of in-page
+ *                token t holds elements 32j+2b (low nibble) and 32j+2b+1
+ *   scale        [num_pages, 1, 4, 64] u8: UE8M0 byte of block j of token t
+ *
+ * Per token with slot >= 0, in fp32, exactly this order (no FMA contraction,
+ * correctly rounded sqrt and division, denormals kept):
+ *   x = bf16 row; S = balanced pairwise tree sum of x_i*x_i (T[a,b) =
+ *   T[a,mid) + T[mid,b)); r = 1 / sqrt(S*(1/128) + eps); y_i = (x_i*r)*g_i;
+ *   RoPE on dims 0..63, pairs (j, j+32): y_j = a*c - b*s, y_{j+32} = b*c + a*s;
+ *   fast Walsh-Hadamard, stages h = 1,2,...,64, (u,v) -> (u+v, u-v); times
+ *   C = fp32(128^-1/2); per 32-block: e = smallest integer with 6*2^e >= amax,
+ *   clamped to [-127,127], scale byte e+127; code = nearest e2m1 value to
+ *   z/2^e, ties to even, sign bit kept.
+ * Writes exactly 64 payload bytes + 4 scale bytes per written token and
+ * touches nothing else.
+ */
+int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                   const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                   int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, void* stream);
+
+/*
+ * Index-Q pack + head weights in one launch.  [P1] Summary (one-launch
+ * index-Q pack + head weights); [P2] Attention runtime (indexer Q rotated and
+ * FP4-quantised).
+ *
+ *   q_bf16   [n_rows, q_row_stride] bf16 bits; head h of row t is the 128
+ *            elements at t*q_row_stride + h*128
+ *   n_heads  16, 32, 64 or 128
+ *   pos      [n_rows] int32 RoPE position of each query row, 0 <= pos < max_pos
+ *   w_in     [n_rows, n_heads] fp32 head weights
+ *   q_fp4    [n_rows, n_heads, 64] u8 (out): same nibble order as K
+ *   q_scale  [n_rows, n_heads, 4] u8 (out): UE8M0 per 32-block
+ *   w_out    [n_rows, n_heads] fp32 (out): w_in * w_scale (one rounding)
+ * Per (row, head): the K steps without RMSNorm (RoPE, Hadamard, FP4).
+ */
+int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                  const int32_t* pos, const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in,
+                  float w_scale, uint8_t* q_fp4, uint8_t* q_scale, float* w_out, void* stream);
+
+/*
+ * Paged-MQA FP4 logits.  [P2] Attention runtime (FP4 paged-MQA logits over
+ * the split payload/scale cache, padded rows at zero context); the score is
+ * the lightning-indexer score
+ *     logits[t][s] = sum_h w[t][h] * ReLU( qhat[t][h] . khat[s] )
+ * with qhat, khat the dequantised FP4 vectors (e2m1 * 2^(byte-127)).
+ *
+ *   q_fp4, q_scale, w   as produced by fp4idx_pack_q ([n_rows, n_heads, ...])
+ *   req_row_indptr      [n_reqs+1] int32: rows of request b are
+ *                       [indptr[b], indptr[b+1]); indptr[0] = 0, indptr[n_reqs] = n_rows
+ *   row_ctx_len         [n_rows] int32: row t scores tokens [0, ctx[t]);
+ *                       0 <= ctx[t] <= max_ctx
+ *   block_table         [n_reqs, bt_stride] int32: token s of request b is in
+ *                       page block_table[b*bt_stride + s/64], slot s%64.  Entries
+ *                       for s/64 < ceil(max ctx of b's rows / 64) must be valid
+ *                       page ids < num_pages; later entries are never read.
+ *   logits              [n_rows, logits_stride] fp32 (out); only [0, ctx[t]) of
+ *                       each row is written, the rest is left untouched.
+ *   max_rows_per_req    host bound >= max_b (indptr[b+1]-indptr[b])
+ *   max_ctx             host bound >= max_t ctx[t]; max_ctx <= bt_stride*64 and
+ *                       max_ctx <= logits_stride
+ * Arithmetic: per 16 heads x 16 tokens, one block-scaled FP4 MFMA
+ * (16x16x128) with fp32 accumulation; ReLU and the head weight in fp32; the
+ * head sum in a fixed order.  The result for (t, s) does not depend on the
+ * batch composition, the physical pages or the launch shape.
+ * No workspace is needed: the launch grid covers (request, row group, token
+ * chunk) from the host bounds and idle work-groups exit at once.
+ */
+int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
+                      const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                      const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                      int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
+                      int64_t max_ctx, void* stream);
+
+/*
+ * Top-k over each logits row.  [P3] Changes (sorted top-k selection) and
+ * Historical results (decode top-k ordered by position, not KV slot).
+ *
+ *   logits      [n_rows, logits_stride] fp32; row t uses [0, ctx[t]); finite values
+ *   row_ctx_len [n_rows] int32, 0 <= ctx[t] <= max_ctx <= logits_stride
+ *   k           1 <= k <= FP4IDX_MAX_TOPK
+ *   out_idx     [n_rows, k] int32 (out): the min(k, ctx[t]) positions with the
+ *               largest values (ties: lower position first), ascending by
+ *               position, then -1.  -0.0 and +0.0 compare equal.
+ */
+int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
+                int32_t* out_idx, int64_t max_ctx, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp4idx_status_string(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int fp4idx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4IDX_H */

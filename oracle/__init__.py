@@ -62,8 +62,8 @@ def _load():
         lib.orc_encode_q_head.argtypes = [P, P, P, P]
         lib.orc_write_k.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, P, i64]
         lib.orc_pack_q.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P]
-        lib.orc_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, P]
-        lib.orc_logits_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, P, i64, i64, P, P, P, P]
+        lib.orc_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, P, P]
+        lib.orc_logits_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, P, i64, i64, P, P, P, P, P]
         lib.orc_topk.argtypes = [P, i64, i64, P, i32, P]
         for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk"):
             getattr(lib, name).restype = ctypes.c_int
@@ -198,7 +198,7 @@ def pack_q(q, pos, cos_sin, w_in, w_scale=1.0):
 def logits(q_fp4, q_scale, w, indptr, row_ctx, block_table, payload, scale, logits_stride=None,
            want_f64=False):
     """Full logits [T, stride] (fp32; entries >= ctx stay NaN).  With want_f64
-    also returns the fp64 values and the tolerance reference sum |w| max(d,0)."""
+    also returns the fp64 values, T = sum |w| max(d,0) and A = sum |w| sum |q k|."""
     q_fp4 = _c(q_fp4, np.uint8); q_scale = _c(q_scale, np.uint8); w = _c(w, np.float32)
     indptr = _c(indptr, np.int32); row_ctx = _c(row_ctx, np.int32); bt = _c(block_table, np.int32)
     T, H = q_fp4.shape[0], q_fp4.shape[1]
@@ -207,25 +207,29 @@ def logits(q_fp4, q_scale, w, indptr, row_ctx, block_table, payload, scale, logi
     out = np.full((T, stride), np.nan, np.float32)
     f64 = np.full((T, stride), np.nan, np.float64) if want_f64 else None
     tol = np.full((T, stride), np.nan, np.float64) if want_f64 else None
+    absr = np.full((T, stride), np.nan, np.float64) if want_f64 else None
     rc = _load().orc_logits(_p(q_fp4), _p(q_scale), _p(w), T, H, _p(indptr), len(indptr) - 1, _p(row_ctx),
                             _p(bt), bt.shape[1] if bt.ndim == 2 else bt.size, _p(payload), _p(scale), num_pages,
-                            _p(out), stride, _p(f64) if want_f64 else None, _p(tol) if want_f64 else None)
+                            _p(out), stride, _p(f64) if want_f64 else None, _p(tol) if want_f64 else None,
+                            _p(absr) if want_f64 else None)
     _check(rc, "logits")
-    return (out, f64, tol) if want_f64 else out
+    return (out, f64, tol, absr) if want_f64 else out
 
 
 def logits_sampled(q_fp4, q_scale, w, indptr, block_table, payload, scale, rows, toks):
+    """fp64 logits at (rows[i], toks[i]) with their T and A tolerance scales."""
     q_fp4 = _c(q_fp4, np.uint8); q_scale = _c(q_scale, np.uint8); w = _c(w, np.float32)
     indptr = _c(indptr, np.int32); bt = _c(block_table, np.int32)
     rows = _c(rows, np.int64); toks = _c(toks, np.int64)
     H = q_fp4.shape[1]
     num_pages = payload.size // (PAGE * D // 2)
     out = np.empty(rows.size, np.float64); tol = np.empty(rows.size, np.float64)
+    absr = np.empty(rows.size, np.float64)
     rc = _load().orc_logits_sampled(_p(q_fp4), _p(q_scale), _p(w), H, _p(indptr), len(indptr) - 1, _p(bt),
                                     bt.shape[1], _p(payload), _p(scale), num_pages, rows.size, _p(rows),
-                                    _p(toks), _p(out), _p(tol))
+                                    _p(toks), _p(out), _p(tol), _p(absr))
     _check(rc, "logits_sampled")
-    return out, tol
+    return out, tol, absr
 
 
 def topk(logits_arr, row_ctx, k):

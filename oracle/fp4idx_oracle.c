@@ -328,17 +328,24 @@ static void dequant_token(const uint8_t *payload, const uint8_t *scale, int64_t 
   orc_dequant128(codes, sc, out);
 }
 
+/* Also returns T = sum_h |w_h| max(d_h, 0) and A = sum_h |w_h| sum_i |q_hi k_i|,
+ * the two scales an fp32 evaluation's error is measured against. */
 static double score_one(const double *qd /* [H][D] */, const float *w /* [H] */, int32_t n_heads,
-                        const double *kd, double *tol_ref) {
-  double L = 0.0, T = 0.0;
+                        const double *kd, double *tol_ref, double *abs_ref) {
+  double L = 0.0, T = 0.0, A = 0.0;
   for (int h = 0; h < n_heads; ++h) {
-    double d = 0.0;
-    for (int i = 0; i < D; ++i) d += qd[h * D + i] * kd[i];
+    double d = 0.0, a = 0.0;
+    for (int i = 0; i < D; ++i) {
+      d += qd[h * D + i] * kd[i];
+      a += fabs(qd[h * D + i] * kd[i]);
+    }
     double r = d > 0.0 ? d : 0.0;
     L += (double)w[h] * r;
     T += fabs((double)w[h]) * r;
+    A += fabs((double)w[h]) * a;
   }
   if (tol_ref) *tol_ref = T;
+  if (abs_ref) *abs_ref = A;
   return L;
 }
 
@@ -372,7 +379,8 @@ int orc_logits(const uint8_t *q_fp4, const uint8_t *q_scale, const float *w, int
                int32_t n_heads, const int32_t *indptr, int32_t n_reqs, const int32_t *row_ctx,
                const int32_t *block_table, int32_t bt_stride, const uint8_t *payload,
                const uint8_t *scale, int64_t num_pages, float *logits, int64_t logits_stride,
-               double *logits_f64 /* optional, same layout */, double *tol_ref /* optional */) {
+               double *logits_f64 /* optional, same layout */, double *tol_ref /* optional */,
+               double *abs_ref /* optional */) {
   int rc = check_logits_args(n_rows, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride, num_pages,
                              logits_stride);
   if (rc) return rc;
@@ -386,11 +394,12 @@ int orc_logits(const uint8_t *q_fp4, const uint8_t *q_scale, const float *w, int
     for (int64_t s = 0; s < row_ctx[t]; ++s) {
       int64_t page = block_table[(int64_t)b * bt_stride + s / PAGE];
       dequant_token(payload, scale, page, (int)(s % PAGE), kd);
-      double T;
-      double L = score_one(qd, w + t * n_heads, n_heads, kd, &T);
+      double T, A;
+      double L = score_one(qd, w + t * n_heads, n_heads, kd, &T, &A);
       logits[t * logits_stride + s] = (float)L;
       if (logits_f64) logits_f64[t * logits_stride + s] = L;
       if (tol_ref) tol_ref[t * logits_stride + s] = T;
+      if (abs_ref) abs_ref[t * logits_stride + s] = A;
     }
     free(qd);
   }
@@ -398,11 +407,13 @@ int orc_logits(const uint8_t *q_fp4, const uint8_t *q_scale, const float *w, int
 }
 
 /* Scores for an explicit list of (row, token) pairs, for sampled checks of
- * large problems.  out[i] = fp64 logit, tol_ref[i] = sum |w| max(d,0). */
+ * large problems.  out[i] = fp64 logit, tol_ref[i] = sum |w| max(d,0),
+ * abs_ref[i] = sum |w| sum |q k|. */
 int orc_logits_sampled(const uint8_t *q_fp4, const uint8_t *q_scale, const float *w, int32_t n_heads,
                        const int32_t *indptr, int32_t n_reqs, const int32_t *block_table, int32_t bt_stride,
                        const uint8_t *payload, const uint8_t *scale, int64_t num_pages, int64_t n_samples,
-                       const int64_t *rows, const int64_t *toks, double *out, double *tol_ref) {
+                       const int64_t *rows, const int64_t *toks, double *out, double *tol_ref,
+                       double *abs_ref) {
   if (n_heads <= 0 || n_samples < 0) return -1;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
@@ -417,7 +428,7 @@ int orc_logits_sampled(const uint8_t *q_fp4, const uint8_t *q_scale, const float
     for (int h = 0; h < n_heads; ++h)
       orc_dequant128(q_fp4 + (t * n_heads + h) * (D / 2), q_scale + (t * n_heads + h) * NBLK, qd + h * D);
     dequant_token(payload, scale, page, (int)(s % PAGE), kd);
-    out[i] = score_one(qd, w + t * n_heads, n_heads, kd, &tol_ref[i]);
+    out[i] = score_one(qd, w + t * n_heads, n_heads, kd, &tol_ref[i], &abs_ref[i]);
     free(qd);
   }
   return bad ? -2 : 0;

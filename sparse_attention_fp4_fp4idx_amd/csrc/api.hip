@@ -1,0 +1,123 @@
+// C ABI of the FP4 lightning-indexer library (declared in include/fp4idx.h).
+//
+// Validation looks at host scalars and pointer values only (never at device
+// memory), so every entry point can be captured in a HIP graph.  On any
+// negative status nothing has been launched.
+#include <atomic>
+#include <cstring>
+
+#include "fp4idx.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP4IDX_E_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return FP4IDX_E_UNSUPPORTED;
+  int a = g_arch[dev].load(std::memory_order_relaxed);
+  if (a == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FP4IDX_E_LAUNCH;
+    a = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(a, std::memory_order_relaxed);
+  }
+  return a == 1 ? FP4IDX_OK : FP4IDX_E_UNSUPPORTED;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int launched(hipError_t e) { return e == hipSuccess ? FP4IDX_OK : FP4IDX_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4idx_version(void) { return 100; }
+
+const char* fp4idx_status_string(int status) {
+  switch (status) {
+    case FP4IDX_OK: return "ok";
+    case FP4IDX_E_INVALID: return "invalid argument";
+    case FP4IDX_E_UNSUPPORTED: return "unsupported device (gfx950 required)";
+    case FP4IDX_E_LAUNCH: return "HIP launch or runtime error";
+    case FP4IDX_E_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                   const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                   int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, void* stream) {
+  if (n_tokens < 0 || num_pages < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
+  if (k_row_stride < FP4IDX_HEAD_DIM || (k_row_stride % 8) != 0) return FP4IDX_E_INVALID;
+  if (n_tokens == 0) return FP4IDX_OK;
+  if (!k_bf16 || !pos || !slot || !norm_w_bf16 || !cos_sin_bf16 || !payload || !scale) return FP4IDX_E_INVALID;
+  if (!aligned(k_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
+  if (!(eps >= 0.0f)) return FP4IDX_E_INVALID;
+  if (n_tokens > ((int64_t)0x7FFFFFFF) * 256) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16,
+                                         payload, scale, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                  const int32_t* pos, const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in,
+                  float w_scale, uint8_t* q_fp4, uint8_t* q_scale, float* w_out, void* stream) {
+  if (n_rows < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (q_row_stride < (int64_t)n_heads * FP4IDX_HEAD_DIM || (q_row_stride % 8) != 0) return FP4IDX_E_INVALID;
+  if (n_rows == 0) return FP4IDX_OK;
+  if (!q_bf16 || !pos || !cos_sin_bf16 || !w_in || !q_fp4 || !q_scale || !w_out) return FP4IDX_E_INVALID;
+  if (!aligned(q_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(q_fp4, 16) || !aligned(q_scale, 4))
+    return FP4IDX_E_INVALID;
+  if (n_rows * n_heads > ((int64_t)0x7FFFFFFF) * 256) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, w_in, w_scale,
+                                        q_fp4, q_scale, w_out, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
+                      const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                      const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                      int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
+                      int64_t max_ctx, void* stream) {
+  if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || logits_stride < 0 || max_rows_per_req < 0 ||
+      max_ctx < 0)
+    return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows) return FP4IDX_E_INVALID;
+  if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
+  if (num_pages == 0) return FP4IDX_E_INVALID;
+  if (!q_fp4 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !payload || !scale || !logits)
+    return FP4IDX_E_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_mqa_logits(q_fp4, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+                                            block_table, bt_stride, payload, scale, num_pages, logits, logits_stride,
+                                            max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
+                int32_t* out_idx, int64_t max_ctx, void* stream) {
+  if (n_rows < 0 || logits_stride < 0 || max_ctx < 0 || max_ctx > logits_stride) return FP4IDX_E_INVALID;
+  if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;
+  if (max_ctx > 0x7FFFFFFF) return FP4IDX_E_INVALID;
+  if (n_rows == 0) return FP4IDX_OK;
+  if (!logits || !row_ctx_len || !out_idx) return FP4IDX_E_INVALID;
+  if (n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_topk(logits, n_rows, logits_stride, row_ctx_len, k, out_idx, max_ctx,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

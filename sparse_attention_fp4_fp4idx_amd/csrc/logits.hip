@@ -1,0 +1,298 @@
+// Paged-MQA FP4 logits on gfx950 block-scaled MFMA.
+//
+// Score (DeepSeek lightning indexer, as the FP4 indexer of "[AMD] Enable FP4
+// indexer for Deepseek V4" computes it over the split payload/scale cache):
+//   logits[t][s] = sum_h w[t][h] * ReLU( qhat[t][h] . khat[s] )
+//
+// Work decomposition
+//   work-group (256 threads = 4 waves) = (request, group of up to RW rows,
+//   chunk of 4*PPW pages); wave w takes PPW consecutive pages of the chunk.
+//   Every wave keeps its rows' packed Q (the MFMA A operand) and head weights
+//   in registers and streams K pages: per 16-token tile each lane loads 16
+//   payload bytes (one 128-bit load; the 64 lanes read 4 runs of 256 B) and
+//   one scale byte, straight into the B operand.  D pages are in flight per
+//   wave; the page ids and Q are requested before the context lengths arrive
+//   so the prologue costs one memory latency less.
+//
+// MFMA mapping (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands FP4 e2m1):
+//   A (16 x 128) = 16 heads of one query row; lane l holds head l%16, K
+//   elements 32*(l/16)..+31 and that block's UE8M0 scale (byte mt of a packed
+//   scale register, picked by op_sel).  B (128 x 16) = 16 tokens; lane l holds
+//   token l%16, block l/16, i.e. exactly the 16-byte payload chunk at
+//   [page][block l/16][token][0..15] and the scale byte [page][block][token]:
+//   the page layout feeds the MFMA without any shuffle.
+//   D (16 x 16, fp32): lane l holds token l%16, heads 4*(l/16)+i, i = 0..3.
+// Epilogue per lane and row: for each of the page's 4 tiles, p_t = sum over
+// the row's M-tiles and i of w * ReLU(d) (two fixed-order chains: even and
+// odd M-tiles), then the four lane groups of the four tiles are summed
+// together with two permlane swap steps that leave tile t's total for token
+// l%16 in lane 16*t + l%16, i.e. the page's 64 logits in lane order, stored
+// as one 256-byte row segment.
+// Each (row, token) is computed by exactly one lane in a fixed order, so the
+// result does not depend on batch composition, page placement or grid shape.
+#include "launch.hpp"
+
+namespace fp4idx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int OPA>
+__device__ __forceinline__ v4f mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  // cbsz = blgp = 4: both operands FP4 (e2m1); op_sel picks the scale byte.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 0, (int)sb);
+}
+
+template <int MT>
+__device__ __forceinline__ v4f mfma_tile(uint4 a, uint4 b, uint32_t sa, uint32_t sb) {
+  return mfma_fp4<MT & 3>(a, b, sa, sb);
+}
+
+// ReLU on the bit pattern: every negative float (and -0) is a negative int32,
+// so max(bits, 0) gives +0 for them and leaves non-negative values unchanged.
+// One integer max instead of the quieting and comparing pair fmaxf needs.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum p[j] over the four 16-lane groups; afterwards lane l holds slot
+// (l/16)'s total.  permlane32_swap(a, b): a <- [a.lo32, b.lo32], b <- [a.hi32, b.hi32];
+// permlane16_swap(a, b): swaps rows 1 and 3 of a with rows 0 and 2 of b.
+__device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3) {
+  auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// One page of B operands: 4 tiles of 16 tokens, 16 payload bytes and one
+// scale byte per lane each.
+struct PageRegs {
+  uint4 b[4];
+  uint32_t s[4];
+};
+
+__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ payload,
+                                          const uint8_t* __restrict__ scale, int64_t pid, uint32_t lane_pay,
+                                          uint32_t lane_sc) {
+  const uint8_t* pp = payload + pid * 4096 + lane_pay;
+  const uint8_t* sp = scale + pid * 256 + lane_sc;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    pr.b[t] = ld_stream16(pp + t * 256);
+    pr.s[t] = sp[t * 16];
+  }
+}
+
+// RW rows per wave, NMT = heads/16, PPW pages per wave, D pages in flight.
+// Few rows per wave (decode) means little work per wave: keep at least four
+// waves per SIMD resident so memory latency overlaps; more rows keep their
+// register budget.
+template <int RW, int NMT>
+constexpr int kMinWavesPerSimd = (RW == 1 && NMT <= 4) ? 4 : 1;
+
+template <int RW, int NMT, int PPW, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<RW, NMT>))) void mqa_logits_kernel(
+    const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale, const float* __restrict__ w,
+    const int32_t* __restrict__ indptr, const int32_t* __restrict__ row_ctx, const int32_t* __restrict__ block_table,
+    int32_t bt_stride, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale, int64_t num_pages,
+    float* __restrict__ logits, int64_t logits_stride, int32_t n_groups, int32_t n_chunks) {
+  static_assert(RW >= 1 && RW <= 4, "rows per wave");
+  static_assert(PPW % D == 0, "pages per wave must be a multiple of the prefetch depth");
+  constexpr int H = NMT * 16;
+  constexpr int NSC = (NMT + 3) / 4;  // packed A-scale registers per row
+
+  const int64_t bid = blockIdx.x;
+  const int chunk = (int)(bid % n_chunks);
+  const int64_t rg = bid / n_chunks;
+  const int grp = (int)(rg % n_groups);
+  const int req = (int)(rg / n_groups);
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int page_begin = (chunk * 4 + wave) * PPW;
+  if (page_begin >= bt_stride) return;
+  const int li = lane & 15;  // token within tile (B, D) / head within M-tile (A)
+  const int lg = lane >> 4;  // K block (A, B) / head quad (D)
+  const uint32_t lane_pay = (uint32_t)(lg * 1024 + li * 16);
+  const uint32_t lane_sc = (uint32_t)(lg * 64 + li);
+
+  // Memory round trip 1: the wave's page ids and the request's row range.
+  const int32_t* bt = block_table + (int64_t)req * bt_stride;
+  int32_t pid[PPW];
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) pid[i] = page_begin + i < bt_stride ? bt[page_begin + i] : -1;
+  const int row0 = indptr[req] + grp * RW;
+  const int row_end = indptr[req + 1];
+  if (row0 >= row_end) return;
+  const int nrows = min(RW, row_end - row0);
+
+  // Round trip 2, all in flight together: the first D pages (fetched before
+  // the context lengths say whether they are needed; any table entry outside
+  // [0, num_pages) is never dereferenced), the stationary Q operands and the
+  // context lengths.
+  PageRegs nxt[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    if (pid[i] >= 0 && pid[i] < num_pages) load_page(nxt[i], payload, scale, pid[i], lane_pay, lane_sc);
+
+  uint4 aq[RW][NMT];
+  uint32_t asc[RW][NSC];
+  float wv[RW][NMT][4];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = row0 + (r < nrows ? r : 0);
+#pragma unroll
+    for (int c = 0; c < NSC; ++c) asc[r][c] = 0;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int64_t hrow = (int64_t)row * H + mt * 16 + li;
+      aq[r][mt] = *reinterpret_cast<const uint4*>(q_fp4 + hrow * 64 + lg * 16);
+      asc[r][mt >> 2] |= (uint32_t)q_scale[hrow * 4 + lg] << (8 * (mt & 3));
+      const float4 w4 = *reinterpret_cast<const float4*>(w + (int64_t)row * H + mt * 16 + lg * 4);
+      const bool live = r < nrows;
+      wv[r][mt][0] = live ? w4.x : 0.f;
+      wv[r][mt][1] = live ? w4.y : 0.f;
+      wv[r][mt][2] = live ? w4.z : 0.f;
+      wv[r][mt][3] = live ? w4.w : 0.f;
+    }
+  }
+
+  int ctx_r[4] = {0, 0, 0, 0};
+  int gmax = 0;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    if (r < nrows) ctx_r[r] = row_ctx[row0 + r];
+    gmax = max(gmax, ctx_r[r]);
+  }
+  const int pages_needed = (gmax + 63) >> 6;
+  if (page_begin >= pages_needed) return;
+  const int n_pages = min(PPW, pages_needed - page_begin);
+
+#pragma unroll
+  for (int g0 = 0; g0 < PPW; g0 += D) {
+    if (g0 >= n_pages) break;
+    PageRegs cur[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) cur[i] = nxt[i];
+    if (g0 + D < PPW) {
+#pragma unroll
+      for (int i = 0; i < D; ++i)
+        if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
+          load_page(nxt[i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (g0 + i >= n_pages) break;
+      const int pg = page_begin + g0 + i;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        if (r < nrows) {
+          // partial sums of this lane's 16 heads for the page's 4 tiles
+          float p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v4f d[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+              switch (mt & 3) {
+                case 0: d[mt] = mfma_tile<0>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
+                case 1: d[mt] = mfma_tile<1>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
+                case 2: d[mt] = mfma_tile<2>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
+                default: d[mt] = mfma_tile<3>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
+              }
+            }
+            // two fixed-order chains (even / odd M-tiles), then their sum
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float rl = relu(d[mt][e]);
+                if (mt & 1) acc1 = __builtin_fmaf(wv[r][mt][e], rl, acc1);
+                else acc0 = __builtin_fmaf(wv[r][mt][e], rl, acc0);
+              }
+            }
+            p[t] = acc0 + acc1;
+            // one row per wave: keep a single tile's MFMA results live at a
+            // time (register budget for four waves per SIMD)
+            if (RW == 1) __builtin_amdgcn_sched_barrier(0);
+          }
+          // lane l now gets tile l/16's total for token l%16: 64 consecutive tokens
+          const float tot = reduce4(p[0], p[1], p[2], p[3]);
+          const int tok = pg * 64 + lane;
+          const int c = r == 0 ? ctx_r[0] : r == 1 ? ctx_r[1] : r == 2 ? ctx_r[2] : ctx_r[3];
+          if (tok < c) logits[(int64_t)(row0 + r) * logits_stride + tok] = tot;
+        }
+      }
+    }
+  }
+}
+
+template <int RW, int NMT, int PPW, int D>
+static hipError_t launch_rw(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+                            int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
+                            const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                            int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  const int64_t pages = (max_ctx + 63) / 64;
+  const int32_t n_chunks = (int32_t)((pages + 4 * PPW - 1) / (4 * PPW));
+  const int32_t n_groups = (max_rows_per_req + RW - 1) / RW;
+  const int64_t blocks = (int64_t)n_reqs * n_groups * n_chunks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mqa_logits_kernel<RW, NMT, PPW, D>), dim3((unsigned)blocks), dim3(256), 0, stream, q_fp4, q_scale,
+                     w, indptr, row_ctx, block_table, bt_stride, payload, scale, num_pages, logits, logits_stride,
+                     n_groups, n_chunks);
+  return hipGetLastError();
+}
+
+template <int NMT>
+static hipError_t launch_nmt(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+                             int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
+                             const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                             int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  if (max_rows_per_req <= 1)
+    return launch_rw<1, NMT, 4, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  if (max_rows_per_req == 2)
+    return launch_rw<2, NMT, 4, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  if (max_rows_per_req == 3 || max_rows_per_req == 6)
+    return launch_rw<3, NMT, 4, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  return launch_rw<4, NMT, 4, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                           num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+}
+
+hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
+                             const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                             const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                             const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                             int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  switch (n_heads) {
+    case 16:
+      return launch_nmt<1>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
+                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 32:
+      return launch_nmt<2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
+                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 64:
+      return launch_nmt<4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
+                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 128:
+      return launch_nmt<8>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
+                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fp4idx

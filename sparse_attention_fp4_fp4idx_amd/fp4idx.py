@@ -1,0 +1,193 @@
+"""Thin Python binding of ``libfp4idx.so`` (C ABI in ``include/fp4idx.h``).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the path runs in the library's HIP kernels.
+There is no fallback: if the library is missing or the device is not gfx950
+the calls raise.
+
+Functions carry the C names (``fp4idx_write_k`` ...) and short aliases
+(``write_k`` ...).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4idx.so")
+_lib = None
+
+FP4IDX_OK = 0
+HEAD_DIM = 128
+ROPE_DIM = 64
+PAGE_TOKENS = 64
+PAYLOAD_PAGE_BYTES = 4096
+SCALE_PAGE_BYTES = 256
+MAX_TOPK = 2048
+
+EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk", "fp4idx_status_string",
+           "fp4idx_version")
+
+
+class Fp4idxError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise Fp4idxError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python -m sparse_attention_fp4_fp4idx_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    lib.fp4idx_write_k.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, P, i64, P]
+    lib.fp4idx_pack_q.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
+    lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
+    lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
+    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fp4idx_status_string.argtypes = [ctypes.c_int]
+    lib.fp4idx_status_string.restype = ctypes.c_char_p
+    lib.fp4idx_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().fp4idx_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return int(load().fp4idx_version())
+
+
+def _check(rc: int, what: str):
+    if rc != FP4IDX_OK:
+        raise Fp4idxError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: torch.Tensor, dtypes, name: str):
+    if not t.is_cuda:
+        raise Fp4idxError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise Fp4idxError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.bfloat16, torch.int16)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+
+
+def _rowstride(t: torch.Tensor, name: str) -> int:
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise Fp4idxError(f"{name} must be 2-D (or more) with unit last stride")
+    return int(t.stride(0))
+
+
+def fp4idx_write_k(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor, eps: float,
+                   cos_sin: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
+    """Encode K rows [N, >=128] bf16 and scatter them into the split pool."""
+    if not (pos.is_contiguous() and slot.is_contiguous() and payload.is_contiguous() and scale.is_contiguous()
+            and cos_sin.is_contiguous() and norm_w.is_contiguous()):
+        raise Fp4idxError("write_k: pos, slot, norm_w, cos_sin and the pools must be contiguous")
+    n = int(k.shape[0])
+    if pos.numel() != n or slot.numel() != n:
+        raise Fp4idxError("write_k: pos/slot length must equal the number of K rows")
+    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    if payload.numel() != num_pages * PAYLOAD_PAGE_BYTES or scale.numel() != num_pages * SCALE_PAGE_BYTES:
+        raise Fp4idxError("write_k: pool sizes must be num_pages*4096 and num_pages*256 bytes")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise Fp4idxError("write_k: cos_sin must be [max_pos, 64]")
+    rc = load().fp4idx_write_k(_ptr(k, _BF16, "k"), n, _rowstride(k, "k") if n else HEAD_DIM,
+                               _ptr(pos, _I32, "pos"), _ptr(slot, _I32, "slot"), _ptr(norm_w, _BF16, "norm_w"),
+                               ctypes.c_float(eps), _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]),
+                               _ptr(payload, _U8, "payload"), _ptr(scale, _U8, "scale"), num_pages, _stream(stream))
+    _check(rc, "fp4idx_write_k")
+
+
+def fp4idx_pack_q(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_in: torch.Tensor,
+                  w_scale: float = 1.0, q_fp4: torch.Tensor = None, q_scale: torch.Tensor = None,
+                  w_out: torch.Tensor = None, stream=None):
+    """q: [T, H, 128] bf16 (rows may be strided) -> (q_fp4 [T,H,64] u8, q_scale [T,H,4] u8, w [T,H] f32)."""
+    T, H = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1 or q.stride(1) != HEAD_DIM:
+        raise Fp4idxError("pack_q: q must be [T, H, 128] with heads packed inside a row")
+    dev = q.device
+    q_fp4 = q_fp4 if q_fp4 is not None else torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+    q_scale = q_scale if q_scale is not None else torch.empty((T, H, 4), dtype=torch.uint8, device=dev)
+    w_out = w_out if w_out is not None else torch.empty((T, H), dtype=torch.float32, device=dev)
+    for t, name in ((pos, "pos"), (w_in, "w_in"), (q_fp4, "q_fp4"), (q_scale, "q_scale"), (w_out, "w_out"),
+                    (cos_sin, "cos_sin")):
+        if not t.is_contiguous():
+            raise Fp4idxError(f"pack_q: {name} must be contiguous")
+    rc = load().fp4idx_pack_q(_ptr(q, _BF16, "q"), T, H, int(q.stride(0)) if T else H * HEAD_DIM,
+                              _ptr(pos, _I32, "pos"), _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]),
+                              _ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_fp4, _U8, "q_fp4"),
+                              _ptr(q_scale, _U8, "q_scale"), _ptr(w_out, _F32, "w_out"), _stream(stream))
+    _check(rc, "fp4idx_pack_q")
+    return q_fp4, q_scale, w_out
+
+
+def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor, req_row_indptr: torch.Tensor,
+                      row_ctx: torch.Tensor, block_table: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor,
+                      max_rows_per_req: int, max_ctx: int, logits: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Paged FP4 logits [T, stride] fp32; only [0, ctx[t]) of each row is written."""
+    T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
+    n_reqs = int(req_row_indptr.numel()) - 1
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise Fp4idxError("mqa_logits: block_table must be [n_reqs, stride] with unit inner stride")
+    if logits is None:
+        logits = torch.empty((T, max(1, int(max_ctx))), dtype=torch.float32, device=q_fp4.device)
+    if logits.stride(-1) != 1:
+        raise Fp4idxError("mqa_logits: logits must have unit inner stride")
+    for t, name in ((q_fp4, "q_fp4"), (q_scale, "q_scale"), (w, "w"), (req_row_indptr, "indptr"),
+                    (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale")):
+        if not t.is_contiguous():
+            raise Fp4idxError(f"mqa_logits: {name} must be contiguous")
+    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    rc = load().fp4idx_mqa_logits(_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
+                                  _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs,
+                                  _ptr(row_ctx, _I32, "row_ctx"), _ptr(block_table, _I32, "block_table"),
+                                  int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
+                                  _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"),
+                                  int(logits.stride(0)), int(max_rows_per_req), int(max_ctx), _stream(stream))
+    _check(rc, "fp4idx_mqa_logits")
+    return logits
+
+
+def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int, out_idx: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+    """[T, k] int32: top-k positions per row, ascending, then -1."""
+    T = int(logits.shape[0])
+    if logits.stride(-1) != 1:
+        raise Fp4idxError("topk: logits must have unit inner stride")
+    if out_idx is None:
+        out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
+    if not out_idx.is_contiguous() or not row_ctx.is_contiguous():
+        raise Fp4idxError("topk: out_idx and row_ctx must be contiguous")
+    rc = load().fp4idx_topk(_ptr(logits, _F32, "logits"), T, int(logits.stride(0)), _ptr(row_ctx, _I32, "row_ctx"),
+                            int(k), _ptr(out_idx, _I32, "out_idx"), int(max_ctx), _stream(stream))
+    _check(rc, "fp4idx_topk")
+    return out_idx
+
+
+write_k = fp4idx_write_k
+pack_q = fp4idx_pack_q
+mqa_logits = fp4idx_mqa_logits
+topk = fp4idx_topk

@@ -1,0 +1,90 @@
+"""C ABI checks that need no GPU: the built library loads, exports every
+symbol include/fp4idx.h declares, and rejects bad host arguments with a
+negative status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4idx.h")
+
+
+@pytest.fixture(scope="module")
+def F():
+    from sparse_attention_fp4_fp4idx_amd import fp4idx
+    if not os.path.exists(fp4idx.lib_path()):
+        pytest.fail("libfp4idx.so is not built; run __graft_entry__.build() first")
+    fp4idx.load()
+    return fp4idx
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4idx_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = declared_functions()
+    for n in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(F):
+    lib = ctypes.CDLL(F.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(F.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings_and_version(F):
+    assert F.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert F.status_string(code) != "unknown status"
+    assert F.status_string(-99) == "unknown status"
+    assert F.version() >= 100
+
+
+def test_host_validation_rejects_before_any_launch(F):
+    lib = F.load()
+    E = -1
+    fake = ctypes.c_void_p(0x1000)
+    # write_k: nulls, bad stride, unaligned row pointer, negative eps
+    assert lib.fp4idx_write_k(None, 5, 128, None, None, None, 1e-6, None, 10, None, None, 1, None) == E
+    assert lib.fp4idx_write_k(fake, 5, 100, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1, None) == E
+    assert lib.fp4idx_write_k(ctypes.c_void_p(0x1002), 5, 128, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1,
+                              None) == E
+    assert lib.fp4idx_write_k(fake, 5, 128, fake, fake, fake, -1.0, fake, 10, fake, fake, 1, None) == E
+    assert lib.fp4idx_write_k(fake, -1, 128, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1, None) == E
+    assert lib.fp4idx_write_k(None, 0, 128, None, None, None, 1e-6, None, 10, None, None, 0, None) == 0
+    # pack_q: unsupported head counts, short stride
+    for h in (0, 8, 48, 256):
+        assert lib.fp4idx_pack_q(fake, 2, h, 128 * 64, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
+    assert lib.fp4idx_pack_q(fake, 2, 64, 100, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
+    # logits: ctx bound beyond the block table or the logits row
+    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 4096, 4, 129,
+                                 None) == E
+    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 100, 4, 128,
+                                 None) == E
+    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128, 5, 128,
+                                 None) == E
+    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 40, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128, 4, 128,
+                                 None) == E
+    # top-k: k out of range, ctx bound beyond the row
+    for k in (0, -3, 2049):
+        assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, 10, None) == E
+    assert lib.fp4idx_topk(fake, 1, 100, fake, 16, fake, 101, None) == E
+    # empty problems are a successful no-op
+    assert lib.fp4idx_topk(None, 0, 100, None, 16, None, 10, None) == 0
+    assert lib.fp4idx_mqa_logits(None, None, None, 0, 64, None, 0, None, None, 0, None, None, 0, None, 0, 0, 0,
+                                 None) == 0
+
+
+def test_binding_imports_no_oracle():
+    import sparse_attention_fp4_fp4idx_amd.fp4idx as m
+    src = open(m.__file__).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    for f in os.listdir(os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc", f)).read().lower()

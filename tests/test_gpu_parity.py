@@ -1,0 +1,368 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: encoder bytes (payload, scale, packed Q) and top-k indices bit-exact;
+logits within |gpu - exact| <= 1e-5 * T + 1e-6 * A, where, for each
+(row, token), T = sum_h |w_h| max(d_h, 0) (the quantity the 1e-5 relative
+tolerance refers to) and A = sum_h |w_h| sum_i |q_hi k_i| (the scale of fp32
+accumulation error, which only matters when a head's dot product cancels).
+Inputs come from the seeded generators; expected values from the oracle only.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_fp4_fp4idx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+RTOL, ATOL_A = 1e-5, 1e-6
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from sparse_attention_fp4_fp4idx_amd import fp4idx
+    fp4idx.load()
+    return fp4idx
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16(a):
+    return dev(a.view(np.int16)).view(torch.bfloat16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_logits(gpu, f64, T, A, where=""):
+    err = np.abs(gpu.astype(np.float64) - f64)
+    bound = RTOL * T + ATOL_A * A
+    bad = err > bound
+    assert not bad.any(), f"{where}: {bad.sum()} logits out of tolerance; worst ratio {np.max(err / np.maximum(bound, 1e-300))}"
+
+
+# ---------------------------------------------------------------- K writer
+
+def _write_both(F, orc, k, pos, slot, norm_w, eps, tab, num_pages, k_row_stride=None):
+    pay_o = np.full(num_pages * 4096, 0xA5, np.uint8)
+    sc_o = np.full(num_pages * 256, 0x5A, np.uint8)
+    orc.write_k(k, pos, slot, norm_w, eps, tab, pay_o, sc_o)
+    pay_g = dev(np.full(num_pages * 4096, 0xA5, np.uint8))
+    sc_g = dev(np.full(num_pages * 256, 0x5A, np.uint8))
+    kk = k
+    if k_row_stride is not None and k_row_stride != 128:
+        kk = np.zeros((k.shape[0], k_row_stride), np.uint16)
+        kk[:, :128] = k
+        kt = bf16(kk)[:, :128]
+    else:
+        kt = bf16(kk)
+    F.write_k(kt, dev(pos), dev(slot), bf16(norm_w), eps, bf16(tab), pay_g, sc_g)
+    torch.cuda.synchronize()
+    return pay_o, sc_o, pay_g.cpu().numpy(), sc_g.cpu().numpy()
+
+
+def test_write_k_small_ragged_bit_exact(F, orc):
+    wl = W.small()
+    say("write_k small: tokens", wl.k_new.shape[0], "pages", wl.num_pages)
+    tab = W.rope_table(wl.max_pos)
+    po, so, pg, sg = _write_both(F, orc, wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tab, wl.num_pages)
+    assert np.array_equal(po, pg) and np.array_equal(so, sg)
+
+
+@pytest.mark.parametrize("n", [300, 20000])   # quad-lane and one-lane kernels; neither a multiple of the block
+def test_write_k_edges_strided_skip_extremes(F, orc, n):
+    rng = np.random.default_rng(21)
+    tab = W.rope_table(4096)
+    k = W.bf16_normal(rng, (n, 128))
+    k[0] = 0                                  # all-zero row: amax 0 -> scale byte 0
+    k[1] = W.bf16_from_f32(np.full(128, 3.0, np.float32))
+    k[2, :] = W.bf16_from_f32(rng.standard_normal(128).astype(np.float32) * 1e-30)   # tiny
+    k[3, :] = W.bf16_from_f32(rng.standard_normal(128).astype(np.float32) * 1e30)    # huge
+    pos = rng.integers(0, 4096, n).astype(np.int32)
+    pos[:2] = [0, 4095]
+    pages = (n + 63) // 64 + 2
+    slot = rng.permutation(pages * 64)[:n].astype(np.int32)
+    slot[5] = -1
+    slot[17] = -7
+    for eps in (1e-6, 0.0):
+        sl = slot.copy()
+        if eps == 0.0:
+            sl[[0, 2]] = -1   # zero / underflowing rows: 1/sqrt(0) is outside the finite-value contract
+        po, so, pg, sg = _write_both(F, orc, k, pos, sl, W.norm_weight(rng), eps, tab, pages, k_row_stride=136)
+        assert np.array_equal(po, pg) and np.array_equal(so, sg), eps
+
+
+def test_write_k_bulk_65536_bit_exact(F, orc):
+    wl = W.make(4, with_q=False)
+    say("write_k bulk:", wl.k_new.shape[0], "tokens into", wl.num_pages, "pages")
+    tab = W.rope_table(wl.max_pos)
+    po, so, pg, sg = _write_both(F, orc, wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tab, wl.num_pages)
+    assert np.array_equal(po, pg) and np.array_equal(so, sg)
+
+
+# ---------------------------------------------------------------- Q pack
+
+def _pack_both(F, orc, q, pos, tab, w, w_scale):
+    qo, so, wo = orc.pack_q(q, pos, tab, w, w_scale)
+    qg, sg, wg = F.pack_q(bf16(q), dev(pos), bf16(tab), dev(w), w_scale)
+    torch.cuda.synchronize()
+    return (qo, so, wo), (qg.cpu().numpy(), sg.cpu().numpy(), wg.cpu().numpy())
+
+
+@pytest.mark.parametrize("heads", [64, 16, 32, 128])
+def test_pack_q_small_bit_exact(F, orc, heads):
+    rng = np.random.default_rng(22 + heads)
+    T = 37
+    tab = W.rope_table(1 << 14)
+    q = W.bf16_normal(rng, (T, heads, 128))
+    q[0, 0] = 0
+    pos = rng.integers(0, 1 << 14, T).astype(np.int32)
+    w = rng.uniform(-1, 1, (T, heads)).astype(np.float32)
+    o, g = _pack_both(F, orc, q, pos, tab, w, 0.37)
+    for a, b in zip(o, g):
+        assert np.array_equal(a, b)
+
+
+def test_pack_q_wide_path_edges(F, orc):
+    rng = np.random.default_rng(23)
+    T, heads = 300, 64            # 19,200 vectors: one-lane kernel
+    tab = W.rope_table(1 << 12)
+    q = W.bf16_normal(rng, (T, heads, 128))
+    q[0] = 0
+    q[1, :5] = W.bf16_from_f32(rng.standard_normal((5, 128)).astype(np.float32) * 1e-36)
+    pos = rng.integers(0, 1 << 12, T).astype(np.int32)
+    w = rng.uniform(-1, 1, (T, heads)).astype(np.float32)
+    o, g = _pack_both(F, orc, q, pos, tab, w, 1.0)
+    for a, b in zip(o, g):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_pack_q_full_size_bit_exact(F, orc, cfg):
+    wl = W.make(cfg)
+    say("pack_q", wl.name, "rows", wl.n_rows)
+    tab = W.rope_table(wl.max_pos)
+    o, g = _pack_both(F, orc, wl.q, wl.pos_q, tab, wl.w, wl.w_scale)
+    for a, b in zip(o, g):
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- logits
+
+def _gpu_logits(F, qf, qs, w, wl, payload, scale, stride=None, sentinel=np.nan):
+    T = qf.shape[0]
+    stride = stride or max(1, wl.max_ctx)
+    out = torch.full((T, stride), float(sentinel), dtype=torch.float32, device=DEV)
+    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table),
+                 dev(payload), dev(scale), wl.max_rows_per_req, wl.max_ctx, logits=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _encoded_small(orc, wl):
+    tab = W.rope_table(wl.max_pos)
+    pay = np.zeros(wl.num_pages * 4096, np.uint8)
+    sc = np.zeros(wl.num_pages * 256, np.uint8)
+    orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tab, pay, sc)
+    qf, qs, w = orc.pack_q(wl.q, wl.pos_q, tab, wl.w, wl.w_scale)
+    return qf, qs, w, pay, sc
+
+
+@pytest.mark.parametrize("heads", [64, 16, 128])
+def test_logits_small_mixed_all_scores(F, orc, heads):
+    wl = W.small(heads=heads)
+    qf, qs, w, pay, sc = _encoded_small(orc, wl)
+    stride = wl.max_ctx + 5
+    gpu = _gpu_logits(F, qf, qs, w, wl, pay, sc, stride=stride)
+    ref, f64, T, A = orc.logits(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay, sc,
+                                logits_stride=stride, want_f64=True)
+    for t in range(wl.n_rows):
+        c = wl.row_ctx[t]
+        check_logits(gpu[t, :c], f64[t, :c], T[t, :c], A[t, :c], f"row {t}")
+        assert np.all(np.isnan(gpu[t, c:])), f"row {t}: wrote past its context"
+
+
+def test_logits_rows_per_request_variants(F, orc):
+    """Every row-group shape the launcher picks (1, 2, 3/6, 4+, 16 rows per
+    request) with ragged contexts and a padded zero-context row."""
+    for rows, ctxs in (((1, 1, 1), (64, 1, 200)), ((2, 2), (100, 65)), ((6, 3), (300, 129)),
+                       ((5, 4, 7), (77, 300, 16)), ((16, 1), (250, 90)), ((9, 2), (0, 40))):
+        wl = W.small(seed=sum(rows) + sum(ctxs), rows=rows, ctxs=ctxs)
+        qf, qs, w, pay, sc = _encoded_small(orc, wl)
+        gpu = _gpu_logits(F, qf, qs, w, wl, pay, sc)
+        ref, f64, T, A = orc.logits(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay, sc,
+                                    logits_stride=gpu.shape[1], want_f64=True)
+        for t in range(wl.n_rows):
+            c = wl.row_ctx[t]
+            check_logits(gpu[t, :c], f64[t, :c], T[t, :c], A[t, :c], f"rows {rows} row {t}")
+            assert np.all(np.isnan(gpu[t, c:]))
+
+
+def _random_q(rng, T, H=64):
+    qf = rng.integers(0, 256, (T, H, 64)).astype(np.uint8)
+    qs = rng.integers(124, 129, (T, H, 4)).astype(np.uint8)
+    w = rng.uniform(0, 1, (T, H)).astype(np.float32)
+    return qf, qs, w
+
+
+def _samples(rng, wl, n):
+    rows = rng.integers(0, wl.n_rows, n)
+    ctx = wl.row_ctx[rows].astype(np.int64)
+    keep = ctx > 0
+    rows, ctx = rows[keep], ctx[keep]
+    toks = (rng.random(rows.size) * ctx).astype(np.int64)
+    # every row's first and last token, and tile / page boundaries
+    live = np.nonzero(wl.row_ctx > 0)[0]
+    extra_r = np.concatenate([live, live])
+    extra_t = np.concatenate([np.zeros(live.size, np.int64), wl.row_ctx[live].astype(np.int64) - 1])
+    return np.concatenate([rows, extra_r]), np.concatenate([toks, extra_t])
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_logits_full_size_sampled(F, orc, cfg):
+    """Each workload at its real shape (random FP4 pool and Q codes from the
+    generator) in the launch configuration the bench times; sampled scores
+    against the oracle, and nothing written past any row's context."""
+    wl = W.make(cfg, with_q=False)
+    rng = np.random.default_rng([cfg, 99])
+    pay, sc = W.random_pool(rng, wl.num_pages)
+    qf, qs, w = _random_q(rng, wl.n_rows)
+    say("logits", wl.name, "scores", wl.scores)
+    stride = wl.max_ctx + 3
+    gpu = _gpu_logits(F, qf, qs, w, wl, pay, sc, stride=stride)
+    rows, toks = _samples(rng, wl, 6000)
+    f64, T, A = orc.logits_sampled(qf, qs, w, wl.req_row_indptr, wl.block_table, pay, sc, rows, toks)
+    check_logits(gpu[rows, toks], f64, T, A, wl.name)
+    cols = np.arange(stride)[None, :]
+    assert np.all(np.isnan(gpu[cols >= wl.row_ctx[:, None]]))
+    assert not np.any(np.isnan(gpu[cols < wl.row_ctx[:, None]]))
+
+
+def test_logits_invariant_to_pages_and_batch(F, orc):
+    """Bitwise: permuting physical pages or scoring a request alone gives the
+    same logits ([P3] Historical results: identical across page layouts)."""
+    wl = W.small(seed=31, rows=(3, 6, 1), ctxs=(500, 257, 64))
+    rng = np.random.default_rng(5)
+    pay, sc = W.random_pool(rng, wl.num_pages)
+    qf, qs, w = _random_q(rng, wl.n_rows)
+    base = _gpu_logits(F, qf, qs, w, wl, pay, sc)
+    perm = rng.permutation(wl.num_pages)
+    inv = np.argsort(perm)
+    pay2 = pay.reshape(wl.num_pages, 4096)[perm].reshape(-1)
+    sc2 = sc.reshape(wl.num_pages, 256)[perm].reshape(-1)
+    wl2 = W.small(seed=31, rows=(3, 6, 1), ctxs=(500, 257, 64))
+    wl2.block_table = np.where(wl.block_table >= 0, inv[np.maximum(wl.block_table, 0)], -1).astype(np.int32)
+    moved = _gpu_logits(F, qf, qs, w, wl2, pay2, sc2)
+    assert np.array_equal(np.nan_to_num(base, nan=7.0).view(np.uint32), np.nan_to_num(moved, nan=7.0).view(np.uint32))
+    # request 1 alone
+    b = 1
+    r0, r1 = wl.req_row_indptr[b], wl.req_row_indptr[b + 1]
+    wl3 = W.small(seed=31, rows=(3, 6, 1), ctxs=(500, 257, 64))
+    wl3.req_row_indptr = np.array([0, r1 - r0], np.int32)
+    wl3.row_ctx = wl.row_ctx[r0:r1].copy()
+    wl3.block_table = wl.block_table[b:b + 1].copy()
+    alone = _gpu_logits(F, qf[r0:r1], qs[r0:r1], w[r0:r1], wl3, pay, sc, stride=base.shape[1])
+    assert np.array_equal(np.nan_to_num(base[r0:r1], nan=7.0).view(np.uint32), np.nan_to_num(alone, nan=7.0).view(np.uint32))
+
+
+# ---------------------------------------------------------------- top-k
+
+def _gpu_topk(F, logits, ctx, k):
+    out = F.topk(dev(logits), dev(ctx), k, int(ctx.max(initial=0)))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_topk_edges_and_ties_bit_exact(F, orc):
+    rng = np.random.default_rng(41)
+    T, S = 12, 5000
+    vals = rng.standard_normal((T, S)).astype(np.float32)
+    vals[1] = rng.integers(-3, 4, S).astype(np.float32)            # massive ties
+    vals[2] = 1.5                                                   # all equal
+    vals[3, ::2] = -0.0; vals[3, 1::2] = 0.0                        # signed zeros only
+    vals[4] = np.round(vals[4] * 4) / 4                             # quantised
+    vals[5] = np.abs(vals[5]) * 1e-40                               # subnormals
+    vals[6] = -np.abs(vals[6]) * 1e30                               # large negatives
+    vals[7, 100] = 3e38; vals[7, 200] = -3e38                       # extreme range
+    ctx = np.array([5000, 5000, 5000, 3000, 4999, 2500, 5000, 5000, 0, 100, 2048, 2049], np.int32)
+    for k in (2048, 256, 1, 7):
+        got = _gpu_topk(F, vals, ctx, k)
+        want = orc.topk(vals, ctx, k)
+        assert np.array_equal(got, want), k
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_topk_full_size_bit_exact(F, orc, cfg):
+    wl = W.make(cfg, with_q=False)
+    rng = np.random.default_rng([cfg, 17])
+    T, S = wl.n_rows, wl.max_ctx
+    say("topk", wl.name, "rows", T, "ctx", S)
+    vals = (rng.standard_normal((T, S)) * 20 + 40).astype(np.float32)
+    vals[:, ::97] = np.round(vals[:, ::97])                         # planted ties
+    got = _gpu_topk(F, vals, wl.row_ctx, wl.topk)
+    want = orc.topk(vals, wl.row_ctx, wl.topk)
+    assert np.array_equal(got, want)
+
+
+def test_topk_long_rows_use_global_path(F, orc):
+    rng = np.random.default_rng(43)
+    T, S = 3, 40000
+    vals = rng.standard_normal((T, S)).astype(np.float32)
+    vals[1] = np.round(vals[1] * 8)
+    ctx = np.array([40000, 39000, 35000], np.int32)
+    got = _gpu_topk(F, vals, ctx, 2048)
+    assert np.array_equal(got, orc.topk(vals, ctx, 2048))
+
+
+# ---------------------------------------------------------------- whole chain
+
+def test_chain_small_write_pack_logits_topk(F, orc):
+    """write_k -> pack_q -> logits -> top-k on the GPU against the oracle's
+    chain.  Top-k sets must match exactly on every row whose gap at the k-th
+    value exceeds twice the logits tolerance; other rows must still be a
+    valid top-k of the oracle's values within that tolerance."""
+    wl = W.small(seed=51, rows=(2, 6, 16, 1), ctxs=(3000, 700, 2100, 300), topk=256)
+    tab = W.rope_table(wl.max_pos)
+    # oracle chain
+    pay_o = np.zeros(wl.num_pages * 4096, np.uint8); sc_o = np.zeros(wl.num_pages * 256, np.uint8)
+    orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tab, pay_o, sc_o)
+    qf_o, qs_o, w_o = orc.pack_q(wl.q, wl.pos_q, tab, wl.w, wl.w_scale)
+    ref, f64, T, A = orc.logits(qf_o, qs_o, w_o, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay_o, sc_o,
+                                want_f64=True)
+    top_o = orc.topk(ref, wl.row_ctx, wl.topk)
+    # GPU chain
+    pay_g = torch.zeros(wl.num_pages * 4096, dtype=torch.uint8, device=DEV)
+    sc_g = torch.zeros(wl.num_pages * 256, dtype=torch.uint8, device=DEV)
+    F.write_k(bf16(wl.k_new), dev(wl.pos_new), dev(wl.slot_new), bf16(wl.norm_w), wl.eps, bf16(tab), pay_g, sc_g)
+    qf_g, qs_g, w_g = F.pack_q(bf16(wl.q), dev(wl.pos_q), bf16(tab), dev(wl.w), wl.w_scale)
+    lg = F.mqa_logits(qf_g, qs_g, w_g, dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table), pay_g, sc_g,
+                      wl.max_rows_per_req, wl.max_ctx)
+    top_g = F.topk(lg, dev(wl.row_ctx), wl.topk, wl.max_ctx)
+    torch.cuda.synchronize()
+    assert np.array_equal(pay_g.cpu().numpy(), pay_o) and np.array_equal(sc_g.cpu().numpy(), sc_o)
+    assert np.array_equal(qf_g.cpu().numpy(), qf_o) and np.array_equal(qs_g.cpu().numpy(), qs_o)
+    lgn = lg.cpu().numpy()
+    tg = top_g.cpu().numpy()
+    for t in range(wl.n_rows):
+        c = int(wl.row_ctx[t])
+        check_logits(lgn[t, :c], f64[t, :c], T[t, :c], A[t, :c], f"chain row {t}")
+        K = min(wl.topk, c)
+        sel_g = tg[t, :K]
+        assert np.all(tg[t, K:] == -1) and np.all(np.diff(sel_g) > 0)
+        tol = RTOL * T[t, :c] + ATOL_A * A[t, :c]
+        if K < c:
+            srt = np.sort(f64[t, :c])[::-1]
+            gap = srt[K - 1] - srt[K]
+            if gap > 2 * tol.max():
+                assert np.array_equal(sel_g, top_o[t, :K]), f"row {t}"
+            else:
+                kth = srt[K - 1]
+                assert np.all(f64[t, sel_g] >= kth - 2 * tol.max())
+        else:
+            assert np.array_equal(sel_g, np.arange(c))

@@ -368,7 +368,7 @@ def _tiny_logit_problem(rng, H=3, ctx=(5, 70), rows=(1, 2)):
 def test_logits_against_exact_rational_brute_force(orc):
     rng = np.random.default_rng(16)
     qf, qs, w, indptr, row_ctx, bt, pay, sc = _tiny_logit_problem(rng)
-    out, f64, tol = orc.logits(qf, qs, w, indptr, row_ctx, bt, pay, sc, logits_stride=80, want_f64=True)
+    out, f64, tol, _ = orc.logits(qf, qs, w, indptr, row_ctx, bt, pay, sc, logits_stride=80, want_f64=True)
     for b in range(len(indptr) - 1):
         for t in range(indptr[b], indptr[b + 1]):
             for s in range(row_ctx[t]):
@@ -401,7 +401,7 @@ def test_logits_integer_lut_formulation_agrees(orc):
     form: per block, sum of (2q)(2k) code products times 2^(eq+ek-2)."""
     rng = np.random.default_rng(18)
     qf, qs, w, indptr, row_ctx, bt, pay, sc = _tiny_logit_problem(rng, H=4, ctx=(33,), rows=(2,))
-    out, f64, _ = orc.logits(qf, qs, w, indptr, row_ctx, bt, pay, sc, logits_stride=33, want_f64=True)
+    out, f64, _, _ = orc.logits(qf, qs, w, indptr, row_ctx, bt, pay, sc, logits_stride=33, want_f64=True)
     twice = np.array([0, 1, 2, 3, 4, 6, 8, 12], np.int64)
 
     def ints(codes):
