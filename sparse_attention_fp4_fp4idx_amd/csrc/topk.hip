@@ -7,23 +7,20 @@
 // ascending position order and padded with -1.
 //
 // Rows up to 32768 positions (topk_reg_kernel), one 1024-thread work-group
-// per row:
-//  1. Coalesced load of the row (32 loads in flight per thread), each value
-//     mapped to an order-preserving 32-bit key (-0 folded onto +0).  Every
-//     thread keeps its 32 keys (positions tid + 1024*j) in registers and also
-//     writes them to LDS at padded addresses for step 3.
-//  2. Exact threshold search on the register keys: the key range [lo, hi]
-//     holding the K-th largest key is cut into at most 2048 equal bins (a
-//     shift of the key offset), an LDS histogram of the in-range keys picks
-//     the bin holding the K-th largest, and the range shrinks to that bin.  At
-//     most three rounds reach a single key T; the count above T is tracked.
-//  3. Ordered compaction: thread t reads a contiguous segment of ceil(ctx/1024)
-//     positions back from LDS (one pad word per 32 spreads the reads over the
-//     banks), counts keys > T and == T, one block-wide scan of both counts gives
-//     every thread its output offset, and keys == T are taken in position order
-//     until K.
-// Longer rows (topk_long_kernel) keep the keys in LDS or re-read them from
-// memory, with four waves per row and ballot-based compaction.
+// per row, everything in registers and a few KiB of LDS:
+//  1. Coalesced load of the row; slot j of thread t is position t + 1024 j
+//     (16 or 32 slots), mapped to an order-preserving 32-bit key (-0 folded
+//     onto +0; slots past the row end hold key 0, which no finite value has).
+//  2. Threshold search for the K-th largest key T: one histogram of 2048 bins
+//     linear in value between the row's min and max, then the chosen bin's
+//     keys (typically a handful) are ranked directly; exact key-space rounds
+//     (bins of the key offset) cover bins with more than 256 keys.
+//  3. Ordered compaction: wave ballots write bit masks of the positions with
+//     key > T and key == T; thread t owns the 32 positions of mask word t, one
+//     block scan of the two popcounts gives its output offset, and ties are
+//     taken in position order until K.
+// Longer rows (topk_long_kernel) re-read the logits in each pass, with four
+// waves per row and ballot-based compaction.
 #include "launch.hpp"
 
 namespace fp4idx {
@@ -35,6 +32,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;  // -0 and +0 are the same value
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Value of an order-preserving key (inverse of order_key; -0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
 struct TopkShared {
@@ -237,30 +239,124 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(const float* __
 
 
 constexpr int kRegThreads = 1024;
-constexpr int kRegKeys = 32;
 constexpr int kRegWaves = kRegThreads / 64;
-constexpr int64_t kRegMaxCtx = (int64_t)kRegThreads * kRegKeys;
+constexpr int64_t kRegMaxCtx = 32768;
+constexpr int kCandMax = 256;  // threshold-bin keys ranked directly
 
-__device__ __forceinline__ int lds_pad(int p) { return p + (p >> 5); }
+// DPP controls (gfx9): quad_perm xor 1 / xor 2, row_half_mirror, row_mirror,
+// row_shr:n.
+constexpr int kQpXor1 = 0xB1, kQpXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t u = (uint32_t)__shfl_up((int)v, off);
-    if (lane >= off) v += u;
-  }
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
+// max / min over the 64 lanes (result uniform): DPP within each 16-lane row,
+// then the four row results through scalar reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dppu<kQpXor1>(v));
+  v = max(v, dppu<kQpXor2>(v));
+  v = max(v, dppu<kRowHalfMirror>(v));
+  v = max(v, dppu<kRowMirror>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dppu<kQpXor1>(v));
+  v = min(v, dppu<kQpXor2>(v));
+  v = min(v, dppu<kRowHalfMirror>(v));
+  v = min(v, dppu<kRowMirror>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
+// row (row_shr 1, 2, 4, 8; lanes shifted past the row start read 0), then the
+// totals of the rows below are added.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+  v += dppu<0x111>(v);
+  v += dppu<0x112>(v);
+  v += dppu<0x114>(v);
+  v += dppu<0x118>(v);
+  const uint32_t t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row == 0 ? 0u : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2);
+}
+
+// Exclusive prefix over the block of per-thread values; `part` holds the 16
+// wave totals.  Includes the barrier that publishes them.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, int lane, int wave, uint32_t* part) {
+  const uint32_t incl = wave_incl_scan(v, lane);
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - v;
+#pragma unroll
+  for (int w = 0; w < kRegWaves; ++w) before += w < wave ? part[w] : 0u;
+  return before;
+}
+
+// Picks the bin holding the K-th largest key given counts hist[0, nb) and
+// cnt_above keys above them: thread t owns reversed bins 2t, 2t+1.  Returns
+// the bin; *s_cnt gets the count of keys above it.  Ends with a barrier.
+__device__ __forceinline__ int select_bin(const uint32_t* hist, int nb, int K, int cnt_above, int tid, int lane,
+                                          int wave, uint32_t* part, int32_t& s_bin, int32_t& s_cnt) {
+  const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
+  const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
+  const uint32_t local = c0 + c1;
+  const int before = cnt_above + (int)block_excl_scan(local, lane, wave, part);
+  if (before < K && before + (int)local >= K) {
+    if (before + (int)c0 >= K) {
+      s_bin = b0;
+      s_cnt = before;
+    } else {
+      s_bin = b1;
+      s_cnt = before + (int)c0;
+    }
+  }
+  __syncthreads();
+  return s_bin;
+}
+
+// The need-th largest of the m candidate keys (1 <= need <= m <= kCandMax):
+// *s_T, and *s_gt = how many candidates exceed it.
+__device__ __forceinline__ void rank_candidates(const uint32_t* cand, int m, int need, int tid, uint32_t& s_T,
+                                                int32_t& s_gt) {
+  if (tid < m) {
+    const uint32_t kt = cand[tid];
+    int gt = 0, ge = 0;
+    for (int c0 = 0; c0 < m; c0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u;
+        const uint32_t kc = cand[min(c, m - 1)];
+        gt += (c < m && kc > kt) ? 1 : 0;
+        ge += (c < m && kc >= kt) ? 1 : 0;
+      }
+    }
+    if (gt < need && need <= ge) {
+      s_T = kt;
+      s_gt = gt;
+    }
+  }
+}
+
+// Rows of up to 1024*J positions: slot j of thread t is position t + 1024 j;
+// slots past the row end hold key 0 (no finite value maps to it).
+template <int J>
 __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __restrict__ logits, int64_t stride,
                                                                const int32_t* __restrict__ row_ctx, int k,
                                                                int32_t* __restrict__ out_idx) {
-  extern __shared__ uint32_t lkeys[];  // padded copy of the row's keys
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t wpart[kRegWaves];
+  __shared__ uint32_t gtmask[kRegThreads], eqmask[kRegThreads];  // one bit per position
+  __shared__ uint32_t cand[kCandMax];
+  __shared__ uint32_t part[kRegWaves];
   __shared__ uint32_t wmin[kRegWaves], wmax[kRegWaves];
-  __shared__ int32_t s_bin, s_cnt;
+  __shared__ int32_t s_bin, s_cnt, s_ncand, s_gt;
+  __shared__ uint32_t s_T;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ctx = row_ctx[row];
@@ -272,32 +368,23 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
   }
   const float* src = logits + row * stride;
 
-  // 1. load.  Slot j of this thread is position tid + 1024 j; slots past the
-  //    row's end are skipped wave by wave (jw = slots any lane of the wave uses).
-  const int jw = min(kRegKeys, max(0, (ctx - wave * 64 + kRegThreads - 1) / kRegThreads));
-  float v[kRegKeys];
+  // 1. load (indices clamped into the row: no branches around the loads)
+  float v[J];
+  uint32_t key[J];
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int p = tid + j * kRegThreads;
-    v[j] = 0.0f;
-    if (j < jw) v[j] = p < ctx ? __builtin_nontemporal_load(src + p) : 0.0f;
-  }
-  uint32_t key[kRegKeys];
+  for (int j = 0; j < J; ++j) v[j] = __builtin_nontemporal_load(src + min(tid + j * kRegThreads, ctx - 1));
+  for (int b = tid; b < kBins; b += kRegThreads) hist[b] = 0;
+  if (tid == 0) s_ncand = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int p = tid + j * kRegThreads;
-    key[j] = order_key(v[j]);
-    if (j < jw && p < ctx) {
-      lkeys[lds_pad(p)] = key[j];
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
-    }
+  for (int j = 0; j < J; ++j) {
+    const bool ok = tid + j * kRegThreads < ctx;
+    key[j] = ok ? order_key(v[j]) : 0u;
+    kmin = min(kmin, ok ? key[j] : 0xFFFFFFFFu);
+    kmax = max(kmax, key[j]);
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     wmin[wave] = kmin;
     wmax[wave] = kmax;
@@ -311,93 +398,154 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(const float* __re
   }
   int cnt_above = 0;  // keys > hi
 
-  // 2. threshold search (at most 3 rounds for 32-bit keys; the cap bounds it)
+  // 2. threshold search.
+  // 2a. First cut, linear in value: bin(v) = min(2047, (v - vmin) * 2048 /
+  //     (vmax - vmin)) is monotone in v, so the bin holding the K-th largest
+  //     value holds exactly the keys of a contiguous key interval, and ties
+  //     share a bin.  (Bins linear in the key would be logarithmic in value
+  //     and pile a row onto a few bins.)  Skipped when the value range is not
+  //     a finite positive float.
+  if (lo < hi) {
+    const float vmin = key_value(lo), vmax = key_value(hi);
+    const float vrange = vmax - vmin;
+    const float vscale = (float)kBins / vrange;
+    if (vrange > 0.0f && vrange <= 3.4028234664e38f && vscale <= 3.4028234664e38f) {
+      int bin[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        bin[j] = min(kBins - 1, (int)((v[j] - vmin) * vscale));
+        if (key[j] != 0u) atomicAdd(&hist[bin[j]], 1u);
+      }
+      __syncthreads();
+      const int bsel = select_bin(hist, kBins, K, cnt_above, tid, lane, wave, part, s_bin, s_cnt);
+      const int m = (int)hist[bsel];
+      cnt_above = s_cnt;
+      uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const bool in = key[j] != 0u && bin[j] == bsel;
+        cmin = min(cmin, in ? key[j] : 0xFFFFFFFFu);
+        cmax = max(cmax, in ? key[j] : 0u);
+        if (m <= kCandMax) {
+          const uint64_t mask = __ballot(in);
+          if (mask) {
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            int base = 0;
+            if (lane == leader) base = atomicAdd(&s_ncand, __popcll(mask));
+            base = __shfl(base, leader);
+            if (in) cand[base + __popcll(mask & ((1ull << lane) - 1ull))] = key[j];
+          }
+        }
+      }
+      if (m <= kCandMax) {
+        __syncthreads();
+        rank_candidates(cand, m, K - cnt_above, tid, s_T, s_gt);
+        __syncthreads();
+        cnt_above += s_gt;
+        lo = hi = s_T;
+      } else {
+        // exact key-space rounds below, over the bin's key interval
+        cmin = wave_min_u32(cmin);
+        cmax = wave_max_u32(cmax);
+        if (lane == 0) {
+          wmin[wave] = cmin;
+          wmax[wave] = cmax;
+        }
+        __syncthreads();
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+#pragma unroll
+        for (int w = 0; w < kRegWaves; ++w) {
+          lo = min(lo, wmin[w]);
+          hi = max(hi, wmax[w]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // 2b. Exact key-space rounds over [lo, hi]: cut into at most 2048 bins (a
+  //     shift of the key offset), keep the bin holding the K-th largest; when
+  //     it holds <= kCandMax keys they are ranked directly.
   for (int round = 0; round < 4 && lo < hi; ++round) {
     const uint32_t range = hi - lo;
     const int width = 32 - __clz(range);
     const int shift = width > 11 ? width - 11 : 0;
     const int nb = (int)(range >> shift) + 1;
     for (int b = tid; b < nb; b += kRegThreads) hist[b] = 0;
-    if (tid == 0) {
-      s_bin = nb - 1;
-      s_cnt = cnt_above;
-    }
+    if (tid == 0) s_ncand = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kRegKeys; ++j) {
-      if (j < jw) {
-        const int p = tid + j * kRegThreads;
-        if (p < ctx && key[j] >= lo && key[j] <= hi) atomicAdd(&hist[(key[j] - lo) >> shift], 1u);
-      }
-    }
+    for (int j = 0; j < J; ++j)
+      if (key[j] >= lo && key[j] <= hi) atomicAdd(&hist[(key[j] - lo) >> shift], 1u);
     __syncthreads();
-    // counts from the top bin down; thread t owns reversed bins 2t, 2t+1
-    const int b0 = nb - 1 - 2 * tid, b1 = b0 - 1;
-    const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
-    const uint32_t local = c0 + c1;
-    const uint32_t incl = wave_incl_scan(local, lane);
-    if (lane == 63) wpart[wave] = incl;
-    __syncthreads();
-    int before = cnt_above + (int)(incl - local);
-    for (int w = 0; w < wave; ++w) before += (int)wpart[w];
-    if (before < K && before + (int)local >= K) {
-      if (before + (int)c0 >= K) {
-        s_bin = b0;
-        s_cnt = before;
-      } else {
-        s_bin = b1;
-        s_cnt = before + (int)c0;
-      }
-    }
-    __syncthreads();
-    const uint32_t b = (uint32_t)s_bin;
+    const int b = select_bin(hist, nb, K, cnt_above, tid, lane, wave, part, s_bin, s_cnt);
+    const int m = (int)hist[b];
     cnt_above = s_cnt;
     const uint64_t nlo = (uint64_t)lo + ((uint64_t)b << shift);
     const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
     lo = (uint32_t)nlo;
     hi = (uint32_t)min<uint64_t>(nhi, (uint64_t)hi);
+    if (lo < hi && m <= kCandMax) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const bool in = key[j] >= lo && key[j] <= hi;
+        const uint64_t mask = __ballot(in);
+        if (mask) {
+          const int leader = __ffsll((unsigned long long)mask) - 1;
+          int base = 0;
+          if (lane == leader) base = atomicAdd(&s_ncand, __popcll(mask));
+          base = __shfl(base, leader);
+          if (in) cand[base + __popcll(mask & ((1ull << lane) - 1ull))] = key[j];
+        }
+      }
+      __syncthreads();
+      rank_candidates(cand, m, K - cnt_above, tid, s_T, s_gt);
+      __syncthreads();
+      cnt_above += s_gt;
+      lo = hi = s_T;
+    }
     __syncthreads();  // everyone has read s_bin / hist before the next clear
   }
   const uint32_t T = lo;
   const int need_eq = K - cnt_above;
 
-  // 3. ordered compaction: thread t owns the contiguous segment
-  //    [seg t, seg t + seg), seg = ceil(ctx / 1024) <= 32.
-  const int seg = (ctx + kRegThreads - 1) / kRegThreads;
-  const int p0 = tid * seg;
-  uint32_t sk[kRegKeys];
-  uint32_t n_gt = 0, n_eq = 0;
+  // 3. ordered compaction.  Bit masks of the positions with key > T and
+  //    key == T, one ballot per slot (slot j of wave w covers positions
+  //    1024 j + 64 w .. +63); invalid slots hold key 0 and set no bit.
 #pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int p = p0 + j;
-    sk[j] = 0u;
-    if (j < seg && p < ctx) {
-      sk[j] = lkeys[lds_pad(p)];
-      n_gt += sk[j] > T ? 1u : 0u;
-      n_eq += sk[j] == T ? 1u : 0u;
+  for (int j = 0; j < J; ++j) {
+    const uint64_t g = __ballot(key[j] > T);
+    const uint64_t e = __ballot(key[j] == T);
+    if (lane == 0) {
+      const int wd = 32 * j + 2 * wave;
+      gtmask[wd] = (uint32_t)g;
+      gtmask[wd + 1] = (uint32_t)(g >> 32);
+      eqmask[wd] = (uint32_t)e;
+      eqmask[wd + 1] = (uint32_t)(e >> 32);
     }
   }
-  // one scan of both counts packed in 16-bit halves (each total <= 32768)
-  const uint32_t packed = n_gt | (n_eq << 16);
-  const uint32_t pincl = wave_incl_scan(packed, lane);
-  if (lane == 63) wpart[wave] = pincl;
   __syncthreads();
-  uint32_t pbefore = pincl - packed;
-  for (int w = 0; w < wave; ++w) pbefore += wpart[w];
-  const int gt_before = (int)(pbefore & 0xFFFFu);
-  int eq_seen = (int)(pbefore >> 16);
-  int out = gt_before + min(eq_seen, need_eq);
-#pragma unroll
-  for (int j = 0; j < kRegKeys; ++j) {
-    const int p = p0 + j;
-    if (j < seg && p < ctx) {
-      bool sel = sk[j] > T;
-      if (sk[j] == T) {
-        sel = eq_seen < need_eq;
-        ++eq_seen;
-      }
-      if (sel && out < K) o[out++] = p;
-    }
+  //    Thread t owns the 32 positions of word t: one scan of both counts
+  //    (packed in 16-bit halves), then ties are taken in position order.
+  const bool own = tid < 32 * J;
+  const uint32_t gw = own ? gtmask[tid] : 0u, ew = own ? eqmask[tid] : 0u;
+  const uint32_t packed = (uint32_t)__popc(gw) | ((uint32_t)__popc(ew) << 16);
+  const uint32_t before = block_excl_scan(packed, lane, wave, part);
+  const int gt_before = (int)(before & 0xFFFFu);
+  const int eq_before = (int)(before >> 16);
+  int take = min(max(need_eq - eq_before, 0), __popc(ew));
+  uint32_t sel = gw;
+  uint32_t e = ew;
+  for (; take > 0; --take) {
+    sel |= e & (~e + 1u);  // lowest remaining tie
+    e &= e - 1u;
+  }
+  int out = gt_before + min(eq_before, need_eq);
+  while (sel) {
+    const int b = __ffs(sel) - 1;
+    if (out < K) o[out] = 32 * tid + b;
+    ++out;
+    sel &= sel - 1u;
   }
   for (int i = K + tid; i < k; i += kRegThreads) o[i] = -1;
 }
@@ -406,9 +554,11 @@ hipError_t launch_topk(const float* logits, int64_t n_rows, int64_t logits_strid
                        int32_t* out_idx, int64_t max_ctx, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  if (max_ctx <= kRegMaxCtx) {
-    const size_t lds = (size_t)(max_ctx + max_ctx / 32 + 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(topk_reg_kernel, dim3((unsigned)n_rows), dim3(kRegThreads), lds, stream, logits,
+  if (max_ctx <= kRegMaxCtx / 2) {
+    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits,
+                       logits_stride, row_ctx, k, out_idx);
+  } else if (max_ctx <= kRegMaxCtx) {
+    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits,
                        logits_stride, row_ctx, k, out_idx);
   } else {
     hipLaunchKernelGGL(topk_long_kernel<false>, dim3((unsigned)n_rows), dim3(kTopkThreads),
