@@ -124,6 +124,7 @@ int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64
  *                       page ids < num_pages; later entries are never read.
  *   logits              [n_rows, logits_stride] fp32 (out); only [0, ctx[t]) of
  *                       each row is written, the rest is left untouched.
+ *   n_reqs              at most 65535
  *   max_rows_per_req    host bound >= max_b (indptr[b+1]-indptr[b])
  *   max_ctx             host bound >= max_t ctx[t]; max_ctx <= bt_stride*64 and
  *                       max_ctx <= logits_stride

@@ -4,7 +4,8 @@ Flags: -ffp-contract=off keeps the encoders' fp32 order exact (no FMA
 formation; the logits kernel asks for its FMAs explicitly); packed fp32
 instructions are turned off for the device code; fp32 sqrt/div stay correctly
 rounded (hipcc's default); MFMA results go to ordinary VGPRs (no copies out
-of accumulation registers in the logits epilogue).
+of accumulation registers in the logits epilogue); kernel arguments are
+preloaded into SGPRs (no dependent argument loads in the kernel prologues).
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
+         "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -93,7 +93,7 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
     return FP4IDX_E_INVALID;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
   if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
-  if (max_rows_per_req > n_rows) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
   if (num_pages == 0) return FP4IDX_E_INVALID;
   if (!q_fp4 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !payload || !scale || !logits)

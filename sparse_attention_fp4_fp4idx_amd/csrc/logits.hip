@@ -6,7 +6,8 @@
 //
 // Work decomposition
 //   work-group (256 threads = 4 waves) = (request, group of up to RW rows,
-//   chunk of 4*PPW pages); wave w takes PPW consecutive pages of the chunk.
+//   chunk of 4*PPW pages), a 3-D grid; wave w takes PPW consecutive pages of
+//   the chunk.
 //   Every wave keeps its rows' packed Q (the MFMA A operand) and head weights
 //   in registers and streams K pages: per 16-token tile each lane loads 16
 //   payload bytes (one 128-bit load; the 64 lanes read 4 runs of 256 B) and
@@ -102,21 +103,21 @@ constexpr int kMinWavesPerSimd = (RW == 1 && NMT <= 4) ? 4 : 1;
 
 template <int RW, int NMT, int PPW, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<RW, NMT>))) void mqa_logits_kernel(
-    const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale, const float* __restrict__ w,
-    const int32_t* __restrict__ indptr, const int32_t* __restrict__ row_ctx, const int32_t* __restrict__ block_table,
-    int32_t bt_stride, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale, int64_t num_pages,
-    float* __restrict__ logits, int64_t logits_stride, int32_t n_groups, int32_t n_chunks) {
+    // the first arguments are preloaded into SGPRs: those the prologue needs
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
+    const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
+    int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
+    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride) {
   static_assert(RW >= 1 && RW <= 4, "rows per wave");
   static_assert(PPW % D == 0, "pages per wave must be a multiple of the prefetch depth");
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;  // packed A-scale registers per row
 
-  const int64_t bid = blockIdx.x;
-  const int chunk = (int)(bid % n_chunks);
-  const int64_t rg = bid / n_chunks;
-  const int grp = (int)(rg % n_groups);
-  const int req = (int)(rg / n_groups);
-  const int wave = threadIdx.x >> 6;
+  // grid: x = page chunk, y = row group, z = request (no index arithmetic)
+  const int chunk = blockIdx.x;
+  const int grp = blockIdx.y;
+  const int req = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int page_begin = (chunk * 4 + wave) * PPW;
   if (page_begin >= bt_stride) return;
@@ -125,31 +126,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   const uint32_t lane_pay = (uint32_t)(lg * 1024 + li * 16);
   const uint32_t lane_sc = (uint32_t)(lg * 64 + li);
 
-  // Memory round trip 1: the wave's page ids and the request's row range.
+  // Memory round trip 1: the wave's page ids (one vector load, lane i reads
+  // entry i, clamped into the table) and the request's row range.  No branch
+  // depends on them before the next loads are issued: an empty row group
+  // (row0 >= row_end) loads page 0 and in-range rows, and leaves afterwards.
   const int32_t* bt = block_table + (int64_t)req * bt_stride;
+  const int32_t my_pid = bt[min(page_begin + (lane % PPW), bt_stride - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keep the load issued ahead of the indptr wait
+  const int ip0 = indptr[req], ip1 = indptr[req + 1];
+  const int row0 = ip0 + grp * RW;
+  const int row_end = ip1;
+  const int nrows = max(0, min(RW, row_end - row0));
+  const int row_hi = max(0, row_end - 1);  // a valid row index to clamp to
+
+  // Round trip 2, all in flight together: the context lengths (lane r reads
+  // row r; requested first so they are not queued behind the page traffic),
+  // the first D pages (fetched before the context lengths say whether they
+  // are needed) and the stationary Q operands.
+  // (lane-dependent address: a vector load, so it is issued ahead of the
+  // page loads and, loads retiring in order, waiting for it does not wait
+  // for the pages)
+  const int32_t my_ctx = row_ctx[min(row0 + (lane & 3), row_hi)];
   int32_t pid[PPW];
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) pid[i] = page_begin + i < bt_stride ? bt[page_begin + i] : -1;
-  const int row0 = indptr[req] + grp * RW;
-  const int row_end = indptr[req + 1];
-  if (row0 >= row_end) return;
-  const int nrows = min(RW, row_end - row0);
-
-  // Round trip 2, all in flight together: the first D pages (fetched before
-  // the context lengths say whether they are needed; any table entry outside
-  // [0, num_pages) is never dereferenced), the stationary Q operands and the
-  // context lengths.
+  for (int i = 0; i < PPW; ++i)
+    pid[i] = (nrows > 0 && page_begin + i < bt_stride) ? __builtin_amdgcn_readlane(my_pid, i) : -1;
+  // Branch-free, so all loads issue back to back: an id outside
+  // [0, num_pages) (a table entry past the request's pages, or an empty row
+  // group) reads page 0 instead and its tile is never stored.
   PageRegs nxt[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    if (pid[i] >= 0 && pid[i] < num_pages) load_page(nxt[i], payload, scale, pid[i], lane_pay, lane_sc);
+  for (int i = 0; i < D; ++i) {
+    const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : 0;
+    load_page(nxt[i], payload, scale, pg, lane_pay, lane_sc);
+  }
 
   uint4 aq[RW][NMT];
   uint32_t asc[RW][NSC];
   float wv[RW][NMT][4];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int row = row0 + (r < nrows ? r : 0);
+    const int row = min(row0 + (r < nrows ? r : 0), row_hi);
 #pragma unroll
     for (int c = 0; c < NSC; ++c) asc[r][c] = 0;
 #pragma unroll
@@ -170,11 +187,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   int gmax = 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    if (r < nrows) ctx_r[r] = row_ctx[row0 + r];
+    ctx_r[r] = r < nrows ? __builtin_amdgcn_readlane(my_ctx, r) : 0;
     gmax = max(gmax, ctx_r[r]);
   }
   const int pages_needed = (gmax + 63) >> 6;
-  if (page_begin >= pages_needed) return;
+  if (nrows == 0 || page_begin >= pages_needed) return;
   const int n_pages = min(PPW, pages_needed - page_begin);
 
 #pragma unroll
@@ -243,14 +260,13 @@ static hipError_t launch_rw(const uint8_t* q_fp4, const uint8_t* q_scale, const 
                             const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
                             int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
   const int64_t pages = (max_ctx + 63) / 64;
-  const int32_t n_chunks = (int32_t)((pages + 4 * PPW - 1) / (4 * PPW));
-  const int32_t n_groups = (max_rows_per_req + RW - 1) / RW;
-  const int64_t blocks = (int64_t)n_reqs * n_groups * n_chunks;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mqa_logits_kernel<RW, NMT, PPW, D>), dim3((unsigned)blocks), dim3(256), 0, stream, q_fp4, q_scale,
-                     w, indptr, row_ctx, block_table, bt_stride, payload, scale, num_pages, logits, logits_stride,
-                     n_groups, n_chunks);
+  const int64_t n_chunks = (pages + 4 * PPW - 1) / (4 * PPW);
+  const int64_t n_groups = (max_rows_per_req + RW - 1) / RW;
+  if (n_chunks == 0 || n_groups == 0 || n_reqs == 0) return hipSuccess;
+  if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mqa_logits_kernel<RW, NMT, PPW, D>), dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs),
+                     dim3(256), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q_fp4,
+                     q_scale, w, logits, logits_stride);
   return hipGetLastError();
 }
 
