@@ -9,8 +9,12 @@ compressed tokens, random page tables, top-k 2048).
 Inputs are synthetic and seeded; the page pool is filled before timing by the
 library's own K writer.  Every timed step reads a different copy of the
 inputs (copies total well above the 256 MB last-level cache), so the HBM
-figures are HBM, not cache.  Per-kernel durations come from HIP events
-recorded on the launch stream around each kernel inside the timed region.
+figures are HBM, not cache.  The timed region replays one HIP graph per input
+copy (the step's four launches), as a serving loop would; `--eager` times
+plain launches instead.  Per-kernel durations come from a second pass over the
+same K steps, launched eagerly, where each kernel carries HIP events that its
+own dispatch stamps with its start and end times (fp4idx_time_next_call ->
+hipExtLaunchKernel); they feed the roofline figures.
 
 Prints one JSON line (rank 0).
 """
@@ -38,14 +42,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+def kernel_source_hash() -> str:
+    """Digest of everything the kernels are compiled from (HIP sources, headers, build flags)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files += [os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "build.py"), os.path.join(ROOT, "include", "fp4idx.h")]
+    for f in files:
+        if os.path.isfile(f):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_file: str, workload_key: str):
+def measured_traffic(workload_key: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
+    taken on the current kernel sources (else None)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -53,7 +65,7 @@ def measured_traffic(kernel_file: str, workload_key: str):
         rec = json.load(open(p)).get(workload_key)
     except Exception:
         return None
-    if not rec or rec.get("source_sha") != kernel_source_hash(kernel_file):
+    if not rec or rec.get("source_sha") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -65,10 +77,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode batch 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graph replays")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to defeat the cache)")
+    ap.add_argument("--source-sha", action="store_true", help="print the kernel-source digest and exit")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB mebibytes (a known-size reference for HBM counters)")
     args = ap.parse_args()
+    if args.source_sha:
+        print(kernel_source_hash())
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -131,23 +148,22 @@ def main():
 
     names = ("write_k", "pack_q", "mqa_logits", "topk")
 
-    def step(s, ev=None):
-        def mark(i):
+    def step(s, strm, ev=None):
+        def arm(i):   # events stamped with kernel i's own start / end (hipExtLaunchKernel)
             if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        F.write_k(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"], stream=stream)
-        mark(1)
-        F.pack_q(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=stream)
-        mark(2)
+                F.time_next_call(ev[i][0], ev[i][1])
+        arm(0)
+        F.write_k(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"], stream=strm)
+        arm(1)
+        F.pack_q(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
+        arm(2)
         F.mqa_logits(s["q_fp4"], s["q_scale"], s["w_out"], indptr, ctx, bt, s["payload"], s["scale"],
-                     wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=stream)
-        mark(3)
-        F.topk(s["logits"], ctx, k, wl.max_ctx, out_idx=s["top"], stream=stream)
-        mark(4)
+                     wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=strm)
+        arm(3)
+        F.topk(s["logits"], ctx, k, wl.max_ctx, out_idx=s["top"], stream=strm)
 
     for i in range(args.warmup):
-        step(sets[i % copies])
+        step(sets[i % copies], stream)
     torch.cuda.synchronize()
     if args.calib_copy:
         # reference for rocprofv3 FETCH_SIZE / WRITE_SIZE: reads and writes exactly MB MiB
@@ -158,15 +174,43 @@ def main():
         torch.cuda.synchronize()
         del csrc, cdst
 
-    # ---- timed region: K steps, events around each kernel on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # ---- one HIP graph per input copy: the step's four launches, replayed as one unit
+    graphs = []
+    if not args.eager:
+        cap = torch.cuda.Stream()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(sets[c], torch.cuda.current_stream())
+            graphs.append(g)
+        for c in range(copies):
+            graphs[c].replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K steps (graph replays, or eager launches with --eager), bracketed by synchronize
     torch.cuda.synchronize()
     start = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % copies], evs[i])
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            step(sets[i % copies], stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - start
-    per_kernel_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+
+    # ---- kernel durations: the same K steps launched eagerly on the launch stream, each kernel carrying
+    # HIP events that its own dispatch stamps with its start and end times (no marker packets in between)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+           for _ in range(args.steps)]
+    for row in evs:          # create the HIP events (torch creates them on first record)
+        for a, b in row:
+            a.record(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(sets[i % copies], stream, evs[i])
+    torch.cuda.synchronize()
+    per_kernel_ms = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
                      for j, n in enumerate(names)}
     ms_per_step = elapsed * 1e3 / args.steps
     scores = wl.scores
@@ -183,8 +227,7 @@ def main():
     dom = max(per_kernel_ms, key=per_kernel_ms.get)
     dom_ms = per_kernel_ms[dom]
     achieved = alg[dom] / (dom_ms * 1e-3) / 1e9
-    kfile = {"mqa_logits": "logits.hip", "topk": "topk.hip", "write_k": "encoders.hip", "pack_q": "encoders.hip"}[dom]
-    traffic = measured_traffic(kfile, f"config{args.config}:{dom}")
+    traffic = measured_traffic(f"config{args.config}:{dom}")
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2)}
@@ -217,23 +260,29 @@ def main():
             keep = np.isin(wl.cached_slots // 64, np.fromiter(pages_used, np.int64))
             orc.write_k(kc[keep], wl.cached_pos[keep], wl.cached_slots[keep], wl.norm_w, wl.eps, tabn, pay_np, sc_np)
             del kc
-        # timed: the step on the oracle
-        c0 = time.perf_counter()
-        orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tabn, pay_np, sc_np)
-        c1 = time.perf_counter()
-        qf, qs, wo = orc.pack_q(wl.q[rows], wl.pos_q[rows], tabn, wl.w[rows], wl.w_scale)
-        c2 = time.perf_counter()
-        lg = orc.logits(qf, qs, wo, ind, wl.row_ctx[rows], wl.block_table[:nb], pay_np, sc_np,
-                        logits_stride=wl.max_ctx)
-        c3 = time.perf_counter()
-        orc.topk(np.nan_to_num(lg), wl.row_ctx[rows], k)
-        c4 = time.perf_counter()
-        cpu_s = (c1 - c0) * (n_rows_s / T) + (c4 - c1)
+        # timed: the sampled step on the oracle, repeated until about 10 s of CPU wall time
+        secs = np.zeros(4)
+        reps = 0
+        while reps < 200 and (reps == 0 or secs.sum() < 10.0):
+            c0 = time.perf_counter()
+            orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tabn, pay_np, sc_np)
+            c1 = time.perf_counter()
+            qf, qs, wo = orc.pack_q(wl.q[rows], wl.pos_q[rows], tabn, wl.w[rows], wl.w_scale)
+            c2 = time.perf_counter()
+            lg = orc.logits(qf, qs, wo, ind, wl.row_ctx[rows], wl.block_table[:nb], pay_np, sc_np,
+                            logits_stride=wl.max_ctx)
+            c3 = time.perf_counter()
+            orc.topk(np.nan_to_num(lg), wl.row_ctx[rows], k)
+            c4 = time.perf_counter()
+            secs += (c1 - c0, c2 - c1, c3 - c2, c4 - c3)
+            reps += 1
+        secs /= reps
+        cpu_s = secs[0] * (n_rows_s / T) + secs[1:].sum()
         cpu = {"value": round(s_scores / cpu_s, 1), "unit": "scores/s", "cores": orc.get_threads(), "kind": "oracle",
                "sample": f"{n_rows_s} of {T} rows ({s_scores} scores): the step's K write (pro rata), pack_q, "
-                         f"logits and top-k on the oracle; {cpu_s:.1f}s of CPU wall time",
-               "seconds": {"write_k": round(c1 - c0, 2), "pack_q": round(c2 - c1, 2), "logits": round(c3 - c2, 2),
-                           "topk": round(c4 - c3, 2)}}
+                         f"logits and top-k on the oracle, run {reps} times ({reps * cpu_s:.1f}s of CPU wall time); "
+                         f"value = scores / mean time per run",
+               "seconds_per_run": {n: round(float(v), 4) for n, v in zip(names, secs)}}
         del pay_np, sc_np, lg
 
     out = {
@@ -249,7 +298,7 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 (e2m1 x e2m1, fp32 accumulate); fp32 encoders",
         "data": "synthetic",
-        "config": {"workload": wl.name, "requests": wl.n_reqs, "rows": T, "heads": H, "head_dim": 128,
+        "config": {"workload": wl.name, "launch": "eager" if args.eager else "hip graph per step", "requests": wl.n_reqs, "rows": T, "heads": H, "head_dim": 128,
                    "scores_per_step": scores, "k_write_tokens_per_step": int(wl.k_new.shape[0]), "topk": k,
                    "pool_pages": wl.num_pages, "input_copies": copies},
         "k_write_tokens_per_s": round(wl.k_new.shape[0] / (per_kernel_ms["write_k"] * 1e-3), 1),

@@ -155,6 +155,26 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
                 int32_t* out_idx, int64_t max_ctx, void* stream);
 
+/*
+ * Kernel timing (measurement support, not part of the method).  Arms two HIP
+ * events for the calling thread's next call of fp4idx_write_k, fp4idx_pack_q,
+ * fp4idx_mqa_logits or fp4idx_topk; each of these launches exactly one kernel.
+ * That kernel is then dispatched with hipExtLaunchKernel, which stamps the
+ * events with the dispatch's own start and end times, so
+ * hipEventElapsedTime(start, stop) is the kernel's execution time with no
+ * marker packets in between.
+ *
+ *   start_event, stop_event  hipEvent_t created by the caller with timing
+ *                            enabled, on the device of the next call; either
+ *                            may be NULL.  Ownership stays with the caller.
+ *
+ * The arming belongs to the calling thread and is used up by its next call
+ * whatever that call returns; a call that launches nothing (empty sizes or a
+ * negative status) leaves the events as they were.  Not meant for use under
+ * graph capture.  Returns FP4IDX_OK.
+ */
+int fp4idx_time_next_call(void* start_event, void* stop_event);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp4idx_status_string(int status);
 

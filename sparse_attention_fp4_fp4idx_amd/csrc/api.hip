@@ -9,7 +9,16 @@
 #include "fp4idx.h"
 #include "launch.hpp"
 
+namespace fp4idx {
+thread_local TimingEvents t_timing = {nullptr, nullptr};
+}
+
 namespace {
+
+// Disarms the timing events when an entry point returns, launched or not.
+struct TimingScope {
+  ~TimingScope() { fp4idx::t_timing = {nullptr, nullptr}; }
+};
 
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other architecture
@@ -39,6 +48,11 @@ extern "C" {
 
 int fp4idx_version(void) { return 100; }
 
+int fp4idx_time_next_call(void* start_event, void* stop_event) {
+  fp4idx::t_timing = {static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  return FP4IDX_OK;
+}
+
 const char* fp4idx_status_string(int status) {
   switch (status) {
     case FP4IDX_OK: return "ok";
@@ -53,6 +67,7 @@ const char* fp4idx_status_string(int status) {
 int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
                    const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
                    int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, void* stream) {
+  const TimingScope timing_scope;
   if (n_tokens < 0 || num_pages < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
   if (k_row_stride < FP4IDX_HEAD_DIM || (k_row_stride % 8) != 0) return FP4IDX_E_INVALID;
   if (n_tokens == 0) return FP4IDX_OK;
@@ -69,6 +84,7 @@ int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_strid
 int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
                   const int32_t* pos, const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in,
                   float w_scale, uint8_t* q_fp4, uint8_t* q_scale, float* w_out, void* stream) {
+  const TimingScope timing_scope;
   if (n_rows < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
   if (q_row_stride < (int64_t)n_heads * FP4IDX_HEAD_DIM || (q_row_stride % 8) != 0) return FP4IDX_E_INVALID;
@@ -88,6 +104,7 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
                       const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
                       int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
                       int64_t max_ctx, void* stream) {
+  const TimingScope timing_scope;
   if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || logits_stride < 0 || max_rows_per_req < 0 ||
       max_ctx < 0)
     return FP4IDX_E_INVALID;
@@ -108,6 +125,7 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
 
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
                 int32_t* out_idx, int64_t max_ctx, void* stream) {
+  const TimingScope timing_scope;
   if (n_rows < 0 || logits_stride < 0 || max_ctx < 0 || max_ctx > logits_stride) return FP4IDX_E_INVALID;
   if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;
   if (max_ctx > 0x7FFFFFFF) return FP4IDX_E_INVALID;

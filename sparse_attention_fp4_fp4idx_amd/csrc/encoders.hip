@@ -186,14 +186,12 @@ hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_str
   if (n_tokens == 0) return hipSuccess;
   if (n_tokens < kQuadMaxTokens) {
     const int64_t blocks = (4 * n_tokens + 255) / 256;
-    hipLaunchKernelGGL(write_k_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride,
-                       pos, slot, norm_w, eps, cos_sin, payload, scale);
-    return hipGetLastError();
+    return launch(write_k_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos,
+                  slot, norm_w, eps, cos_sin, payload, scale);
   }
   const int64_t blocks = (n_tokens + 255) / 256;
-  hipLaunchKernelGGL(write_k_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos,
-                     slot, norm_w, eps, cos_sin, payload, scale);
-  return hipGetLastError();
+  return launch(write_k_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos, slot,
+                norm_w, eps, cos_sin, payload, scale);
 }
 
 hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride, const int32_t* pos,
@@ -203,14 +201,12 @@ hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t
   if (n == 0) return hipSuccess;
   if (n < kQuadMaxVectors) {
     const int64_t blocks = (4 * n + 255) / 256;
-    hipLaunchKernelGGL(pack_q_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads,
-                       q_row_stride, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
-    return hipGetLastError();
+    return launch(pack_q_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride,
+                  pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
   }
   const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(pack_q_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride,
-                     pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
-  return hipGetLastError();
+  return launch(pack_q_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride, pos,
+                cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
 }
 
 }  // namespace fp4idx

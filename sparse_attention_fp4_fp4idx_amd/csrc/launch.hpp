@@ -2,10 +2,34 @@
 // argument validation).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fp4idx {
+
+// Events armed by fp4idx_time_next_call() for the calling thread's next entry
+// point call (cleared when that call returns).
+struct TimingEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local TimingEvents t_timing;
+
+// Every kernel of the library is launched through here.  With armed events the
+// launch goes through hipExtLaunchKernel, which stamps the events with the
+// dispatch's own start and end times.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds_bytes, hipStream_t stream,
+                         Args... args) {
+  if (t_timing.start != nullptr || t_timing.stop != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, t_timing.start, t_timing.stop, 0,
+                          static_cast<KArgs>(args)...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, static_cast<KArgs>(args)...);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
                           const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,

@@ -264,10 +264,9 @@ static hipError_t launch_rw(const uint8_t* q_fp4, const uint8_t* q_scale, const 
   const int64_t n_groups = (max_rows_per_req + RW - 1) / RW;
   if (n_chunks == 0 || n_groups == 0 || n_reqs == 0) return hipSuccess;
   if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mqa_logits_kernel<RW, NMT, PPW, D>), dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs),
-                     dim3(256), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q_fp4,
-                     q_scale, w, logits, logits_stride);
-  return hipGetLastError();
+  return launch(mqa_logits_kernel<RW, NMT, PPW, D>, dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs),
+                dim3(256), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q_fp4, q_scale,
+                w, logits, logits_stride);
 }
 
 template <int NMT>

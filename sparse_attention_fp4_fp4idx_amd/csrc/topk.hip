@@ -554,17 +554,14 @@ hipError_t launch_topk(const float* logits, int64_t n_rows, int64_t logits_strid
                        int32_t* out_idx, int64_t max_ctx, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  if (max_ctx <= kRegMaxCtx / 2) {
-    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits,
-                       logits_stride, row_ctx, k, out_idx);
-  } else if (max_ctx <= kRegMaxCtx) {
-    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits,
-                       logits_stride, row_ctx, k, out_idx);
-  } else {
-    hipLaunchKernelGGL(topk_long_kernel<false>, dim3((unsigned)n_rows), dim3(kTopkThreads),
-                       (size_t)kBins * sizeof(uint32_t), stream, logits, logits_stride, row_ctx, k, out_idx);
-  }
-  return hipGetLastError();
+  if (max_ctx <= kRegMaxCtx / 2)
+    return launch(topk_reg_kernel<16>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits, logits_stride,
+                  row_ctx, k, out_idx);
+  if (max_ctx <= kRegMaxCtx)
+    return launch(topk_reg_kernel<32>, dim3((unsigned)n_rows), dim3(kRegThreads), 0, stream, logits, logits_stride,
+                  row_ctx, k, out_idx);
+  return launch(topk_long_kernel<false>, dim3((unsigned)n_rows), dim3(kTopkThreads), kBins * sizeof(uint32_t), stream,
+                logits, logits_stride, row_ctx, k, out_idx);
 }
 
 }  // namespace fp4idx

@@ -26,8 +26,8 @@ PAYLOAD_PAGE_BYTES = 4096
 SCALE_PAGE_BYTES = 256
 MAX_TOPK = 2048
 
-EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk", "fp4idx_status_string",
-           "fp4idx_version")
+EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk", "fp4idx_time_next_call",
+           "fp4idx_status_string", "fp4idx_version")
 
 
 class Fp4idxError(RuntimeError):
@@ -54,6 +54,8 @@ def load():
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.fp4idx_time_next_call.argtypes = [P, P]
+    lib.fp4idx_time_next_call.restype = ctypes.c_int
     lib.fp4idx_status_string.argtypes = [ctypes.c_int]
     lib.fp4idx_status_string.restype = ctypes.c_char_p
     lib.fp4idx_version.restype = ctypes.c_int
@@ -187,7 +189,26 @@ def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: in
     return out_idx
 
 
+def _event_handle(ev):
+    if ev is None:
+        return None
+    h = int(getattr(ev, "cuda_event", ev) or 0)
+    if h == 0:
+        raise Fp4idxError("time_next_call: the event has no HIP event yet (record it once first)")
+    return ctypes.c_void_p(h)
+
+
+def fp4idx_time_next_call(start_event, stop_event) -> None:
+    """Arm two timing events (torch.cuda.Event with enable_timing=True, already
+    recorded once so that the HIP event exists, or raw hipEvent_t handles) for
+    this thread's next write_k / pack_q / mqa_logits / topk call: they receive
+    that call's kernel start and end timestamps."""
+    _check(load().fp4idx_time_next_call(_event_handle(start_event), _event_handle(stop_event)),
+           "fp4idx_time_next_call")
+
+
 write_k = fp4idx_write_k
 pack_q = fp4idx_pack_q
 mqa_logits = fp4idx_mqa_logits
 topk = fp4idx_topk
+time_next_call = fp4idx_time_next_call

@@ -76,6 +76,10 @@ def test_host_validation_rejects_before_any_launch(F):
     for k in (0, -3, 2049):
         assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, 10, None) == E
     assert lib.fp4idx_topk(fake, 1, 100, fake, 16, fake, 101, None) == E
+    # timing events armed before a rejected call are dropped with it (no launch, events untouched)
+    assert lib.fp4idx_time_next_call(None, None) == 0
+    assert lib.fp4idx_time_next_call(fake, fake) == 0
+    assert lib.fp4idx_topk(fake, 1, 100, fake, 0, fake, 10, None) == E
     # empty problems are a successful no-op
     assert lib.fp4idx_topk(None, 0, 100, None, 16, None, 10, None) == 0
     assert lib.fp4idx_mqa_logits(None, None, None, 0, 64, None, 0, None, None, 0, None, None, 0, None, 0, 0, 0,

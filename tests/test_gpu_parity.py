@@ -366,3 +366,83 @@ def test_chain_small_write_pack_logits_topk(F, orc):
                 assert np.all(f64[t, sel_g] >= kth - 2 * tol.max())
         else:
             assert np.array_equal(sel_g, np.arange(c))
+
+
+# ---------------------------------------------------------------- kernel timing hook
+
+def test_time_next_call_stamps_kernel_and_keeps_results(F, orc):
+    """Armed timing events go to the next call's kernel only; the call's result
+    is unchanged and the arming is used up by that call."""
+    rng = np.random.default_rng(47)
+    vals = rng.standard_normal((9, 3000)).astype(np.float32)
+    ctx = np.array([3000, 2999, 1, 0, 2048, 2049, 100, 3000, 1500], np.int32)
+    want = orc.topk(vals, ctx, 2048)
+    lg, cx = dev(vals), dev(ctx)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    F.time_next_call(ev[0], ev[1])
+    a = F.topk(lg, cx, 2048, 3000)
+    b = F.topk(lg, cx, 2048, 3000)           # not timed: the arming was used up
+    F.time_next_call(ev[2], ev[3])
+    c = F.topk(lg, cx, 2048, 3000)
+    torch.cuda.synchronize()
+    for got in (a, b, c):
+        assert np.array_equal(got.cpu().numpy(), want)
+    t1, t2 = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    say("topk kernel ms", t1, t2)
+    assert 0.0 < t1 < 100.0 and 0.0 < t2 < 100.0
+
+
+# ---------------------------------------------------------------- HIP graph capture
+
+def test_chain_graph_replays_match_eager(F):
+    """The four calls captured in one HIP graph: every replay, with eager work
+    and synchronisation between replays, reproduces the eager results exactly
+    (pool bytes, packed Q, logits bits, top-k)."""
+    wl = W.small(seed=53, rows=(3, 1, 8), ctxs=(2500, 900, 4100), topk=512)
+    tab = bf16(W.rope_table(wl.max_pos))
+    ins = dict(k=bf16(wl.k_new), pos=dev(wl.pos_new), slot=dev(wl.slot_new), nw=bf16(wl.norm_w), q=bf16(wl.q),
+               pq=dev(wl.pos_q), w=dev(wl.w), ind=dev(wl.req_row_indptr), ctx=dev(wl.row_ctx), bt=dev(wl.block_table))
+    T, H = wl.n_rows, wl.heads
+
+    def outs():
+        return dict(pay=torch.zeros(wl.num_pages * 4096, dtype=torch.uint8, device=DEV),
+                    sc=torch.zeros(wl.num_pages * 256, dtype=torch.uint8, device=DEV),
+                    qf=torch.empty((T, H, 64), dtype=torch.uint8, device=DEV),
+                    qs=torch.empty((T, H, 4), dtype=torch.uint8, device=DEV),
+                    wo=torch.empty((T, H), dtype=torch.float32, device=DEV),
+                    lg=torch.full((T, wl.max_ctx), -7.0, dtype=torch.float32, device=DEV),
+                    top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV))
+
+    def chain(o, strm):
+        F.write_k(ins["k"], ins["pos"], ins["slot"], ins["nw"], wl.eps, tab, o["pay"], o["sc"], stream=strm)
+        F.pack_q(ins["q"], ins["pq"], tab, ins["w"], wl.w_scale, o["qf"], o["qs"], o["wo"], stream=strm)
+        F.mqa_logits(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"],
+                     wl.max_rows_per_req, wl.max_ctx, logits=o["lg"], stream=strm)
+        F.topk(o["lg"], ins["ctx"], wl.topk, wl.max_ctx, out_idx=o["top"], stream=strm)
+
+    ref = outs()
+    chain(ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = {n: v.cpu() for n, v in ref.items()}
+
+    o = outs()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        chain(o, torch.cuda.current_stream())
+    for rep in range(4):
+        for n in ("pay", "sc", "qf", "qs", "wo", "top"):   # eager work between replays
+            o[n].zero_()
+        o["lg"].fill_(-7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, v in want.items():
+            got = o[n].cpu()
+            if n in ("wo", "lg"):
+                assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (rep, n)
+            else:
+                assert torch.equal(got, v), (rep, n)
