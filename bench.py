@@ -10,8 +10,9 @@ Inputs are synthetic and seeded; the page pool is filled before timing by the
 library's own K writer.  Every timed step reads a different copy of the
 inputs (copies total well above the 256 MB last-level cache), so the HBM
 figures are HBM, not cache.  The timed region replays one HIP graph per input
-copy (the step's four launches), as a serving loop would; `--eager` times
-plain launches instead.  Per-kernel durations come from a second pass over the
+copy (the step's four launches in sequence; capturing the independent K
+write and Q pack as two parallel branches measured slower), as a serving
+loop would; `--eager` times plain launches instead.  Per-kernel durations come from a second pass over the
 same K steps, launched eagerly, where each kernel carries HIP events that its
 own dispatch stamps with its start and end times (fp4idx_time_next_call ->
 hipExtLaunchKernel); they feed the roofline figures.

@@ -310,6 +310,23 @@ def test_topk_full_size_bit_exact(F, orc, cfg):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("rows,max_ctx", [(300, 8000), (300, 12000), (300, 16000), (300, 18000), (300, 24000),
+                                          (300, 30000), (40, 20000), (40, 30000)])
+def test_topk_every_register_variant_bit_exact(F, orc, rows, max_ctx):
+    """Row counts on both sides of the 1024- / 512-thread switch and row
+    lengths in every register band; ragged rows (including ctx 0, ctx < k,
+    ctx = k, ctx = k + 1), planted ties and a crowded row."""
+    rng = np.random.default_rng([rows, max_ctx])
+    vals = (rng.standard_normal((rows, max_ctx)) * 10).astype(np.float32)
+    vals[:, ::61] = np.round(vals[:, ::61])                          # ties
+    vals[3] = rng.integers(-2, 3, max_ctx).astype(np.float32)        # crowded bins
+    ctx = rng.integers(max_ctx // 2, max_ctx + 1, rows).astype(np.int32)
+    ctx[:4] = [0, 1000, 2048, 2049]
+    ctx[-1] = max_ctx
+    got = _gpu_topk(F, vals, ctx, 2048)
+    assert np.array_equal(got, orc.topk(vals, ctx, 2048))
+
+
 def test_topk_long_rows_use_global_path(F, orc):
     rng = np.random.default_rng(43)
     T, S = 3, 40000
@@ -398,9 +415,10 @@ def test_time_next_call_stamps_kernel_and_keeps_results(F, orc):
 # ---------------------------------------------------------------- HIP graph capture
 
 def test_chain_graph_replays_match_eager(F):
-    """The four calls captured in one HIP graph: every replay, with eager work
-    and synchronisation between replays, reproduces the eager results exactly
-    (pool bytes, packed Q, logits bits, top-k)."""
+    """The four calls captured in one HIP graph (in sequence, and with the K
+    write on a parallel branch as the benchmark captures it): every replay,
+    with eager work and synchronisation between replays, reproduces the eager
+    results exactly (pool bytes, packed Q, logits bits, top-k)."""
     wl = W.small(seed=53, rows=(3, 1, 8), ctxs=(2500, 900, 4100), topk=512)
     tab = bf16(W.rope_table(wl.max_pos))
     ins = dict(k=bf16(wl.k_new), pos=dev(wl.pos_new), slot=dev(wl.slot_new), nw=bf16(wl.norm_w), q=bf16(wl.q),
@@ -416,9 +434,19 @@ def test_chain_graph_replays_match_eager(F):
                     lg=torch.full((T, wl.max_ctx), -7.0, dtype=torch.float32, device=DEV),
                     top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV))
 
-    def chain(o, strm):
-        F.write_k(ins["k"], ins["pos"], ins["slot"], ins["nw"], wl.eps, tab, o["pay"], o["sc"], stream=strm)
+    def chain(o, strm, side=None):
+        kw = strm
+        if side is not None:   # K write on a parallel branch, joined before the logits
+            fork = torch.cuda.Event()
+            fork.record(strm)
+            side.wait_event(fork)
+            kw = side
+        F.write_k(ins["k"], ins["pos"], ins["slot"], ins["nw"], wl.eps, tab, o["pay"], o["sc"], stream=kw)
         F.pack_q(ins["q"], ins["pq"], tab, ins["w"], wl.w_scale, o["qf"], o["qs"], o["wo"], stream=strm)
+        if side is not None:
+            join = torch.cuda.Event()
+            join.record(side)
+            strm.wait_event(join)
         F.mqa_logits(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"],
                      wl.max_rows_per_req, wl.max_ctx, logits=o["lg"], stream=strm)
         F.topk(o["lg"], ins["ctx"], wl.topk, wl.max_ctx, out_idx=o["top"], stream=strm)
@@ -428,21 +456,22 @@ def test_chain_graph_replays_match_eager(F):
     torch.cuda.synchronize()
     want = {n: v.cpu() for n, v in ref.items()}
 
-    o = outs()
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    with torch.cuda.graph(g, stream=cap):
-        chain(o, torch.cuda.current_stream())
-    for rep in range(4):
-        for n in ("pay", "sc", "qf", "qs", "wo", "top"):   # eager work between replays
-            o[n].zero_()
-        o["lg"].fill_(-7.0)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        for n, v in want.items():
-            got = o[n].cpu()
-            if n in ("wo", "lg"):
-                assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (rep, n)
-            else:
-                assert torch.equal(got, v), (rep, n)
+    for forked in (False, True):
+        o = outs()
+        g = torch.cuda.CUDAGraph()
+        cap, side = torch.cuda.Stream(), torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=cap):
+            chain(o, torch.cuda.current_stream(), side if forked else None)
+        for rep in range(4):
+            for n in ("pay", "sc", "qf", "qs", "wo", "top"):   # eager work between replays
+                o[n].zero_()
+            o["lg"].fill_(-7.0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for n, v in want.items():
+                got = o[n].cpu()
+                if n in ("wo", "lg"):
+                    assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (forked, rep, n)
+                else:
+                    assert torch.equal(got, v), (forked, rep, n)
