@@ -281,9 +281,9 @@ static hipError_t launch_nmt(const uint8_t* q_fp4, const uint8_t* q_scale, const
     return launch_rw<2, NMT, 4, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
                              num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
   if (max_rows_per_req == 3 || max_rows_per_req == 6)
-    return launch_rw<3, NMT, 4, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+    return launch_rw<3, NMT, 8, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
                              num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-  return launch_rw<4, NMT, 4, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+  return launch_rw<4, NMT, 8, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
                            num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
 }
 
