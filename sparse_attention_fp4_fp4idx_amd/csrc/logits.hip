@@ -6,8 +6,8 @@
 //
 // Work decomposition
 //   work-group (256 threads = 4 waves) = (request, group of up to RW rows,
-//   chunk of 4*PPW pages), a 3-D grid; wave w takes PPW consecutive pages of
-//   the chunk.
+//   chunk of 4*PPW pages), a 3-D grid with each request's chunks rotated
+//   across the XCDs; wave w takes PPW consecutive pages of the chunk.
 //   Every wave keeps its rows' packed Q (the MFMA A operand) and head weights
 //   in registers and streams K pages: per 16-token tile each lane loads 16
 //   payload bytes (one 128-bit load; the 64 lanes read 4 runs of 256 B) and
@@ -113,10 +113,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;  // packed A-scale registers per row
 
-  // grid: x = page chunk, y = row group, z = request (no index arithmetic)
-  const int chunk = blockIdx.x;
+  // grid: x = page chunk, y = row group, z = request.  Work-groups go to the
+  // eight XCDs round robin by linear id, so with the chunk count a multiple
+  // of 8 a fixed chunk index would always land on the same XCD; early chunks
+  // exist for every request, late ones only for long requests, which would
+  // load the first XCDs most.  Rotating each request's chunks by its index
+  // spreads every request over all XCDs (a bijection per request).
+  const int n_chunks = gridDim.x;
   const int grp = blockIdx.y;
   const int req = blockIdx.z;
+  int rot = req & 7;
+  if (rot >= n_chunks) rot %= n_chunks;
+  int chunk = (int)blockIdx.x + rot;
+  if (chunk >= n_chunks) chunk -= n_chunks;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int page_begin = (chunk * 4 + wave) * PPW;
@@ -147,17 +156,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // page loads and, loads retiring in order, waiting for it does not wait
   // for the pages)
   const int32_t my_ctx = row_ctx[min(row0 + (lane & 3), row_hi)];
+  __builtin_amdgcn_sched_barrier(0);  // issued before the exit test below
   int32_t pid[PPW];
 #pragma unroll
   for (int i = 0; i < PPW; ++i)
     pid[i] = (nrows > 0 && page_begin + i < bt_stride) ? __builtin_amdgcn_readlane(my_pid, i) : -1;
-  // Branch-free, so all loads issue back to back: an id outside
-  // [0, num_pages) (a table entry past the request's pages, or an empty row
-  // group) reads page 0 instead and its tile is never stored.
+  // A wave whose first page id is outside [0, num_pages) has nothing to
+  // store: the table only promises valid ids for pages some row needs, and
+  // the wave's pages start past them (an empty row group has no ids at all).
+  // It leaves before loading anything, so it neither holds a slot nor queues
+  // page traffic ahead of the waves that have work.
+  if (!(pid[0] >= 0 && pid[0] < num_pages)) return;
+  // Branch-free from here, so all loads issue back to back: another id
+  // outside the pool (past the request's pages) re-reads the first page and
+  // its tile is never stored.
   PageRegs nxt[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : 0;
+    const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
     load_page(nxt[i], payload, scale, pg, lane_pay, lane_sc);
   }
 
