@@ -74,7 +74,7 @@ int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_strid
   if (!k_bf16 || !pos || !slot || !norm_w_bf16 || !cos_sin_bf16 || !payload || !scale) return FP4IDX_E_INVALID;
   if (!aligned(k_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
   if (!(eps >= 0.0f)) return FP4IDX_E_INVALID;
-  if (n_tokens > ((int64_t)0x7FFFFFFF) * 256) return FP4IDX_E_INVALID;
+  if (n_tokens > ((int64_t)0x7FFFFFFF) * 64) return FP4IDX_E_INVALID;  // 4 lanes per token, grid x < 2^31
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16,
@@ -92,7 +92,7 @@ int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64
   if (!q_bf16 || !pos || !cos_sin_bf16 || !w_in || !q_fp4 || !q_scale || !w_out) return FP4IDX_E_INVALID;
   if (!aligned(q_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(q_fp4, 16) || !aligned(q_scale, 4))
     return FP4IDX_E_INVALID;
-  if (n_rows * n_heads > ((int64_t)0x7FFFFFFF) * 256) return FP4IDX_E_INVALID;
+  if (n_rows * n_heads > ((int64_t)0x7FFFFFFF) * 64) return FP4IDX_E_INVALID;  // 4 lanes per vector
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, w_in, w_scale,

@@ -1,11 +1,11 @@
-// Four-lane variant of the FP4 encoders, for small batches where the
-// one-lane-per-vector kernels are latency bound.
+// Device helpers of the two FP4 encoders (K writer, Q pack) on gfx950.
 //
 // A quad of lanes q = 0..3 owns one 128-vector; lane q holds the 32 elements
 //   i = 32*c + 8*q + e,   c = 0..3 (register chunk), e = 0..7.
 // Index bits 0-2 (e) and 5-6 (c) are in-lane, bits 3-4 (q) are across the
 // quad.  With this placement:
 //  * the 16-byte loads are contiguous (chunk c of lane q = bytes 64c + 16q),
+//    so a wave's load instruction covers 16 rows x 64 contiguous bytes,
 //  * RoPE pairs (j, j+32) are chunks 0 and 1 of the same lane,
 //  * Hadamard stages h = 1, 2, 4, 32, 64 are in-lane and h = 8, 16 are one
 //    quad-permute DPP exchange each,
@@ -13,16 +13,46 @@
 //    lane q's 8 codes are bytes 4q..4q+3 of that block's 16 bytes,
 //  * the RMSNorm balanced tree is: 8-element subtrees in-lane, then the
 //    quad levels (xor 1, xor 2), then the chunk levels in-lane.
-// Every floating-point operation is the one the single-lane encoder does, on
-// the same operands and in the same order (additions only ever change operand
+// Every floating-point operation is the one of the canonical encoder order
+// stated in include/fp4idx.h (one vector evaluated in program order), on the
+// same operands and in the same order; additions only ever change operand
 // order where IEEE addition is commutative, and u - v is formed as
-// v' + (-u') only where that is the identical IEEE operation), so both
-// variants produce identical bytes.
+// v' + (-u') only where that is the identical IEEE operation, so the bytes
+// are exactly the canonical ones.  Build flags keep it exact:
+// -ffp-contract=off (no FMA formation), default correctly rounded fp32
+// sqrt/div, fp32 denormals kept.
 #pragma once
 
-#include "encode.hpp"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fp4idx {
+
+constexpr int kDim = 128;
+constexpr int kRope = 64;
+constexpr int kPageTokens = 64;
+constexpr int kPayloadPage = 4096;  // [1, 4, 64, 16]
+constexpr int kScalePage = 256;     // [1, 4, 64]
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: read once, do not keep in cache).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 8 bf16 packed in 16 bytes -> 8 fp32 (exact widening).
+__device__ __forceinline__ void widen8(uint4 v, float* x) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
 
 // quad_perm DPP controls: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1]
 constexpr int kDppXor1 = 0xB1;

@@ -7,103 +7,15 @@
 // "dsv4.1-amd: KV cache layouts, FP4 indexer, ..." Summary: index-Q and the
 // head weights are packed in one launch.
 //
-// Two mappings with identical arithmetic:
-//  * wide (large batches): one lane per token (K) or per (row, head) (Q).  The
-//    whole 128-vector lives in the lane's registers, so normalisation,
-//    rotation, the 7-stage Hadamard and the block quantisation are all
-//    in-lane: no cross-lane traffic, fewest instructions per vector.  With
-//    consecutive slots the 64 lanes of a wave write 64 consecutive 16-byte
-//    payload chunks per block (1 KiB contiguous) and 64 consecutive scale bytes.
-//  * quad (small batches): four lanes per vector (encode_quad.hpp), a quarter
-//    of the serial instruction chain per lane, for decode-sized batches whose
-//    time is latency, not throughput.
-#include "encode.hpp"
+// Four lanes per 128-vector (encode_quad.hpp): a quarter of the serial
+// instruction chain per lane, and each load instruction of a wave covers 16
+// rows x 64 contiguous bytes.  (One lane per vector, with the whole vector in
+// one lane's registers, measured 1.5-2x slower at every batch size: its loads
+// touch 64 rows per instruction.)
 #include "encode_quad.hpp"
 #include "launch.hpp"
 
 namespace fp4idx {
-
-__global__ __launch_bounds__(256) void write_k_kernel(const uint16_t* __restrict__ k, int64_t n_tokens,
-                                                      int64_t k_row_stride, const int32_t* __restrict__ pos,
-                                                      const int32_t* __restrict__ slot,
-                                                      const uint16_t* __restrict__ norm_w, float eps,
-                                                      const uint16_t* __restrict__ cos_sin,
-                                                      uint8_t* __restrict__ payload, uint8_t* __restrict__ scale) {
-  __shared__ float g[kDim];
-  if (threadIdx.x < kDim) g[threadIdx.x] = __uint_as_float((uint32_t)norm_w[threadIdx.x] << 16);
-  __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_tokens) return;
-  const int32_t s = slot[i];
-  if (s < 0) return;
-  const int32_t p = pos[i];
-
-  float x[kDim];
-  load_row128(k + i * k_row_stride, x);
-
-  // RMSNorm: balanced pairwise tree of squares (adjacent pairs first).
-  float t[kDim / 2];
-#pragma unroll
-  for (int j = 0; j < kDim / 2; ++j) {
-    const float a = x[2 * j] * x[2 * j], b = x[2 * j + 1] * x[2 * j + 1];
-    t[j] = a + b;
-  }
-#pragma unroll
-  for (int len = kDim / 2; len > 1; len >>= 1) {
-#pragma unroll
-    for (int j = 0; j < len / 2; ++j) t[j] = t[2 * j] + t[2 * j + 1];
-  }
-  const float ms = t[0] * 0.0078125f;
-  const float r = 1.0f / sqrtf(ms + eps);
-#pragma unroll
-  for (int j = 0; j < kDim; ++j) {
-    const float xr = x[j] * r;
-    x[j] = xr * g[j];
-  }
-
-  rope64(x, cos_sin + (int64_t)p * kRope);
-  hadamard128(x);
-  uint4 codes[4];
-  uint32_t sc;
-  quant128(x, codes, sc);
-
-  const int64_t page = s >> 6;
-  const int tok = s & 63;
-  uint8_t* pp = payload + page * kPayloadPage + tok * 16;
-  uint8_t* sp = scale + page * kScalePage + tok;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint4*>(pp + j * 1024) = codes[j];
-    sp[j * 64] = (uint8_t)(sc >> (8 * j));
-  }
-}
-
-__global__ __launch_bounds__(256) void pack_q_kernel(const uint16_t* __restrict__ q, int64_t n_rows, int n_heads,
-                                                     int64_t q_row_stride, const int32_t* __restrict__ pos,
-                                                     const uint16_t* __restrict__ cos_sin,
-                                                     const float* __restrict__ w_in, float w_scale,
-                                                     uint8_t* __restrict__ q_fp4, uint8_t* __restrict__ q_scale,
-                                                     float* __restrict__ w_out) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, head)
-  if (idx >= n_rows * n_heads) return;
-  const int64_t row = idx / n_heads;
-  const int h = (int)(idx - row * n_heads);
-  const int32_t p = pos[row];
-
-  float x[kDim];
-  load_row128(q + row * q_row_stride + (int64_t)h * kDim, x);
-  rope64(x, cos_sin + (int64_t)p * kRope);
-  hadamard128(x);
-  uint4 codes[4];
-  uint32_t sc;
-  quant128(x, codes, sc);
-
-  uint4* out = reinterpret_cast<uint4*>(q_fp4 + idx * 64);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = codes[j];
-  reinterpret_cast<uint32_t*>(q_scale)[idx] = sc;
-  w_out[idx] = w_in[idx] * w_scale;
-}
 
 __global__ __launch_bounds__(256) void write_k_quad_kernel(const uint16_t* __restrict__ k, int64_t n_tokens,
                                                            int64_t k_row_stride, const int32_t* __restrict__ pos,
@@ -175,22 +87,12 @@ __global__ __launch_bounds__(256) void pack_q_quad_kernel(const uint16_t* __rest
   if (q == 0) w_out[idx] = w_in[idx] * w_scale;
 }
 
-// Batches below these sizes take the quad kernels (latency), larger ones the
-// wide kernels (throughput).
-constexpr int64_t kQuadMaxTokens = 16384;
-constexpr int64_t kQuadMaxVectors = 16384;
-
 hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
                           const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
                           uint8_t* payload, uint8_t* scale, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
-  if (n_tokens < kQuadMaxTokens) {
-    const int64_t blocks = (4 * n_tokens + 255) / 256;
-    return launch(write_k_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos,
-                  slot, norm_w, eps, cos_sin, payload, scale);
-  }
-  const int64_t blocks = (n_tokens + 255) / 256;
-  return launch(write_k_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos, slot,
+  const int64_t blocks = (4 * n_tokens + 255) / 256;
+  return launch(write_k_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos, slot,
                 norm_w, eps, cos_sin, payload, scale);
 }
 
@@ -199,13 +101,8 @@ hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t
                          uint8_t* q_scale, float* w_out, hipStream_t stream) {
   const int64_t n = n_rows * n_heads;
   if (n == 0) return hipSuccess;
-  if (n < kQuadMaxVectors) {
-    const int64_t blocks = (4 * n + 255) / 256;
-    return launch(pack_q_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride,
-                  pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
-  }
-  const int64_t blocks = (n + 255) / 256;
-  return launch(pack_q_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride, pos,
+  const int64_t blocks = (4 * n + 255) / 256;
+  return launch(pack_q_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride, pos,
                 cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
 }
 

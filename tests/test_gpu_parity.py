@@ -75,7 +75,7 @@ def test_write_k_small_ragged_bit_exact(F, orc):
     assert np.array_equal(po, pg) and np.array_equal(so, sg)
 
 
-@pytest.mark.parametrize("n", [300, 20000])   # quad-lane and one-lane kernels; neither a multiple of the block
+@pytest.mark.parametrize("n", [300, 20000])   # a partial block and a multi-wave batch; neither a multiple of the block
 def test_write_k_edges_strided_skip_extremes(F, orc, n):
     rng = np.random.default_rng(21)
     tab = W.rope_table(4096)
@@ -129,9 +129,9 @@ def test_pack_q_small_bit_exact(F, orc, heads):
         assert np.array_equal(a, b)
 
 
-def test_pack_q_wide_path_edges(F, orc):
+def test_pack_q_edges_zero_and_tiny_rows(F, orc):
     rng = np.random.default_rng(23)
-    T, heads = 300, 64            # 19,200 vectors: one-lane kernel
+    T, heads = 300, 64            # 19,200 vectors: zero rows, near-underflow heads, signed weights
     tab = W.rope_table(1 << 12)
     q = W.bf16_normal(rng, (T, heads, 128))
     q[0] = 0
