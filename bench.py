@@ -9,13 +9,17 @@ compressed tokens, random page tables, top-k 2048).
 Inputs are synthetic and seeded; the page pool is filled before timing by the
 library's own K writer.  Every timed step reads a different copy of the
 inputs (copies total well above the 256 MB last-level cache), so the HBM
-figures are HBM, not cache.  The timed region replays one HIP graph per input
-copy (the step's four launches in sequence; capturing the independent K
-write and Q pack as two parallel branches measured slower), as a serving
-loop would; `--eager` times plain launches instead.  Per-kernel durations come from a second pass over the
-same K steps, launched eagerly, where each kernel carries HIP events that its
-own dispatch stamps with its start and end times (fp4idx_time_next_call ->
-hipExtLaunchKernel); they feed the roofline figures.
+figures are HBM, not cache.  A timed step is three launches in sequence (the
+K write and Q pack together in one launch, the logits, the top-k), issued as
+prepared library calls (arguments marshalled once per input copy, one ctypes
+call per launch: about 10 us of host time per step, below the GPU time) or,
+with `--launch graph`, as a replay of a HIP graph captured per input copy
+(slower on this stack: hipGraphLaunch costs more host time than the three
+calls).  Per-kernel durations come from a second pass over the
+same K steps, launched eagerly with the two encoders as separate kernels,
+where each kernel carries HIP events that its own dispatch stamps with its
+start and end times (fp4idx_time_next_call -> hipExtLaunchKernel); they feed
+the roofline figures.
 
 Prints one JSON line (rank 0).
 """
@@ -78,7 +82,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode batch 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of HIP graph replays")
+    ap.add_argument("--launch", choices=("prepared", "graph"), default="prepared",
+                    help="timed steps as prepared library calls (default) or as HIP graph replays")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to defeat the cache)")
     ap.add_argument("--source-sha", action="store_true", help="print the kernel-source digest and exit")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MB",
@@ -150,13 +155,21 @@ def main():
     names = ("write_k", "pack_q", "mqa_logits", "topk")
 
     def step(s, strm, ev=None):
+        """One pass of the path on stream strm.  The timed steps encode the
+        step's K tokens and query rows in one launch (fp4idx_write_k_pack_q);
+        the kernel-timing pass (ev given) launches the two encoders separately
+        so that each component kernel gets its own duration."""
         def arm(i):   # events stamped with kernel i's own start / end (hipExtLaunchKernel)
             if ev is not None:
                 F.time_next_call(ev[i][0], ev[i][1])
-        arm(0)
-        F.write_k(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"], stream=strm)
-        arm(1)
-        F.pack_q(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
+        if ev is None:
+            F.write_k_pack_q(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"],
+                             s["q"], pos_q, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
+        else:
+            arm(0)
+            F.write_k(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"], stream=strm)
+            arm(1)
+            F.pack_q(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
         arm(2)
         F.mqa_logits(s["q_fp4"], s["q_scale"], s["w_out"], indptr, ctx, bt, s["payload"], s["scale"],
                      wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=strm)
@@ -176,26 +189,42 @@ def main():
         del csrc, cdst
 
     # ---- one HIP graph per input copy: the step's four launches, replayed as one unit
-    graphs = []
-    if not args.eager:
+    # ---- the timed steps: per input copy either three prepared library calls
+    # (arguments marshalled once, one ctypes call each) or one captured HIP graph
+    runners = []
+    if args.launch == "graph":
         cap = torch.cuda.Stream()
         for c in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 step(sets[c], torch.cuda.current_stream())
-            graphs.append(g)
+            runners.append(g.replay)
+            sets[c]["graph"] = g
+    else:
         for c in range(copies):
-            graphs[c].replay()
-        torch.cuda.synchronize()
+            s_ = sets[c]
+            pw, _ = F.prepare_write_k_pack_q(s_["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s_["payload"],
+                                             s_["scale"], s_["q"], pos_q, s_["w"], wl.w_scale, s_["q_fp4"],
+                                             s_["q_scale"], s_["w_out"], stream=stream)
+            pl, _ = F.prepare_mqa_logits(s_["q_fp4"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, s_["payload"],
+                                         s_["scale"], wl.max_rows_per_req, wl.max_ctx, logits=s_["logits"],
+                                         stream=stream)
+            pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
 
-    # ---- timed region: K steps (graph replays, or eager launches with --eager), bracketed by synchronize
+            def run(pw=pw, pl=pl, pt=pt):
+                pw()
+                pl()
+                pt()
+            runners.append(run)
+    for c in range(copies):
+        runners[c]()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, bracketed by synchronize
     torch.cuda.synchronize()
     start = time.perf_counter()
     for i in range(args.steps):
-        if graphs:
-            graphs[i % copies].replay()
-        else:
-            step(sets[i % copies], stream)
+        runners[i % copies]()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - start
 
@@ -299,7 +328,8 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 (e2m1 x e2m1, fp32 accumulate); fp32 encoders",
         "data": "synthetic",
-        "config": {"workload": wl.name, "launch": "eager" if args.eager else "hip graph per step", "requests": wl.n_reqs, "rows": T, "heads": H, "head_dim": 128,
+        "config": {"workload": wl.name, "launch": ("prepared calls" if args.launch == "prepared" else "hip graph per step")
+                   + ": write_k+pack_q in one launch, logits, top-k", "requests": wl.n_reqs, "rows": T, "heads": H, "head_dim": 128,
                    "scores_per_step": scores, "k_write_tokens_per_step": int(wl.k_new.shape[0]), "topk": k,
                    "pool_pages": wl.num_pages, "input_copies": copies},
         "k_write_tokens_per_s": round(wl.k_new.shape[0] / (per_kernel_ms["write_k"] * 1e-3), 1),

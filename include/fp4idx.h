@@ -107,6 +107,24 @@ int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64
                   float w_scale, uint8_t* q_fp4, uint8_t* q_scale, float* w_out, void* stream);
 
 /*
+ * A decode step's K write and Q pack in one launch.  The two are independent
+ * ([P2] FP4 kernel adapters: the writer is fed the step's positions and
+ * slots; the Q adapter packs the step's query rows), so one grid does both:
+ * its first work-groups run fp4idx_write_k's kernel, the rest
+ * fp4idx_pack_q's.  Arguments, layouts, results and errors are exactly those
+ * of the two calls (the cos/sin table and max_pos are shared; pos_k is the
+ * K tokens' positions, pos_q the query rows'); either batch may be empty.
+ * Equivalent to fp4idx_write_k followed by fp4idx_pack_q on the same stream,
+ * with one launch less.
+ */
+int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
+                          const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                          int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages,
+                          const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                          const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp4, uint8_t* q_scale,
+                          float* w_out, void* stream);
+
+/*
  * Paged-MQA FP4 logits.  [P2] Attention runtime (FP4 paged-MQA logits over
  * the split payload/scale cache, padded rows at zero context); the score is
  * the lightning-indexer score
@@ -158,7 +176,8 @@ int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, cons
 /*
  * Kernel timing (measurement support, not part of the method).  Arms two HIP
  * events for the calling thread's next call of fp4idx_write_k, fp4idx_pack_q,
- * fp4idx_mqa_logits or fp4idx_topk; each of these launches exactly one kernel.
+ * fp4idx_write_k_pack_q, fp4idx_mqa_logits or fp4idx_topk; each of these
+ * launches exactly one kernel.
  * That kernel is then dispatched with hipExtLaunchKernel, which stamps the
  * events with the dispatch's own start and end times, so
  * hipEventElapsedTime(start, stop) is the kernel's execution time with no

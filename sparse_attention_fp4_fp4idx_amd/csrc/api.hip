@@ -64,10 +64,14 @@ const char* fp4idx_status_string(int status) {
   }
 }
 
-int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
-                   const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
-                   int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, void* stream) {
-  const TimingScope timing_scope;
+}  // extern "C"
+
+namespace {
+
+// Host checks of the K writer's arguments (an empty batch checks no pointer).
+int check_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                  const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                  int32_t max_pos, const uint8_t* payload, const uint8_t* scale, int64_t num_pages) {
   if (n_tokens < 0 || num_pages < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
   if (k_row_stride < FP4IDX_HEAD_DIM || (k_row_stride % 8) != 0) return FP4IDX_E_INVALID;
   if (n_tokens == 0) return FP4IDX_OK;
@@ -75,6 +79,35 @@ int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_strid
   if (!aligned(k_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
   if (!(eps >= 0.0f)) return FP4IDX_E_INVALID;
   if (n_tokens > ((int64_t)0x7FFFFFFF) * 64) return FP4IDX_E_INVALID;  // 4 lanes per token, grid x < 2^31
+  return FP4IDX_OK;
+}
+
+// Host checks of the Q pack's arguments (an empty batch checks no pointer).
+int check_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride, const int32_t* pos,
+                 const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in, const uint8_t* q_fp4,
+                 const uint8_t* q_scale, const float* w_out) {
+  if (n_rows < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (q_row_stride < (int64_t)n_heads * FP4IDX_HEAD_DIM || (q_row_stride % 8) != 0) return FP4IDX_E_INVALID;
+  if (n_rows == 0) return FP4IDX_OK;
+  if (!q_bf16 || !pos || !cos_sin_bf16 || !w_in || !q_fp4 || !q_scale || !w_out) return FP4IDX_E_INVALID;
+  if (!aligned(q_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(q_fp4, 16) || !aligned(q_scale, 4))
+    return FP4IDX_E_INVALID;
+  if (n_rows * n_heads > ((int64_t)0x7FFFFFFF) * 64) return FP4IDX_E_INVALID;  // 4 lanes per vector
+  return FP4IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                   const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                   int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, void* stream) {
+  const TimingScope timing_scope;
+  const int rc = check_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16, max_pos,
+                               payload, scale, num_pages);
+  if (rc != FP4IDX_OK || n_tokens == 0) return rc;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16,
@@ -85,18 +118,35 @@ int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64
                   const int32_t* pos, const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in,
                   float w_scale, uint8_t* q_fp4, uint8_t* q_scale, float* w_out, void* stream) {
   const TimingScope timing_scope;
-  if (n_rows < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
-  if (q_row_stride < (int64_t)n_heads * FP4IDX_HEAD_DIM || (q_row_stride % 8) != 0) return FP4IDX_E_INVALID;
-  if (n_rows == 0) return FP4IDX_OK;
-  if (!q_bf16 || !pos || !cos_sin_bf16 || !w_in || !q_fp4 || !q_scale || !w_out) return FP4IDX_E_INVALID;
-  if (!aligned(q_bf16, 16) || !aligned(cos_sin_bf16, 16) || !aligned(q_fp4, 16) || !aligned(q_scale, 4))
-    return FP4IDX_E_INVALID;
-  if (n_rows * n_heads > ((int64_t)0x7FFFFFFF) * 64) return FP4IDX_E_INVALID;  // 4 lanes per vector
+  const int rc = check_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, max_pos, w_in, q_fp4,
+                              q_scale, w_out);
+  if (rc != FP4IDX_OK || n_rows == 0) return rc;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, w_in, w_scale,
                                         q_fp4, q_scale, w_out, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
+                          const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                          int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages,
+                          const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                          const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp4, uint8_t* q_scale,
+                          float* w_out, void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_write_k(k_bf16, n_tokens, k_row_stride, pos_k, slot, norm_w_bf16, eps, cos_sin_bf16, max_pos,
+                         payload, scale, num_pages);
+  if (rc != FP4IDX_OK) return rc;
+  rc = check_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos_q, cos_sin_bf16, max_pos, w_in, q_fp4, q_scale,
+                    w_out);
+  if (rc != FP4IDX_OK) return rc;
+  if (n_tokens == 0 && n_rows == 0) return FP4IDX_OK;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_write_k_pack_q(k_bf16, n_tokens, k_row_stride, pos_k, slot, norm_w_bf16, eps,
+                                                cos_sin_bf16, payload, scale, q_bf16, n_rows, n_heads, q_row_stride,
+                                                pos_q, w_in, w_scale, q_fp4, q_scale, w_out,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,

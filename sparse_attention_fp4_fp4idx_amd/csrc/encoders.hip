@@ -17,27 +17,50 @@
 
 namespace fp4idx {
 
-__global__ __launch_bounds__(256) void write_k_quad_kernel(const uint16_t* __restrict__ k, int64_t n_tokens,
-                                                           int64_t k_row_stride, const int32_t* __restrict__ pos,
-                                                           const int32_t* __restrict__ slot,
-                                                           const uint16_t* __restrict__ norm_w, float eps,
-                                                           const uint16_t* __restrict__ cos_sin,
-                                                           uint8_t* __restrict__ payload,
-                                                           uint8_t* __restrict__ scale) {
+// Arguments of the two encoders (kernel arguments by value).
+struct WriteKArgs {
+  const uint16_t* k;
+  int64_t n_tokens;
+  int64_t k_row_stride;
+  const int32_t* pos;
+  const int32_t* slot;
+  const uint16_t* norm_w;
+  float eps;
+  const uint16_t* cos_sin;
+  uint8_t* payload;
+  uint8_t* scale;
+};
+
+struct PackQArgs {
+  const uint16_t* q;
+  int64_t n_rows;
+  int n_heads;
+  int64_t q_row_stride;
+  const int32_t* pos;
+  const uint16_t* cos_sin;
+  const float* w_in;
+  float w_scale;
+  uint8_t* q_fp4;
+  uint8_t* q_scale;
+  float* w_out;
+};
+
+// Block b of the K writer: tokens 64 b .. 64 b + 63, four lanes each.
+__device__ __forceinline__ void write_k_block(const WriteKArgs& a, int64_t b) {
   __shared__ float g[kDim];
-  if (threadIdx.x < kDim) g[threadIdx.x] = __uint_as_float((uint32_t)norm_w[threadIdx.x] << 16);
+  if (threadIdx.x < kDim) g[threadIdx.x] = __uint_as_float((uint32_t)a.norm_w[threadIdx.x] << 16);
   __syncthreads();
-  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gl = b * 256 + threadIdx.x;
   const int64_t i = gl >> 2;  // token; its four lanes leave or stay together
   const int q = (int)(gl & 3);
-  if (i >= n_tokens) return;
-  const int32_t s = slot[i];
+  if (i >= a.n_tokens) return;
+  const int32_t s = a.slot[i];
   if (s < 0) return;
-  const int32_t p = pos[i];
+  const int32_t p = a.pos[i];
 
   QuadVec v;
-  quad_load(k + i * k_row_stride, q, v);
-  const float r = quad_rms_factor(v, eps);
+  quad_load(a.k + i * a.k_row_stride, q, v);
+  const float r = quad_rms_factor(v, a.eps);
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -45,55 +68,66 @@ __global__ __launch_bounds__(256) void write_k_quad_kernel(const uint16_t* __res
       const float xr = v.x[c][e] * r;
       v.x[c][e] = xr * g[32 * c + 8 * q + e];
     }
-  quad_rope(v, cos_sin + (int64_t)p * kRope, q);
+  quad_rope(v, a.cos_sin + (int64_t)p * kRope, q);
   quad_hadamard(v, q);
   uint32_t word[4], sc;
   quad_quant(v, word, sc);
 
   const int64_t page = s >> 6;
   const int tok = s & 63;
-  uint8_t* pp = payload + page * kPayloadPage + tok * 16 + 4 * q;
+  uint8_t* pp = a.payload + page * kPayloadPage + tok * 16 + 4 * q;
 #pragma unroll
   for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(pp + c * 1024) = word[c];
-  scale[page * kScalePage + q * 64 + tok] = (uint8_t)(sc >> (8 * q));
+  a.scale[page * kScalePage + q * 64 + tok] = (uint8_t)(sc >> (8 * q));
 }
 
-__global__ __launch_bounds__(256) void pack_q_quad_kernel(const uint16_t* __restrict__ q_in, int64_t n_rows,
-                                                          int n_heads, int64_t q_row_stride,
-                                                          const int32_t* __restrict__ pos,
-                                                          const uint16_t* __restrict__ cos_sin,
-                                                          const float* __restrict__ w_in, float w_scale,
-                                                          uint8_t* __restrict__ q_fp4, uint8_t* __restrict__ q_scale,
-                                                          float* __restrict__ w_out) {
-  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Block b of the Q pack: (row, head) vectors 64 b .. 64 b + 63, four lanes each.
+__device__ __forceinline__ void pack_q_block(const PackQArgs& a, int64_t b) {
+  const int64_t gl = b * 256 + threadIdx.x;
   const int64_t idx = gl >> 2;  // (row, head)
   const int q = (int)(gl & 3);
-  if (idx >= n_rows * n_heads) return;
-  const int64_t row = idx / n_heads;
-  const int h = (int)(idx - row * n_heads);
-  const int32_t p = pos[row];
+  if (idx >= a.n_rows * a.n_heads) return;
+  const int64_t row = idx / a.n_heads;
+  const int h = (int)(idx - row * a.n_heads);
+  const int32_t p = a.pos[row];
 
   QuadVec v;
-  quad_load(q_in + row * q_row_stride + (int64_t)h * kDim, q, v);
-  quad_rope(v, cos_sin + (int64_t)p * kRope, q);
+  quad_load(a.q + row * a.q_row_stride + (int64_t)h * kDim, q, v);
+  quad_rope(v, a.cos_sin + (int64_t)p * kRope, q);
   quad_hadamard(v, q);
   uint32_t word[4], sc;
   quad_quant(v, word, sc);
 
-  uint8_t* out = q_fp4 + idx * 64 + 4 * q;
+  uint8_t* out = a.q_fp4 + idx * 64 + 4 * q;
 #pragma unroll
   for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(out + 16 * c) = word[c];
-  q_scale[idx * 4 + q] = (uint8_t)(sc >> (8 * q));
-  if (q == 0) w_out[idx] = w_in[idx] * w_scale;
+  a.q_scale[idx * 4 + q] = (uint8_t)(sc >> (8 * q));
+  if (q == 0) a.w_out[idx] = a.w_in[idx] * a.w_scale;
 }
+
+__global__ __launch_bounds__(256) void write_k_quad_kernel(WriteKArgs a) { write_k_block(a, blockIdx.x); }
+
+__global__ __launch_bounds__(256) void pack_q_quad_kernel(PackQArgs a) { pack_q_block(a, blockIdx.x); }
+
+// One launch for a decode step's two independent encodes: the first
+// k_blocks work-groups write K, the rest pack Q (the branch is uniform per
+// work-group).
+__global__ __launch_bounds__(256) void write_k_pack_q_kernel(WriteKArgs ka, PackQArgs qa, int64_t k_blocks) {
+  const int64_t b = blockIdx.x;
+  if (b < k_blocks)
+    write_k_block(ka, b);
+  else
+    pack_q_block(qa, b - k_blocks);
+}
+
+static inline int64_t quad_blocks(int64_t n) { return (4 * n + 255) / 256; }
 
 hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
                           const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
                           uint8_t* payload, uint8_t* scale, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
-  const int64_t blocks = (4 * n_tokens + 255) / 256;
-  return launch(write_k_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, n_tokens, k_row_stride, pos, slot,
-                norm_w, eps, cos_sin, payload, scale);
+  const WriteKArgs a{k, n_tokens, k_row_stride, pos, slot, norm_w, eps, cos_sin, payload, scale};
+  return launch(write_k_quad_kernel, dim3((unsigned)quad_blocks(n_tokens)), dim3(256), 0, stream, a);
 }
 
 hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride, const int32_t* pos,
@@ -101,9 +135,21 @@ hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t
                          uint8_t* q_scale, float* w_out, hipStream_t stream) {
   const int64_t n = n_rows * n_heads;
   if (n == 0) return hipSuccess;
-  const int64_t blocks = (4 * n + 255) / 256;
-  return launch(pack_q_quad_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, n_rows, n_heads, q_row_stride, pos,
-                cos_sin, w_in, w_scale, q_fp4, q_scale, w_out);
+  const PackQArgs a{q, n_rows, n_heads, q_row_stride, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out};
+  return launch(pack_q_quad_kernel, dim3((unsigned)quad_blocks(n)), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_write_k_pack_q(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
+                                 const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
+                                 uint8_t* payload, uint8_t* scale, const uint16_t* q, int64_t n_rows, int n_heads,
+                                 int64_t q_row_stride, const int32_t* pos_q, const float* w_in, float w_scale,
+                                 uint8_t* q_fp4, uint8_t* q_scale, float* w_out, hipStream_t stream) {
+  const int64_t kb = quad_blocks(n_tokens), qb = quad_blocks(n_rows * n_heads);
+  if (kb + qb == 0) return hipSuccess;
+  if (kb + qb > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const WriteKArgs ka{k, n_tokens, k_row_stride, pos_k, slot, norm_w, eps, cos_sin, payload, scale};
+  const PackQArgs qa{q, n_rows, n_heads, q_row_stride, pos_q, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out};
+  return launch(write_k_pack_q_kernel, dim3((unsigned)(kb + qb)), dim3(256), 0, stream, ka, qa, kb);
 }
 
 }  // namespace fp4idx

@@ -39,6 +39,12 @@ hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t
                          const uint16_t* cos_sin, const float* w_in, float w_scale, uint8_t* q_fp4,
                          uint8_t* q_scale, float* w_out, hipStream_t stream);
 
+hipError_t launch_write_k_pack_q(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
+                                 const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
+                                 uint8_t* payload, uint8_t* scale, const uint16_t* q, int64_t n_rows, int n_heads,
+                                 int64_t q_row_stride, const int32_t* pos_q, const float* w_in, float w_scale,
+                                 uint8_t* q_fp4, uint8_t* q_scale, float* w_out, hipStream_t stream);
+
 hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
                              const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,

@@ -26,8 +26,8 @@ PAYLOAD_PAGE_BYTES = 4096
 SCALE_PAGE_BYTES = 256
 MAX_TOPK = 2048
 
-EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk", "fp4idx_time_next_call",
-           "fp4idx_status_string", "fp4idx_version")
+EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
+           "fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
 class Fp4idxError(RuntimeError):
@@ -50,9 +50,11 @@ def load():
     P, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     lib.fp4idx_write_k.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, P, i64, P]
     lib.fp4idx_pack_q.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
+    lib.fp4idx_write_k_pack_q.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, P, i64,
+                                          P, i64, i32, i64, P, P, f32, P, P, P, P]
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
-    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
+    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fp4idx_time_next_call.argtypes = [P, P]
     lib.fp4idx_time_next_call.restype = ctypes.c_int
@@ -74,6 +76,31 @@ def version() -> int:
 def _check(rc: int, what: str):
     if rc != FP4IDX_OK:
         raise Fp4idxError(f"{what}: {status_string(rc)} (status {rc})")
+
+
+def _run(name: str, args) -> None:
+    _check(getattr(load(), name)(*args), name)
+
+
+class Prepared:
+    """One library call with its arguments marshalled once (device pointers,
+    sizes, stream): calling it issues the same call again with a single ctypes
+    call.  For loops that run the same step over the same buffers (a serving
+    loop's decode step, a benchmark).  It holds references to the tensors it
+    was prepared from; they must keep their storage (no resize_ / set_)."""
+
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, name: str, args, keep=()):
+        self._name = name
+        self._fn = getattr(load(), name)
+        self._args = tuple(args)
+        self._keep = tuple(keep)
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != FP4IDX_OK:
+            _check(rc, self._name)
 
 
 def _stream(stream):
@@ -102,9 +129,7 @@ def _rowstride(t: torch.Tensor, name: str) -> int:
     return int(t.stride(0))
 
 
-def fp4idx_write_k(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor, eps: float,
-                   cos_sin: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
-    """Encode K rows [N, >=128] bf16 and scatter them into the split pool."""
+def _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale):
     if not (pos.is_contiguous() and slot.is_contiguous() and payload.is_contiguous() and scale.is_contiguous()
             and cos_sin.is_contiguous() and norm_w.is_contiguous()):
         raise Fp4idxError("write_k: pos, slot, norm_w, cos_sin and the pools must be contiguous")
@@ -116,19 +141,27 @@ def fp4idx_write_k(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_
         raise Fp4idxError("write_k: pool sizes must be num_pages*4096 and num_pages*256 bytes")
     if cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
         raise Fp4idxError("write_k: cos_sin must be [max_pos, 64]")
-    rc = load().fp4idx_write_k(_ptr(k, _BF16, "k"), n, _rowstride(k, "k") if n else HEAD_DIM,
-                               _ptr(pos, _I32, "pos"), _ptr(slot, _I32, "slot"), _ptr(norm_w, _BF16, "norm_w"),
-                               ctypes.c_float(eps), _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]),
-                               _ptr(payload, _U8, "payload"), _ptr(scale, _U8, "scale"), num_pages, _stream(stream))
-    _check(rc, "fp4idx_write_k")
+    return [_ptr(k, _BF16, "k"), n, _rowstride(k, "k") if n else HEAD_DIM, _ptr(pos, _I32, "pos"),
+            _ptr(slot, _I32, "slot"), _ptr(norm_w, _BF16, "norm_w"), ctypes.c_float(eps),
+            _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]), _ptr(payload, _U8, "payload"),
+            _ptr(scale, _U8, "scale"), num_pages]
 
 
-def fp4idx_pack_q(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_in: torch.Tensor,
-                  w_scale: float = 1.0, q_fp4: torch.Tensor = None, q_scale: torch.Tensor = None,
-                  w_out: torch.Tensor = None, stream=None):
-    """q: [T, H, 128] bf16 (rows may be strided) -> (q_fp4 [T,H,64] u8, q_scale [T,H,4] u8, w [T,H] f32)."""
+def fp4idx_write_k(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor, eps: float,
+                   cos_sin: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
+    """Encode K rows [N, >=128] bf16 and scatter them into the split pool."""
+    _run("fp4idx_write_k", _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale) + [_stream(stream)])
+
+
+def prepare_write_k(k, pos, slot, norm_w, eps, cos_sin, payload, scale, stream=None) -> "Prepared":
+    """fp4idx_write_k with its arguments marshalled once (see Prepared)."""
+    return Prepared("fp4idx_write_k", _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale)
+                    + [_stream(stream)], keep=(k, pos, slot, norm_w, cos_sin, payload, scale))
+
+
+def _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out, with_table=True):
     T, H = int(q.shape[0]), int(q.shape[1])
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1 or q.stride(1) != HEAD_DIM:
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or (T and (q.stride(2) != 1 or q.stride(1) != HEAD_DIM)):
         raise Fp4idxError("pack_q: q must be [T, H, 128] with heads packed inside a row")
     dev = q.device
     q_fp4 = q_fp4 if q_fp4 is not None else torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
@@ -138,18 +171,58 @@ def fp4idx_pack_q(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_i
                     (cos_sin, "cos_sin")):
         if not t.is_contiguous():
             raise Fp4idxError(f"pack_q: {name} must be contiguous")
-    rc = load().fp4idx_pack_q(_ptr(q, _BF16, "q"), T, H, int(q.stride(0)) if T else H * HEAD_DIM,
-                              _ptr(pos, _I32, "pos"), _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]),
-                              _ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_fp4, _U8, "q_fp4"),
-                              _ptr(q_scale, _U8, "q_scale"), _ptr(w_out, _F32, "w_out"), _stream(stream))
-    _check(rc, "fp4idx_pack_q")
-    return q_fp4, q_scale, w_out
+    head = [_ptr(q, _BF16, "q"), T, H, int(q.stride(0)) if T else H * HEAD_DIM, _ptr(pos, _I32, "pos")]
+    table = [_ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0])] if with_table else []
+    tail = [_ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_fp4, _U8, "q_fp4"),
+            _ptr(q_scale, _U8, "q_scale"), _ptr(w_out, _F32, "w_out")]
+    return head + table + tail, (q_fp4, q_scale, w_out)
 
 
-def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor, req_row_indptr: torch.Tensor,
-                      row_ctx: torch.Tensor, block_table: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor,
-                      max_rows_per_req: int, max_ctx: int, logits: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """Paged FP4 logits [T, stride] fp32; only [0, ctx[t]) of each row is written."""
+def fp4idx_pack_q(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_in: torch.Tensor,
+                  w_scale: float = 1.0, q_fp4: torch.Tensor = None, q_scale: torch.Tensor = None,
+                  w_out: torch.Tensor = None, stream=None):
+    """q: [T, H, 128] bf16 (rows may be strided) -> (q_fp4 [T,H,64] u8, q_scale [T,H,4] u8, w [T,H] f32)."""
+    args, outs = _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out)
+    _run("fp4idx_pack_q", args + [_stream(stream)])
+    return outs
+
+
+def prepare_pack_q(q, pos, cos_sin, w_in, w_scale=1.0, q_fp4=None, q_scale=None, w_out=None, stream=None):
+    """fp4idx_pack_q with its arguments marshalled once: (Prepared, outputs)."""
+    args, outs = _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out)
+    return Prepared("fp4idx_pack_q", args + [_stream(stream)], keep=(q, pos, cos_sin, w_in) + outs), outs
+
+
+def _write_k_pack_q_args(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale, q, pos_q, w_in, w_scale, q_fp4,
+                         q_scale, w_out, stream):
+    kargs = _write_k_args(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale)
+    qargs, outs = _pack_q_args(q, pos_q, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out, with_table=False)
+    return kargs + qargs + [_stream(stream)], outs
+
+
+def fp4idx_write_k_pack_q(k: torch.Tensor, pos_k: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor,
+                          eps: float, cos_sin: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor,
+                          q: torch.Tensor, pos_q: torch.Tensor, w_in: torch.Tensor, w_scale: float = 1.0,
+                          q_fp4: torch.Tensor = None, q_scale: torch.Tensor = None, w_out: torch.Tensor = None,
+                          stream=None):
+    """write_k and pack_q in one launch; returns pack_q's (q_fp4, q_scale, w_out)."""
+    args, outs = _write_k_pack_q_args(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale, q, pos_q, w_in, w_scale,
+                                      q_fp4, q_scale, w_out, stream)
+    _run("fp4idx_write_k_pack_q", args)
+    return outs
+
+
+def prepare_write_k_pack_q(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale, q, pos_q, w_in, w_scale=1.0,
+                           q_fp4=None, q_scale=None, w_out=None, stream=None):
+    """fp4idx_write_k_pack_q with its arguments marshalled once: (Prepared, outputs)."""
+    args, outs = _write_k_pack_q_args(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale, q, pos_q, w_in, w_scale,
+                                      q_fp4, q_scale, w_out, stream)
+    keep = (k, pos_k, slot, norm_w, cos_sin, payload, scale, q, pos_q, w_in) + outs
+    return Prepared("fp4idx_write_k_pack_q", args, keep=keep), outs
+
+
+def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, max_rows_per_req,
+                     max_ctx, logits, stream):
     T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
     n_reqs = int(req_row_indptr.numel()) - 1
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -163,19 +236,34 @@ def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tenso
         if not t.is_contiguous():
             raise Fp4idxError(f"mqa_logits: {name} must be contiguous")
     num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
-    rc = load().fp4idx_mqa_logits(_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
-                                  _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs,
-                                  _ptr(row_ctx, _I32, "row_ctx"), _ptr(block_table, _I32, "block_table"),
-                                  int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
-                                  _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"),
-                                  int(logits.stride(0)), int(max_rows_per_req), int(max_ctx), _stream(stream))
-    _check(rc, "fp4idx_mqa_logits")
+    args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
+            _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
+            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
+            _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"), int(logits.stride(0)),
+            int(max_rows_per_req), int(max_ctx), _stream(stream)]
+    return args, logits
+
+
+def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor, req_row_indptr: torch.Tensor,
+                      row_ctx: torch.Tensor, block_table: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor,
+                      max_rows_per_req: int, max_ctx: int, logits: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Paged FP4 logits [T, stride] fp32; only [0, ctx[t]) of each row is written."""
+    args, logits = _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                    max_rows_per_req, max_ctx, logits, stream)
+    _run("fp4idx_mqa_logits", args)
     return logits
 
 
-def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int, out_idx: torch.Tensor = None,
-                stream=None) -> torch.Tensor:
-    """[T, k] int32: top-k positions per row, ascending, then -1."""
+def prepare_mqa_logits(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, max_rows_per_req,
+                       max_ctx, logits=None, stream=None):
+    """fp4idx_mqa_logits with its arguments marshalled once: (Prepared, logits)."""
+    args, logits = _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                    max_rows_per_req, max_ctx, logits, stream)
+    keep = (q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits)
+    return Prepared("fp4idx_mqa_logits", args, keep=keep), logits
+
+
+def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
     T = int(logits.shape[0])
     if logits.stride(-1) != 1:
         raise Fp4idxError("topk: logits must have unit inner stride")
@@ -183,10 +271,23 @@ def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: in
         out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
     if not out_idx.is_contiguous() or not row_ctx.is_contiguous():
         raise Fp4idxError("topk: out_idx and row_ctx must be contiguous")
-    rc = load().fp4idx_topk(_ptr(logits, _F32, "logits"), T, int(logits.stride(0)), _ptr(row_ctx, _I32, "row_ctx"),
-                            int(k), _ptr(out_idx, _I32, "out_idx"), int(max_ctx), _stream(stream))
-    _check(rc, "fp4idx_topk")
+    args = [_ptr(logits, _F32, "logits"), T, int(logits.stride(0)), _ptr(row_ctx, _I32, "row_ctx"), int(k),
+            _ptr(out_idx, _I32, "out_idx"), int(max_ctx), _stream(stream)]
+    return args, out_idx
+
+
+def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int, out_idx: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+    """[T, k] int32: top-k positions per row, ascending, then -1."""
+    args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
+    _run("fp4idx_topk", args)
     return out_idx
+
+
+def prepare_topk(logits, row_ctx, k, max_ctx, out_idx=None, stream=None):
+    """fp4idx_topk with its arguments marshalled once: (Prepared, out_idx)."""
+    args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
+    return Prepared("fp4idx_topk", args, keep=(logits, row_ctx, out_idx)), out_idx
 
 
 def _event_handle(ev):
@@ -211,4 +312,5 @@ write_k = fp4idx_write_k
 pack_q = fp4idx_pack_q
 mqa_logits = fp4idx_mqa_logits
 topk = fp4idx_topk
+write_k_pack_q = fp4idx_write_k_pack_q
 time_next_call = fp4idx_time_next_call

@@ -76,6 +76,14 @@ def test_host_validation_rejects_before_any_launch(F):
     for k in (0, -3, 2049):
         assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, 10, None) == E
     assert lib.fp4idx_topk(fake, 1, 100, fake, 16, fake, 101, None) == E
+    # write_k_pack_q: each half is checked as its own call would check it
+    wk = [fake, 5, 128, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1]
+    pq = [fake, 2, 64, 128 * 64, fake, fake, 1.0, fake, fake, fake]
+    assert lib.fp4idx_write_k_pack_q(*wk[:2], 100, *wk[3:], *pq, None) == E          # K row stride
+    assert lib.fp4idx_write_k_pack_q(*wk, fake, 2, 48, *pq[3:], None) == E           # head count
+    assert lib.fp4idx_write_k_pack_q(*wk, None, 2, 64, *pq[3:], None) == E           # null Q
+    assert lib.fp4idx_write_k_pack_q(None, 0, 128, None, None, None, 1e-6, None, 10, None, None, 0,
+                                     None, 0, 64, 128 * 64, None, None, 1.0, None, None, None, None) == 0
     # timing events armed before a rejected call are dropped with it (no launch, events untouched)
     assert lib.fp4idx_time_next_call(None, None) == 0
     assert lib.fp4idx_time_next_call(fake, fake) == 0

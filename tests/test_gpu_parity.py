@@ -143,6 +143,34 @@ def test_pack_q_edges_zero_and_tiny_rows(F, orc):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("n_tok,n_rows", [(64, 64), (1000, 7), (0, 5), (300, 0)])
+def test_write_k_pack_q_one_launch_bit_exact(F, orc, n_tok, n_rows):
+    """The combined launch produces the oracle's bytes for both halves (either
+    side may be empty) and leaves every other pool byte untouched."""
+    rng = np.random.default_rng([n_tok, n_rows, 5])
+    tab = W.rope_table(1 << 12)
+    num_pages = max(1, (n_tok + 63) // 64 + 3)
+    k = W.bf16_normal(rng, (n_tok, 128))
+    pos_k = rng.integers(0, 1 << 12, n_tok).astype(np.int32)
+    slot = rng.permutation(num_pages * 64)[:n_tok].astype(np.int32)
+    if n_tok > 2:
+        slot[1] = -1                                                # padding token
+    nw = W.norm_weight(rng)
+    q = W.bf16_normal(rng, (n_rows, 64, 128))
+    pos_q = rng.integers(0, 1 << 12, n_rows).astype(np.int32)
+    w = rng.uniform(-1, 1, (n_rows, 64)).astype(np.float32)
+    pay_o = np.full(num_pages * 4096, 0xA5, np.uint8); sc_o = np.full(num_pages * 256, 0x5A, np.uint8)
+    orc.write_k(k, pos_k, slot, nw, 1e-6, tab, pay_o, sc_o)
+    qf_o, qs_o, w_o = orc.pack_q(q, pos_q, tab, w, 0.5)
+    pay_g = dev(np.full(num_pages * 4096, 0xA5, np.uint8)); sc_g = dev(np.full(num_pages * 256, 0x5A, np.uint8))
+    qf_g, qs_g, w_g = F.write_k_pack_q(bf16(k), dev(pos_k), dev(slot), bf16(nw), 1e-6, bf16(tab), pay_g, sc_g,
+                                       bf16(q), dev(pos_q), dev(w), 0.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(pay_g.cpu().numpy(), pay_o) and np.array_equal(sc_g.cpu().numpy(), sc_o)
+    assert np.array_equal(qf_g.cpu().numpy(), qf_o) and np.array_equal(qs_g.cpu().numpy(), qs_o)
+    assert np.array_equal(w_g.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_pack_q_full_size_bit_exact(F, orc, cfg):
     wl = W.make(cfg)
