@@ -65,7 +65,8 @@ def _load():
         lib.orc_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, P, P]
         lib.orc_logits_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, P, i64, i64, P, P, P, P, P]
         lib.orc_topk.argtypes = [P, i64, i64, P, i32, P]
-        for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk"):
+        lib.orc_read_k.argtypes = [P, P, i64, P, i64, P]
+        for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk", "orc_read_k"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -238,4 +239,14 @@ def topk(logits_arr, row_ctx, k):
     out = np.empty((T, k), np.int32)
     rc = _load().orc_topk(_p(logits_arr), T, logits_arr.shape[1], _p(row_ctx), int(k), _p(out))
     _check(rc, "topk")
+    return out
+
+
+def read_k(payload, scale, slots) -> np.ndarray:
+    """Pool tokens at `slots` back to their exact values, fp64 [N, 128]; a
+    slot outside the pool reads as zeros."""
+    payload = _c(payload, np.uint8); scale = _c(scale, np.uint8); slots = _c(slots, np.int32)
+    num_pages = payload.size // 4096
+    out = np.empty((slots.size, D), np.float64)
+    _check(_load().orc_read_k(_p(payload), _p(scale), num_pages, _p(slots), slots.size, _p(out)), "orc_read_k")
     return out

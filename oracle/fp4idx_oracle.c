@@ -328,6 +328,24 @@ static void dequant_token(const uint8_t *payload, const uint8_t *scale, int64_t 
   orc_dequant128(codes, sc, out);
 }
 
+/* ---- the split-pool reader ------------------------------------------------ */
+/* [P1] Summary and [P2] Device memory (a split writer and reader for the
+ * FP4 pool): token `slot` of the pool back to its 128 values, exactly, in
+ * fp64.  A slot outside [0, num_pages*64) (padding) reads as zeros. */
+int orc_read_k(const uint8_t *payload, const uint8_t *scale, int64_t num_pages, const int32_t *slot,
+               int64_t n_tokens, double *out) {
+  if (n_tokens < 0 || num_pages < 0) return -1;
+  for (int64_t i = 0; i < n_tokens; ++i) {
+    const int64_t s = slot[i];
+    if (s < 0 || s >= num_pages * PAGE) {
+      for (int e = 0; e < D; ++e) out[i * D + e] = 0.0;
+      continue;
+    }
+    dequant_token(payload, scale, s / PAGE, (int)(s % PAGE), out + i * D);
+  }
+  return 0;
+}
+
 /* Also returns T = sum_h |w_h| max(d_h, 0) and A = sum_h |w_h| sum_i |q_hi k_i|,
  * the two scales an fp32 evaluation's error is measured against. */
 static double score_one(const double *qd /* [H][D] */, const float *w /* [H] */, int32_t n_heads,

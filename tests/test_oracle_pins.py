@@ -449,3 +449,32 @@ def test_topk_full_sort_ties_and_edges(orc):
     assert np.array_equal(got[4][:10], np.arange(10)) and np.all(got[4][10:] == -1)
     assert np.array_equal(got[3], np.arange(50))
     assert np.array_equal(got[2], np.arange(50))                 # all equal -> lowest positions
+
+
+# ---------------------------------------------------------------- split-pool reader
+
+def test_reader_matches_exact_decoding_through_the_page_shapes(orc):
+    """The reader against exact rational decoding of the same bytes read
+    through the printed page shapes [P,1,4,64,16] / [P,1,4,64] ([P2]
+    Motivation); scale bytes 0..254 cover the subnormal and near-overflow
+    ends, and slots outside the pool read as zeros."""
+    rng = np.random.default_rng(61)
+    P = 3
+    pay = rng.integers(0, 256, P * 4096).astype(np.uint8)
+    sc = rng.integers(0, 255, P * 256).astype(np.uint8)
+    sc[:4] = [0, 1, 253, 254]
+    slots = np.array([0, 1, 63, 64, 130, 191, -1, P * 64, 5], np.int32)
+    got = orc.read_k(pay, sc, slots)
+    for i, s in enumerate(slots):
+        if s < 0 or s >= P * 64:
+            assert np.all(got[i] == 0.0)
+            continue
+        codes, scales = brute.pool_token(pay, sc, int(s))
+        want = [float(v) for v in brute.decode_vector(codes, scales)]
+        assert np.array_equal(got[i], np.array(want)), s
+    # a planted token: element 2b in the low nibble, sign bit 8, scale 2^(byte-127)
+    pay2 = np.zeros(4096, np.uint8); sc2 = np.full(256, 127, np.uint8)
+    pay2[1 * 1024 + 5 * 16 + 0] = 0x9F          # token 5, block 1, byte 0: element 32 = 0xF (-6), element 33 = 0x9 (-0.5)
+    sc2[1 * 64 + 5] = 129                       # block 1 of token 5 scaled by 4
+    v = orc.read_k(pay2, sc2, np.array([5], np.int32))[0]
+    assert v[32] == -24.0 and v[33] == -2.0 and np.count_nonzero(v) == 2
