@@ -262,6 +262,28 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2)}
 
+    # ---- split-pool reader: every cached token of the workload back to fp32, one launch (not part of the step)
+    extras = {}
+    if wl.cached_slots.size:
+        rslots = t(wl.cached_slots)
+        rout = torch.empty((rslots.numel(), 128), dtype=torch.float32, device=dev)
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in rev:
+            a.record(stream)
+            b.record(stream)
+        F.read_k(payload, scale, rslots, out=rout, stream=stream)      # warm-up
+        torch.cuda.synchronize()
+        for a, b in rev:
+            F.time_next_call(a, b)
+            F.read_k(payload, scale, rslots, out=rout, stream=stream)
+        torch.cuda.synchronize()
+        r_ms = float(np.median([a.elapsed_time(b) for a, b in rev]))
+        r_bytes = 584 * rslots.numel()   # 64 code + 4 scale + 4 slot bytes read, 512 bytes written per token
+        extras["read_k"] = {"tokens": int(rslots.numel()), "us": round(r_ms * 1e3, 2),
+                            "GB/s": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del rout
+
     # ---- CPU baseline: the oracle on the same workload (bounded sample)
     cpu = None
     if not args.no_cpu_baseline:
@@ -336,6 +358,7 @@ def main():
         "kernels_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     print(json.dumps(out), flush=True)
 

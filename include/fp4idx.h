@@ -174,10 +174,27 @@ int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, cons
                 int32_t* out_idx, int64_t max_ctx, void* stream);
 
 /*
+ * Split-pool reader: pool tokens back to their values.  [P1] Summary (split
+ * writer and reader for the FP4 pool); [P2] Device memory.
+ *
+ *   payload, scale  the pool as fp4idx_write_k fills it (num_pages pages)
+ *   slot            [n_tokens] int32 pool slots (page = slot/64, in-page
+ *                   index = slot%64); a slot outside [0, num_pages*64)
+ *                   (e.g. -1 padding) reads as a zero row
+ *   out             [n_tokens, out_row_stride] fp32 (out), 16-byte aligned,
+ *                   out_row_stride >= 128 and a multiple of 4: row i gets the
+ *                   128 values e2m1(code) * 2^(scale byte - 127), exactly
+ *                   (+-inf where the value exceeds fp32; the writer never
+ *                   stores scale byte 255, whose result is unspecified)
+ */
+int fp4idx_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,
+                  int64_t n_tokens, float* out, int64_t out_row_stride, void* stream);
+
+/*
  * Kernel timing (measurement support, not part of the method).  Arms two HIP
  * events for the calling thread's next call of fp4idx_write_k, fp4idx_pack_q,
- * fp4idx_write_k_pack_q, fp4idx_mqa_logits or fp4idx_topk; each of these
- * launches exactly one kernel.
+ * fp4idx_write_k_pack_q, fp4idx_mqa_logits, fp4idx_topk or fp4idx_read_k;
+ * each of these launches exactly one kernel.
  * That kernel is then dispatched with hipExtLaunchKernel, which stamps the
  * events with the dispatch's own start and end times, so
  * hipEventElapsedTime(start, stop) is the kernel's execution time with no

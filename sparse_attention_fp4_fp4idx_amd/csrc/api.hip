@@ -173,6 +173,21 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
                                             max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }
 
+int fp4idx_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,
+                  int64_t n_tokens, float* out, int64_t out_row_stride, void* stream) {
+  const TimingScope timing_scope;
+  if (n_tokens < 0 || num_pages < 0) return FP4IDX_E_INVALID;
+  if (out_row_stride < FP4IDX_HEAD_DIM || (out_row_stride % 4) != 0) return FP4IDX_E_INVALID;
+  if (n_tokens == 0) return FP4IDX_OK;
+  if (!payload || !scale || !slot || !out) return FP4IDX_E_INVALID;
+  if (!aligned(payload, 4) || !aligned(out, 16)) return FP4IDX_E_INVALID;
+  if (n_tokens > ((int64_t)0x7FFFFFFF) * 16) return FP4IDX_E_INVALID;  // 16 lanes per token, grid x < 2^31
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_read_k(payload, scale, num_pages, slot, n_tokens, out, out_row_stride,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
                 int32_t* out_idx, int64_t max_ctx, void* stream) {
   const TimingScope timing_scope;

@@ -51,6 +51,9 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);
 
+hipError_t launch_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,
+                         int64_t n_tokens, float* out, int64_t out_stride, hipStream_t stream);
+
 hipError_t launch_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx, int32_t k,
                        int32_t* out_idx, int64_t max_ctx, hipStream_t stream);
 

@@ -27,7 +27,7 @@ SCALE_PAGE_BYTES = 256
 MAX_TOPK = 2048
 
 EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
-           "fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
+           "fp4idx_read_k", "fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
 class Fp4idxError(RuntimeError):
@@ -54,7 +54,9 @@ def load():
                                           P, i64, i32, i64, P, P, f32, P, P, P, P]
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
-    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk"):
+    lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
+    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
+                 "fp4idx_read_k"):
         getattr(lib, name).restype = ctypes.c_int
     lib.fp4idx_time_next_call.argtypes = [P, P]
     lib.fp4idx_time_next_call.restype = ctypes.c_int
@@ -290,6 +292,23 @@ def prepare_topk(logits, row_ctx, k, max_ctx, out_idx=None, stream=None):
     return Prepared("fp4idx_topk", args, keep=(logits, row_ctx, out_idx)), out_idx
 
 
+def fp4idx_read_k(payload: torch.Tensor, scale: torch.Tensor, slot: torch.Tensor, out: torch.Tensor = None,
+                  stream=None) -> torch.Tensor:
+    """Pool tokens at `slot` back to fp32 [N, 128] (a slot outside the pool gives a zero row)."""
+    n = int(slot.numel())
+    if not (payload.is_contiguous() and scale.is_contiguous() and slot.is_contiguous()):
+        raise Fp4idxError("read_k: payload, scale and slot must be contiguous")
+    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    if payload.numel() != num_pages * PAYLOAD_PAGE_BYTES or scale.numel() != num_pages * SCALE_PAGE_BYTES:
+        raise Fp4idxError("read_k: pool sizes must be num_pages*4096 and num_pages*256 bytes")
+    if out is None:
+        out = torch.empty((n, HEAD_DIM), dtype=torch.float32, device=payload.device)
+    _run("fp4idx_read_k", [_ptr(payload, _U8, "payload"), _ptr(scale, _U8, "scale"), num_pages,
+                           _ptr(slot, _I32, "slot"), n, _ptr(out, _F32, "out"),
+                           _rowstride(out, "out") if n else HEAD_DIM, _stream(stream)])
+    return out
+
+
 def _event_handle(ev):
     if ev is None:
         return None
@@ -313,4 +332,5 @@ pack_q = fp4idx_pack_q
 mqa_logits = fp4idx_mqa_logits
 topk = fp4idx_topk
 write_k_pack_q = fp4idx_write_k_pack_q
+read_k = fp4idx_read_k
 time_next_call = fp4idx_time_next_call

@@ -503,3 +503,44 @@ def test_chain_graph_replays_match_eager(F):
                     assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (forked, rep, n)
                 else:
                     assert torch.equal(got, v), (forked, rep, n)
+
+
+# ---------------------------------------------------------------- split-pool reader
+
+def test_read_k_bit_exact_on_random_pool_bytes(F, orc):
+    """Every code and every scale byte the writer can store (0..254), slots
+    in order, shuffled, repeated, padding (-1) and past the pool: fp32 bits
+    equal the oracle's exact values rounded to fp32 (exact, or +-inf)."""
+    rng = np.random.default_rng(71)
+    P = 40
+    pay = rng.integers(0, 256, P * 4096).astype(np.uint8)
+    sc = rng.integers(0, 255, P * 256).astype(np.uint8)
+    sc[:8] = [0, 1, 2, 126, 127, 128, 253, 254]
+    slots = np.concatenate([np.arange(P * 64), rng.integers(0, P * 64, 1000), [-1, P * 64, -7, 5, 5]]).astype(np.int32)
+    with np.errstate(over="ignore"):
+        want = orc.read_k(pay, sc, slots).astype(np.float32)      # exact values; overflow becomes +-inf
+    got = F.read_k(dev(pay), dev(sc), dev(slots))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_read_k_round_trips_the_writer(F, orc):
+    """write_k then read_k on the GPU: the values the oracle decodes from its
+    own pool, for a strided output."""
+    rng = np.random.default_rng(72)
+    n, num_pages = 777, 20
+    tab = W.rope_table(1 << 12)
+    k = W.bf16_normal(rng, (n, 128)); pos = rng.integers(0, 1 << 12, n).astype(np.int32)
+    slot = rng.permutation(num_pages * 64)[:n].astype(np.int32); nw = W.norm_weight(rng)
+    pay_o = np.zeros(num_pages * 4096, np.uint8); sc_o = np.zeros(num_pages * 256, np.uint8)
+    orc.write_k(k, pos, slot, nw, 1e-6, tab, pay_o, sc_o)
+    want = orc.read_k(pay_o, sc_o, slot).astype(np.float32)
+    pay_g = torch.zeros(num_pages * 4096, dtype=torch.uint8, device=DEV)
+    sc_g = torch.zeros(num_pages * 256, dtype=torch.uint8, device=DEV)
+    F.write_k(bf16(k), dev(pos), dev(slot), bf16(nw), 1e-6, bf16(tab), pay_g, sc_g)
+    out = torch.full((n, 136), 9.0, dtype=torch.float32, device=DEV)
+    F.read_k(pay_g, sc_g, dev(slot), out=out[:, :128])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(o[:, :128].view(np.uint32), want.view(np.uint32))
+    assert np.all(o[:, 128:] == 9.0)
