@@ -161,7 +161,8 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
 
 /*
  * Top-k over each logits row.  [P3] Changes (sorted top-k selection) and
- * Historical results (decode top-k ordered by position, not KV slot).
+ * Historical results (the decode selection is returned in token-position order,
+ * not in pool-slot order).
  *
  *   logits      [n_rows, logits_stride] fp32; row t uses [0, ctx[t]); finite values
  *   row_ctx_len [n_rows] int32, 0 <= ctx[t] <= max_ctx <= logits_stride

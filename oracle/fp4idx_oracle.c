@@ -453,8 +453,8 @@ int orc_logits_sampled(const uint8_t *q_fp4, const uint8_t *q_scale, const float
 }
 
 /* ---- a12: top-k ---------------------------------------------------------- */
-/* [P3] Changes: sorted top-k selection; Historical results: decode top-k is
- * ordered by position, not KV slot.
+/* [P3] Changes: sorted top-k selection; Historical results: the decode
+ * selection comes back in token-position order rather than pool-slot order.
  * Row t: among positions s < ctx[t], the K* = min(k, ctx[t]) positions with
  * the largest values, ties broken toward the lower position (reading: the
  * pages give no tie rule); written ascending by position, then -1 padding.

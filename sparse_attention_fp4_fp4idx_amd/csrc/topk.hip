@@ -1,10 +1,10 @@
 // Position-ordered top-k over logits rows on gfx950.
 //
 // "[AMD] DeepSeek-V4.1-Flash on MI350X (gfx950)", Changes (sorted top-k
-// selection) and Historical results (decode top-k is ordered by position, not
-// by KV slot).  Result for a row: the K = min(k, ctx) positions with the
-// largest values, ties resolved toward the lower position, written in
-// ascending position order and padded with -1.
+// selection) and Historical results (decode selections come back in
+// token-position order rather than pool-slot order).  Result for a row: the
+// K = min(k, ctx) positions with the largest values, ties resolved toward the
+// lower position, written in ascending position order and padded with -1.
 //
 // Rows up to 32768 positions (topk_reg_kernel), one 1024-thread work-group
 // per row, everything in registers and a few KiB of LDS:
