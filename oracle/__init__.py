@@ -66,7 +66,22 @@ def _load():
         lib.orc_logits_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, P, i64, i64, P, P, P, P, P]
         lib.orc_topk.argtypes = [P, i64, i64, P, i32, P]
         lib.orc_read_k.argtypes = [P, P, i64, P, i64, P]
-        for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk", "orc_read_k"):
+        lib.orc_fp8_exponent.argtypes = [f32]
+        lib.orc_fp8_exponent.restype = ctypes.c_int
+        lib.orc_e4m3_value.argtypes = [ctypes.c_int]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_code.argtypes = [f32, ctypes.c_int]
+        lib.orc_e4m3_code.restype = ctypes.c_int
+        lib.orc_quant_fp8_128.argtypes = [P, P, P]
+        lib.orc_dequant_fp8_128.argtypes = [P, f32, P]
+        lib.orc_encode_k_token_fp8.argtypes = [P, P, f32, P, P, P]
+        lib.orc_encode_q_head_fp8.argtypes = [P, P, P, P]
+        lib.orc_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64]
+        lib.orc_pack_q_fp8.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P]
+        lib.orc_logits_fp8.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, i64, P, i64, P, P, P]
+        lib.orc_logits_fp8_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, i64, i64, P, P, P, P, P]
+        for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk", "orc_read_k",
+                     "orc_write_k_fp8", "orc_pack_q_fp8", "orc_logits_fp8", "orc_logits_fp8_sampled"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -250,3 +265,107 @@ def read_k(payload, scale, slots) -> np.ndarray:
     out = np.empty((slots.size, D), np.float64)
     _check(_load().orc_read_k(_p(payload), _p(scale), num_pages, _p(slots), slots.size, _p(out)), "orc_read_k")
     return out
+
+
+# ---- FP8 indexer variant ------------------------------------------------------
+
+FP8_PAGE_BYTES = PAGE * (D + 4)   # 64 tokens x (128 codes + fp32 scale)
+
+
+def fp8_exponent(amax: float) -> int:
+    return int(_load().orc_fp8_exponent(ctypes.c_float(amax)))
+
+
+def e4m3_value(code: int) -> float:
+    return float(_load().orc_e4m3_value(int(code)))
+
+
+def e4m3_code(z: float, e: int) -> int:
+    return int(_load().orc_e4m3_code(ctypes.c_float(z), int(e)))
+
+
+def quant_fp8_128(z: np.ndarray):
+    z = _c(z, np.float32)
+    codes = np.empty(D, np.uint8); sc = np.empty(1, np.float32)
+    _load().orc_quant_fp8_128(_p(z), _p(codes), _p(sc))
+    return codes, np.float32(sc[0])
+
+
+def dequant_fp8_128(codes, scale) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    out = np.empty(D, np.float64)
+    _load().orc_dequant_fp8_128(_p(codes), ctypes.c_float(float(scale)), _p(out))
+    return out
+
+
+def encode_k_token_fp8(k_row, norm_w, eps, cs_row):
+    k_row = _c(k_row, np.uint16); norm_w = _c(norm_w, np.uint16); cs_row = _c(cs_row, np.uint16)
+    codes = np.empty(D, np.uint8); sc = np.empty(1, np.float32)
+    _load().orc_encode_k_token_fp8(_p(k_row), _p(norm_w), ctypes.c_float(eps), _p(cs_row), _p(codes), _p(sc))
+    return codes, np.float32(sc[0])
+
+
+def encode_q_head_fp8(q_row, cs_row):
+    q_row = _c(q_row, np.uint16); cs_row = _c(cs_row, np.uint16)
+    codes = np.empty(D, np.uint8); sc = np.empty(1, np.float32)
+    _load().orc_encode_q_head_fp8(_p(q_row), _p(cs_row), _p(codes), _p(sc))
+    return codes, np.float32(sc[0])
+
+
+def write_k_fp8(k, pos, slot, norm_w, eps, cos_sin, pool):
+    """Encode K rows into the fused FP8 pool (num_pages * 8448 bytes, in place)."""
+    k = _c(k, np.uint16); pos = _c(pos, np.int32); slot = _c(slot, np.int32)
+    norm_w = _c(norm_w, np.uint16); cos_sin = _c(cos_sin, np.uint16)
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.size % FP8_PAGE_BYTES == 0
+    n = k.shape[0]
+    rc = _load().orc_write_k_fp8(_p(k), n, k.shape[1] if n else D, _p(pos), _p(slot), _p(norm_w),
+                                 ctypes.c_float(eps), _p(cos_sin), cos_sin.shape[0], _p(pool),
+                                 pool.size // FP8_PAGE_BYTES)
+    _check(rc, "write_k_fp8")
+
+
+def pack_q_fp8(q, pos, cos_sin, w_in, w_scale=1.0):
+    """q: uint16 [T, H, 128] -> (q_fp8 [T,H,128] u8, q_scale [T,H] f32, w_out [T,H] f32)."""
+    q = _c(q, np.uint16); pos = _c(pos, np.int32); cos_sin = _c(cos_sin, np.uint16)
+    w_in = _c(w_in, np.float32)
+    T, H = q.shape[0], q.shape[1]
+    q_fp8 = np.empty((T, H, D), np.uint8); q_scale = np.empty((T, H), np.float32)
+    w_out = np.empty((T, H), np.float32)
+    rc = _load().orc_pack_q_fp8(_p(q), T, H, H * D, _p(pos), _p(cos_sin), cos_sin.shape[0], _p(w_in),
+                                ctypes.c_float(w_scale), _p(q_fp8), _p(q_scale), _p(w_out))
+    _check(rc, "pack_q_fp8")
+    return q_fp8, q_scale, w_out
+
+
+def logits_fp8(q_fp8, q_scale, w, indptr, row_ctx, block_table, pool, logits_stride=None, want_f64=False):
+    """FP8-variant logits [T, stride] (fp32; entries >= ctx stay NaN); with
+    want_f64 also the fp64 values and the T, A tolerance scales."""
+    q_fp8 = _c(q_fp8, np.uint8); q_scale = _c(q_scale, np.float32); w = _c(w, np.float32)
+    indptr = _c(indptr, np.int32); row_ctx = _c(row_ctx, np.int32); bt = _c(block_table, np.int32)
+    T, H = q_fp8.shape[0], q_fp8.shape[1]
+    stride = int(logits_stride if logits_stride is not None else max(1, int(row_ctx.max(initial=0))))
+    out = np.full((T, stride), np.nan, np.float32)
+    f64 = np.full((T, stride), np.nan, np.float64) if want_f64 else None
+    tol = np.full((T, stride), np.nan, np.float64) if want_f64 else None
+    absr = np.full((T, stride), np.nan, np.float64) if want_f64 else None
+    rc = _load().orc_logits_fp8(_p(q_fp8), _p(q_scale), _p(w), T, H, _p(indptr), len(indptr) - 1, _p(row_ctx),
+                                _p(bt), bt.shape[1], _p(pool), pool.size // FP8_PAGE_BYTES, _p(out), stride,
+                                _p(f64) if want_f64 else None, _p(tol) if want_f64 else None,
+                                _p(absr) if want_f64 else None)
+    _check(rc, "logits_fp8")
+    return (out, f64, tol, absr) if want_f64 else out
+
+
+def logits_fp8_sampled(q_fp8, q_scale, w, indptr, block_table, pool, rows, toks):
+    """fp64 FP8-variant logits at (rows[i], toks[i]) with their T and A scales."""
+    q_fp8 = _c(q_fp8, np.uint8); q_scale = _c(q_scale, np.float32); w = _c(w, np.float32)
+    indptr = _c(indptr, np.int32); bt = _c(block_table, np.int32)
+    rows = _c(rows, np.int64); toks = _c(toks, np.int64)
+    H = q_fp8.shape[1]
+    out = np.empty(rows.size, np.float64); tol = np.empty(rows.size, np.float64)
+    absr = np.empty(rows.size, np.float64)
+    rc = _load().orc_logits_fp8_sampled(_p(q_fp8), _p(q_scale), _p(w), H, _p(indptr), len(indptr) - 1, _p(bt),
+                                        bt.shape[1], _p(pool), pool.size // FP8_PAGE_BYTES, rows.size, _p(rows),
+                                        _p(toks), _p(out), _p(tol), _p(absr))
+    _check(rc, "logits_fp8_sampled")
+    return out, tol, absr

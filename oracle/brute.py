@@ -81,3 +81,53 @@ def logit(qcodes, qscales, w, kcodes, kscales) -> Fraction:
         if d > 0:
             total += exact(w[h]) * d
     return total
+
+
+# ---- FP8 E4M3 (OCP OFP8 v1.0): bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN
+
+def e4m3_magnitude(code: int) -> Fraction:
+    """Exact magnitude of an e4m3 code (sign bit ignored); codes 0x7F/0xFF are NaN."""
+    ex, m = (code >> 3) & 15, code & 7
+    if ex == 0:
+        return Fraction(m, 8) * Fraction(2) ** -6
+    return (1 + Fraction(m, 8)) * Fraction(2) ** (ex - 7)
+
+
+def fp8_exponent(amax) -> int:
+    """Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]."""
+    a = exact(amax)
+    if a == 0:
+        return -127
+    e = -127
+    while e < 127 and Fraction(448) * Fraction(2) ** e < a:
+        e += 1
+    return e
+
+
+def e4m3_code(z, e: int) -> int:
+    """Nearest e4m3 magnitude to |z| / 2^e, ties to the even code; sign bit 7."""
+    v = abs(exact(z)) / Fraction(2) ** e
+    best, bd = 0, v
+    for c in range(1, 127):
+        d = abs(v - e4m3_magnitude(c))
+        if d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    neg = np.signbit(np.float32(z))
+    return best | (0x80 if neg else 0)
+
+
+def fp8_pool_token(pool: np.ndarray, slot: int):
+    """One token of the fused FP8 pool through its page shape: 64 x 128 code
+    bytes, then 64 fp32 scales."""
+    P = pool.size // 8448
+    pages = pool.reshape(P, 8448)
+    page, t = divmod(int(slot), 64)
+    codes = pages[page, :8192].reshape(64, 128)[t]
+    scale = pages[page, 8192:].view(np.float32)[t]
+    return codes, scale
+
+
+def fp8_decode(codes, scale):
+    """128 exact values of an FP8 token (codes + fp32 power-of-two scale)."""
+    s = exact(scale)
+    return [(-1 if c & 0x80 else 1) * e4m3_magnitude(int(c)) * s for c in codes]

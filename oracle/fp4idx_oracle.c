@@ -452,6 +452,214 @@ int orc_logits_sampled(const uint8_t *q_fp4, const uint8_t *q_scale, const float
   return bad ? -2 : 0;
 }
 
+/* ==== FP8 indexer variant ================================================== */
+/* [P2] Device memory and sizing: the FP8 indexer keeps 132 bytes per
+ * compressed token in one fused region, where the FP4 indexer splits a
+ * 64-byte payload and 4 scale bytes.  The pages give no byte-level layout;
+ * the readings taken here:
+ *   - 128 e4m3 codes (OCP FP8 E4M3: bias 7, 3 mantissa bits, largest finite
+ *     448, subnormal step 2^-9, 0x7F/0xFF NaN) + one fp32 scale per token;
+ *   - the scale is the power of two 2^e with e the smallest integer such
+ *     that 448 * 2^e >= amax over the token's 128 values, clamped to
+ *     [-127, 127] (amax = 0 gives -127), so z / 2^e is exact and the only
+ *     rounding is onto the e4m3 grid: nearest, ties to the even code, the
+ *     sign of zero kept;
+ *   - the same steps as the FP4 writer up to the Hadamard (RMSNorm, RoPE,
+ *     Hadamard in the canonical fp32 order), and Q per (row, head) likewise
+ *     without RMSNorm;
+ *   - page layout: [64 tokens][128 code bytes] then [64][fp32 scale], 8448
+ *     bytes per page, code byte i of a token = element i. */
+#define FP8_MAX 448.0
+#define PAGE8_BYTES (PAGE * (D + 4))
+
+int orc_fp8_exponent(float amax) {
+  double a = (double)amax;
+  int e;
+  if (a == 0.0) return -127;
+  (void)frexp(a, &e); /* start near the answer, then walk to the definition */
+  e -= 9;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  while (e < 127 && ldexp(FP8_MAX, e) < a) ++e;
+  while (e > -127 && ldexp(FP8_MAX, e - 1) >= a) --e;
+  return e;
+}
+
+/* Value of an e4m3 magnitude code 0..126 (bit 7 is the sign). */
+double orc_e4m3_value(int code) {
+  int ex = (code >> 3) & 15, m = code & 7;
+  double v = ex == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ex - 7);
+  return (code & 0x80) ? -v : v;
+}
+
+/* Code of z at token exponent e: the e4m3 magnitude nearest to |z| 2^-e
+ * (exact), ties to the even code, sign bit of z kept. */
+int orc_e4m3_code(float z, int e) {
+  double v = ldexp(fabs((double)z), -e);
+  int best = 0;
+  double bd = v;
+  for (int c = 1; c <= 126; ++c) {
+    double d = fabs(v - orc_e4m3_value(c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return best | (signbit(z) ? 0x80 : 0);
+}
+
+/* One 128-vector: codes[128] and its fp32 scale 2^e. */
+void orc_quant_fp8_128(const float *z, uint8_t *codes, float *scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < D; ++i) {
+    float m = fabsf(z[i]);
+    if (m > amax) amax = m;
+  }
+  int e = orc_fp8_exponent(amax);
+  *scale = (float)ldexp(1.0, e); /* exact: 2^-127 .. 2^127 are fp32 values (2^-127 subnormal) */
+  for (int i = 0; i < D; ++i) codes[i] = (uint8_t)orc_e4m3_code(z[i], e);
+}
+
+void orc_encode_k_token_fp8(const uint16_t *k_row, const uint16_t *norm_w, float eps, const uint16_t *cs_row,
+                            uint8_t *codes, float *scale) {
+  float x[D], g[D], y[D], cs[ROPE];
+  for (int i = 0; i < D; ++i) {
+    x[i] = f32_of_bf16(k_row[i]);
+    g[i] = f32_of_bf16(norm_w[i]);
+  }
+  for (int i = 0; i < ROPE; ++i) cs[i] = f32_of_bf16(cs_row[i]);
+  orc_rmsnorm128(x, g, eps, y);
+  orc_rope64(y, cs);
+  orc_fwht128(y);
+  orc_quant_fp8_128(y, codes, scale);
+}
+
+void orc_encode_q_head_fp8(const uint16_t *q_row, const uint16_t *cs_row, uint8_t *codes, float *scale) {
+  float y[D], cs[ROPE];
+  for (int i = 0; i < D; ++i) y[i] = f32_of_bf16(q_row[i]);
+  for (int i = 0; i < ROPE; ++i) cs[i] = f32_of_bf16(cs_row[i]);
+  orc_rope64(y, cs);
+  orc_fwht128(y);
+  orc_quant_fp8_128(y, codes, scale);
+}
+
+/* K tokens into the fused FP8 pool (num_pages * 8448 bytes); slot < 0 skips,
+ * duplicate slots are rejected as in orc_write_k. */
+int orc_write_k_fp8(const uint16_t *k, int64_t n_tokens, int64_t k_row_stride, const int32_t *pos,
+                    const int32_t *slot, const uint16_t *norm_w, float eps, const uint16_t *cos_sin,
+                    int32_t max_pos, uint8_t *pool, int64_t num_pages) {
+  if (n_tokens < 0 || k_row_stride < D || max_pos <= 0 || num_pages < 0) return -1;
+  for (int64_t n = 0; n < n_tokens; ++n) {
+    if (slot[n] >= 0 && (int64_t)slot[n] >= num_pages * PAGE) return -2;
+    if (slot[n] >= 0 && (pos[n] < 0 || pos[n] >= max_pos)) return -3;
+  }
+  if (n_tokens > 0 && num_pages > 0) {
+    uint8_t *seen = (uint8_t *)calloc((size_t)(num_pages * PAGE), 1);
+    if (!seen) return -4;
+    int dup = 0;
+    for (int64_t n = 0; n < n_tokens; ++n) {
+      if (slot[n] < 0) continue;
+      if (seen[slot[n]]) dup = 1;
+      seen[slot[n]] = 1;
+    }
+    free(seen);
+    if (dup) return -5;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < n_tokens; ++n) {
+    if (slot[n] < 0) continue;
+    uint8_t codes[D];
+    float sc;
+    orc_encode_k_token_fp8(k + n * k_row_stride, norm_w, eps, cos_sin + (int64_t)pos[n] * ROPE, codes, &sc);
+    int64_t page = slot[n] / PAGE, t = slot[n] % PAGE;
+    memcpy(pool + page * PAGE8_BYTES + t * D, codes, D);
+    memcpy(pool + page * PAGE8_BYTES + PAGE * D + t * 4, &sc, 4);
+  }
+  return 0;
+}
+
+/* Q rows: q_fp8[t][h][128] codes, q_scale[t][h] fp32, w_out = w_in * w_scale. */
+int orc_pack_q_fp8(const uint16_t *q, int64_t n_rows, int32_t n_heads, int64_t q_row_stride, const int32_t *pos,
+                   const uint16_t *cos_sin, int32_t max_pos, const float *w_in, float w_scale, uint8_t *q_fp8,
+                   float *q_scale, float *w_out) {
+  if (n_rows < 0 || n_heads <= 0 || q_row_stride < (int64_t)n_heads * D || max_pos <= 0) return -1;
+  for (int64_t t = 0; t < n_rows; ++t)
+    if (pos[t] < 0 || pos[t] >= max_pos) return -3;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    for (int h = 0; h < n_heads; ++h) {
+      int64_t o = t * n_heads + h;
+      orc_encode_q_head_fp8(q + t * q_row_stride + (int64_t)h * D, cos_sin + (int64_t)pos[t] * ROPE, q_fp8 + o * D,
+                            q_scale + o);
+      w_out[o] = w_in[o] * w_scale;
+    }
+  }
+  return 0;
+}
+
+/* Exact values of one 128-vector of e4m3 codes with its fp32 scale. */
+void orc_dequant_fp8_128(const uint8_t *codes, float scale, double *out) {
+  for (int i = 0; i < D; ++i) out[i] = orc_e4m3_value(codes[i]) * (double)scale;
+}
+
+static void dequant_token_fp8(const uint8_t *pool, int64_t page, int t, double *out) {
+  float sc;
+  memcpy(&sc, pool + page * PAGE8_BYTES + PAGE * D + t * 4, 4);
+  orc_dequant_fp8_128(pool + page * PAGE8_BYTES + t * D, sc, out);
+}
+
+/* The same score on the FP8 variant's exact values (fp64, rounded once). */
+int orc_logits_fp8(const uint8_t *q_fp8, const float *q_scale, const float *w, int64_t n_rows, int32_t n_heads,
+                   const int32_t *indptr, int32_t n_reqs, const int32_t *row_ctx, const int32_t *block_table,
+                   int32_t bt_stride, const uint8_t *pool, int64_t num_pages, float *logits, int64_t logits_stride,
+                   double *logits_f64, double *tol_ref, double *abs_ref) {
+  int rc = check_logits_args(n_rows, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride, num_pages,
+                             logits_stride);
+  if (rc) return rc;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    int b = row_request(indptr, n_reqs, t);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)n_heads * D);
+    double kd[D];
+    for (int h = 0; h < n_heads; ++h) orc_dequant_fp8_128(q_fp8 + (t * n_heads + h) * D, q_scale[t * n_heads + h], qd + h * D);
+    for (int64_t s = 0; s < row_ctx[t]; ++s) {
+      int64_t page = block_table[(int64_t)b * bt_stride + s / PAGE];
+      dequant_token_fp8(pool, page, (int)(s % PAGE), kd);
+      double T, A;
+      double L = score_one(qd, w + t * n_heads, n_heads, kd, &T, &A);
+      logits[t * logits_stride + s] = (float)L;
+      if (logits_f64) logits_f64[t * logits_stride + s] = L;
+      if (tol_ref) tol_ref[t * logits_stride + s] = T;
+      if (abs_ref) abs_ref[t * logits_stride + s] = A;
+    }
+    free(qd);
+  }
+  return 0;
+}
+
+int orc_logits_fp8_sampled(const uint8_t *q_fp8, const float *q_scale, const float *w, int32_t n_heads,
+                           const int32_t *indptr, int32_t n_reqs, const int32_t *block_table, int32_t bt_stride,
+                           const uint8_t *pool, int64_t num_pages, int64_t n_samples, const int64_t *rows,
+                           const int64_t *toks, double *out, double *tol_ref, double *abs_ref) {
+  if (n_heads <= 0 || n_samples < 0) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+  for (int64_t i = 0; i < n_samples; ++i) {
+    int64_t t = rows[i], s = toks[i];
+    int b = row_request(indptr, n_reqs, t);
+    if (b < 0 || s < 0 || s / PAGE >= bt_stride) { bad = 1; continue; }
+    int64_t page = block_table[(int64_t)b * bt_stride + s / PAGE];
+    if (page < 0 || page >= num_pages) { bad = 1; continue; }
+    double *qd = (double *)malloc(sizeof(double) * (size_t)n_heads * D);
+    double kd[D];
+    for (int h = 0; h < n_heads; ++h) orc_dequant_fp8_128(q_fp8 + (t * n_heads + h) * D, q_scale[t * n_heads + h], qd + h * D);
+    dequant_token_fp8(pool, page, (int)(s % PAGE), kd);
+    out[i] = score_one(qd, w + t * n_heads, n_heads, kd, &tol_ref[i], &abs_ref[i]);
+    free(qd);
+  }
+  return bad ? -2 : 0;
+}
+
 /* ---- a12: top-k ---------------------------------------------------------- */
 /* [P3] Changes: sorted top-k selection; Historical results: the decode
  * selection comes back in token-position order rather than pool-slot order.

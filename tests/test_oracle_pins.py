@@ -478,3 +478,147 @@ def test_reader_matches_exact_decoding_through_the_page_shapes(orc):
     sc2[1 * 64 + 5] = 129                       # block 1 of token 5 scaled by 4
     v = orc.read_k(pay2, sc2, np.array([5], np.int32))[0]
     assert v[32] == -24.0 and v[33] == -2.0 and np.count_nonzero(v) == 2
+
+
+# ---------------------------------------------------------------- FP8 indexer variant
+
+def test_golden_e4m3_values_match_oracle(orc):
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "e4m3_ocp_values.txt")) if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 10
+    for code_s, val_s in rows:
+        code, val = int(code_s), float(val_s)
+        assert orc.e4m3_value(code) == val and np.signbit(orc.e4m3_value(code)) == np.signbit(val)
+        assert float(brute.e4m3_magnitude(code)) == abs(val)
+        for e in (-9, 0, 4):      # each grid value scaled by 2^e encodes to its own code
+            z = np.float32(val * 2.0 ** e)
+            assert orc.e4m3_code(z, e) == code, (code, e)
+    mags = [orc.e4m3_value(c) for c in range(127)]
+    assert all(a < b for a, b in zip(mags, mags[1:])) and mags[-1] == 448.0
+
+
+def test_fp8_exponent_against_exact_definition(orc):
+    edge = []
+    for k in (-140, -127, -126, -20, -1, 0, 1, 50, 119):
+        base = 448.0 * 2.0 ** k
+        for f in (1.0, 1.0 - 2 ** -24, 1.0 + 2 ** -23, 0.5, 0.5000001, 0.875):
+            v = np.float32(base * f)
+            if np.isfinite(v):
+                edge.append(v)
+    edge += [np.float32(0.0), np.float32(1e-45), np.float32(1.17e-38), np.float32(3.4e38), np.float32(1.0)]
+    rng = np.random.default_rng(81)
+    edge += list((np.abs(rng.standard_normal(300)) * 10.0 ** rng.integers(-30, 30, 300)).astype(np.float32))
+    for v in edge:
+        a = abs(np.float32(v))
+        e = orc.fp8_exponent(a)
+        assert e == brute.fp8_exponent(a), a
+        if a > 448 * 2.0 ** -127:
+            r = Fraction(float(a)) / Fraction(2) ** e
+            assert Fraction(224) < r <= Fraction(448)
+
+
+def test_fp8_codes_match_exact_nearest_even(orc):
+    """Codes against rational nearest-with-ties-to-even on random values over
+    many binades (subnormal range included), exact midpoints and signed zero."""
+    rng = np.random.default_rng(82)
+    vals = list((rng.standard_normal(400) * 2.0 ** rng.integers(-12, 10, 400)).astype(np.float32))
+    # midpoints between neighbouring grid values (ties must go to the even code)
+    for c in list(range(0, 20)) + list(range(60, 70)) + [120, 124, 125]:
+        mid = (brute.e4m3_magnitude(c) + brute.e4m3_magnitude(c + 1)) / 2
+        vals.append(np.float32(float(mid)))
+        vals.append(np.float32(-float(mid)))
+    vals += [np.float32(-0.0), np.float32(0.0), np.float32(448.0), np.float32(447.99997)]
+    for z in vals:
+        for e in (0, -3, 5):
+            zz = np.float32(float(z) * 2.0 ** e)
+            if abs(float(zz)) / 2.0 ** e > 448 or not np.isfinite(zz):
+                continue
+            assert orc.e4m3_code(zz, e) == brute.e4m3_code(zz, e), (zz, e)
+
+
+def test_fp8_pool_footprint_is_132_bytes(orc):
+    """Writing one token changes exactly its 128 code bytes and 4 scale bytes
+    at the fused page layout, and the scale is a power of two."""
+    rng = np.random.default_rng(83)
+    tab = W.rope_table(64)
+    pool = np.full(2 * 8448, 0xA5, np.uint8)
+    k = W.bf16_normal(rng, (1, 128))
+    orc.write_k_fp8(k, np.array([7], np.int32), np.array([64 + 9], np.int32), W.norm_weight(rng), 1e-6, tab, pool)
+    changed = np.nonzero(pool != 0xA5)[0]
+    allowed = set(range(8448 + 9 * 128, 8448 + 10 * 128)) | set(range(8448 + 8192 + 36, 8448 + 8192 + 40))
+    assert set(changed.tolist()) <= allowed and len(changed) >= 128
+    codes, sc = brute.fp8_pool_token(pool, 64 + 9)
+    m, ex = np.frexp(np.float64(sc))
+    assert m == 0.5
+
+
+def test_fp8_encoding_decodes_within_half_a_step_of_the_fp64_pipeline(orc):
+    rng = np.random.default_rng(84)
+    tab = W.rope_table(4096)
+    n = 48
+    k = W.bf16_normal(rng, (n, 128)); g = W.norm_weight(rng)
+    pos = rng.integers(0, 4096, n).astype(np.int32)
+    slot = rng.permutation(128)[:n].astype(np.int32)
+    pool = np.zeros(2 * 8448, np.uint8)
+    orc.write_k_fp8(k, pos, slot, g, 1e-6, tab, pool)
+    tabf = W.f32_from_bf16(tab).astype(np.float64)
+    for i in range(n):
+        x = W.f32_from_bf16(k[i]).astype(np.float64)
+        y = x / np.sqrt(np.mean(x * x) + 1e-6) * W.f32_from_bf16(g)
+        z = (y[:32] + 1j * y[32:64]) * (tabf[pos[i], :32] + 1j * tabf[pos[i], 32:])
+        y[:32], y[32:64] = z.real, z.imag
+        ref = (H128 @ y) / np.sqrt(128.0)
+        codes, sc = brute.fp8_pool_token(pool, slot[i])
+        dec = np.array([float(v) for v in brute.fp8_decode(codes, sc)])
+        s = float(sc)
+        a = np.abs(ref) / s
+        # half a step at each value's binade (step 2^(k-3), k >= -6), plus fp32 pipeline slack
+        kk = np.maximum(np.floor(np.log2(np.maximum(a, 2.0 ** -10))), -6)
+        assert np.all(np.abs(dec - ref) <= 0.5 * 2.0 ** (kk - 3) * s * (1 + 1e-6) + 1e-6 * np.abs(ref).max()), i
+        assert 224 < np.abs(ref).max() / s <= 448 * (1 + 1e-5)
+
+
+def test_fp8_q_pack_matches_k_encoding_without_norm(orc):
+    rng = np.random.default_rng(85)
+    tab = W.rope_table(512)
+    q = W.bf16_normal(rng, (2, 3, 128))
+    pos = np.array([5, 300], np.int32)
+    w = rng.uniform(0, 1, (2, 3)).astype(np.float32)
+    qf, qs, wo = orc.pack_q_fp8(q, pos, tab, w, 2.0)
+    assert np.array_equal(wo, w * np.float32(2.0))
+    for t in range(2):
+        for h in range(3):
+            c, s = orc.encode_q_head_fp8(q[t, h], tab[pos[t]])
+            assert np.array_equal(qf[t, h], c) and qs[t, h] == s
+    kq = W.bf16_from_f32(np.ones(128, np.float32))
+    ck, sk = orc.encode_k_token_fp8(kq, W.bf16_from_f32(np.ones(128, np.float32)), 0.0, tab[9])
+    cq, sq = orc.encode_q_head_fp8(kq, tab[9])
+    assert np.array_equal(ck, cq) and sk == sq
+
+
+def test_fp8_logits_against_exact_rational_brute_force(orc):
+    rng = np.random.default_rng(86)
+    H, ctx, rows = 3, (5, 70), (1, 2)
+    indptr = np.array([0, 1, 3], np.int32)
+    row_ctx = np.array([5, 70, 70], np.int32)
+    num_pages = 4
+    bt = np.array([[2, -1], [0, 3]], np.int32)
+    pool = np.zeros(num_pages * 8448, np.uint8)
+    pv = pool.reshape(num_pages, 8448)
+    codes = rng.integers(0, 256, (num_pages, 8192)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11                           # no NaN codes
+    pv[:, :8192] = codes
+    pv[:, 8192:].view(np.float32)[:] = (2.0 ** rng.integers(-12, 4, (num_pages, 64))).astype(np.float32)
+    qf = rng.integers(0, 256, (3, H, 128)).astype(np.uint8); qf[(qf & 0x7F) == 0x7F] = 0x22
+    qs = (2.0 ** rng.integers(-6, 3, (3, H))).astype(np.float32)
+    w = rng.uniform(-1, 1, (3, H)).astype(np.float32)
+    out, f64, tol, _ = orc.logits_fp8(qf, qs, w, indptr, row_ctx, bt, pool, logits_stride=80, want_f64=True)
+    for b in range(2):
+        for t in range(indptr[b], indptr[b + 1]):
+            qd = [brute.fp8_decode(qf[t, h], qs[t, h]) for h in range(H)]
+            for s in range(row_ctx[t]):
+                kc, ks = brute.fp8_pool_token(pool, bt[b, s // 64] * 64 + s % 64)
+                kd = brute.fp8_decode(kc, ks)
+                ex = sum(Fraction(float(w[t, h])) * max(sum(a * c for a, c in zip(qd[h], kd)), Fraction(0))
+                         for h in range(H))
+                assert abs(f64[t, s] - float(ex)) <= 1e-12 * abs(float(ex)) + 1e-300
+                assert out[t, s] == np.float32(float(ex))
