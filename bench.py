@@ -21,6 +21,10 @@ where each kernel carries HIP events that its own dispatch stamps with its
 start and end times (fp4idx_time_next_call -> hipExtLaunchKernel); they feed
 the roofline figures.
 
+The same step is then timed on the FP8 indexer cache (132-byte fused tokens,
+the layout the FP4 cache replaces) and reported under extras.fp8_cache; the
+headline value is the FP4 path's.
+
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
@@ -82,6 +86,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode batch 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache comparison leg")
     ap.add_argument("--launch", choices=("prepared", "graph"), default="prepared",
                     help="timed steps as prepared library calls (default) or as HIP graph replays")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to defeat the cache)")
@@ -133,52 +138,122 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] pool filled ({time.time() - t0:.1f}s)")
 
-    # ---- per-step inputs and rotating copies
     T, H, k = wl.n_rows, wl.heads, wl.topk
-    base = dict(payload=payload, scale=scale, q=b16(wl.q), w=t(wl.w), k_new=b16(wl.k_new))
-    step_bytes = sum(v.numel() * v.element_size() for v in base.values()) + T * wl.max_ctx * 4 * 2
-    copies = args.copies or max(2, int(np.ceil(2 * CACHE_BYTES / step_bytes)))
-    copies = min(copies, max(2, int(0.5 * torch.cuda.mem_get_info()[0] // step_bytes)))
-    sets = []
-    for c in range(copies):
-        s = {n: (v if c == 0 else v.clone()) for n, v in base.items()}
-        s["logits"] = torch.empty((T, wl.max_ctx), dtype=torch.float32, device=dev)
-        s["q_fp4"] = torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
-        s["q_scale"] = torch.empty((T, H, 4), dtype=torch.uint8, device=dev)
-        s["w_out"] = torch.empty((T, H), dtype=torch.float32, device=dev)
-        s["top"] = torch.empty((T, k), dtype=torch.int32, device=dev)
-        sets.append(s)
     pos_new, slot_new = t(wl.pos_new), t(wl.slot_new)
     pos_q, indptr, ctx, bt = t(wl.pos_q), t(wl.req_row_indptr), t(wl.row_ctx), t(wl.block_table)
-    log(f"[bench] {copies} input copies of {step_bytes / 1e6:.1f} MB ({time.time() - t0:.1f}s)")
-
     names = ("write_k", "pack_q", "mqa_logits", "topk")
 
-    def step(s, strm, ev=None):
-        """One pass of the path on stream strm.  The timed steps encode the
-        step's K tokens and query rows in one launch (fp4idx_write_k_pack_q);
-        the kernel-timing pass (ev given) launches the two encoders separately
-        so that each component kernel gets its own duration."""
-        def arm(i):   # events stamped with kernel i's own start / end (hipExtLaunchKernel)
-            if ev is not None:
-                F.time_next_call(ev[i][0], ev[i][1])
-        if ev is None:
-            F.write_k_pack_q(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"],
-                             s["q"], pos_q, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
-        else:
-            arm(0)
-            F.write_k(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s["payload"], s["scale"], stream=strm)
-            arm(1)
-            F.pack_q(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_fp4"], s["q_scale"], s["w_out"], stream=strm)
-        arm(2)
-        F.mqa_logits(s["q_fp4"], s["q_scale"], s["w_out"], indptr, ctx, bt, s["payload"], s["scale"],
-                     wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=strm)
-        arm(3)
-        F.topk(s["logits"], ctx, k, wl.max_ctx, out_idx=s["top"], stream=strm)
+    def run_cache(fp8: bool, pools: dict):
+        """Time the step on one cache format: rotating input copies, the timed
+        prepared calls (or graph replays), then the per-kernel event pass.
+        Returns (ms_per_step, per-kernel ms, copies)."""
+        qcode_b = 128 if fp8 else 64
+        base = dict(pools, q=b16(wl.q), w=t(wl.w), k_new=b16(wl.k_new))
+        step_bytes = sum(v.numel() * v.element_size() for v in base.values()) + T * wl.max_ctx * 4 * 2
+        copies = args.copies or max(2, int(np.ceil(2 * CACHE_BYTES / step_bytes)))
+        copies = min(copies, max(2, int(0.5 * torch.cuda.mem_get_info()[0] // step_bytes)))
+        sets = []
+        for c in range(copies):
+            s = {n: (v if c == 0 else v.clone()) for n, v in base.items()}
+            s["logits"] = torch.empty((T, wl.max_ctx), dtype=torch.float32, device=dev)
+            s["q_code"] = torch.empty((T, H, qcode_b), dtype=torch.uint8, device=dev)
+            s["q_scale"] = (torch.empty((T, H), dtype=torch.float32, device=dev) if fp8
+                            else torch.empty((T, H, 4), dtype=torch.uint8, device=dev))
+            s["w_out"] = torch.empty((T, H), dtype=torch.float32, device=dev)
+            s["top"] = torch.empty((T, k), dtype=torch.int32, device=dev)
+            sets.append(s)
+        log(f"[bench] {'fp8' if fp8 else 'fp4'}: {copies} input copies of {step_bytes / 1e6:.1f} MB "
+            f"({time.time() - t0:.1f}s)")
 
-    for i in range(args.warmup):
-        step(sets[i % copies], stream)
-    torch.cuda.synchronize()
+        def pool_args(s):
+            return (s["pool"],) if fp8 else (s["payload"], s["scale"])
+
+        def step(s, strm, ev=None):
+            """One pass of the path on stream strm.  The timed steps encode the
+            step's K tokens and query rows in one launch (write_k_pack_q); the
+            kernel-timing pass (ev given) launches the two encoders separately
+            so that each component kernel gets its own duration."""
+            def arm(i):   # events stamped with kernel i's own start / end (hipExtLaunchKernel)
+                if ev is not None:
+                    F.time_next_call(ev[i][0], ev[i][1])
+            if ev is None:
+                (F.write_k_pack_q_fp8 if fp8 else F.write_k_pack_q)(
+                    s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, *pool_args(s), s["q"], pos_q, s["w"],
+                    wl.w_scale, s["q_code"], s["q_scale"], s["w_out"], stream=strm)
+            else:
+                arm(0)
+                (F.write_k_fp8 if fp8 else F.write_k)(s["k_new"], pos_new, slot_new, norm_w, wl.eps, tab,
+                                                      *pool_args(s), stream=strm)
+                arm(1)
+                (F.pack_q_fp8 if fp8 else F.pack_q)(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_code"],
+                                                    s["q_scale"], s["w_out"], stream=strm)
+            arm(2)
+            (F.mqa_logits_fp8 if fp8 else F.mqa_logits)(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt,
+                                                        *pool_args(s), wl.max_rows_per_req, wl.max_ctx,
+                                                        logits=s["logits"], stream=strm)
+            arm(3)
+            F.topk(s["logits"], ctx, k, wl.max_ctx, out_idx=s["top"], stream=strm)
+
+        for i in range(args.warmup):
+            step(sets[i % copies], stream)
+        torch.cuda.synchronize()
+
+        # the timed steps: per input copy either three prepared library calls
+        # (arguments marshalled once, one ctypes call each) or one captured HIP graph
+        runners = []
+        if args.launch == "graph":
+            cap = torch.cuda.Stream()
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step(sets[c], torch.cuda.current_stream())
+                runners.append(g.replay)
+                sets[c]["graph"] = g
+        else:
+            for c in range(copies):
+                s_ = sets[c]
+                pw, _ = (F.prepare_write_k_pack_q_fp8 if fp8 else F.prepare_write_k_pack_q)(
+                    s_["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, *pool_args(s_), s_["q"], pos_q, s_["w"],
+                    wl.w_scale, s_["q_code"], s_["q_scale"], s_["w_out"], stream=stream)
+                pl, _ = (F.prepare_mqa_logits_fp8 if fp8 else F.prepare_mqa_logits)(
+                    s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, *pool_args(s_), wl.max_rows_per_req,
+                    wl.max_ctx, logits=s_["logits"], stream=stream)
+                pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
+
+                def run(pw=pw, pl=pl, pt=pt):
+                    pw()
+                    pl()
+                    pt()
+                runners.append(run)
+        for c in range(copies):
+            runners[c]()
+        torch.cuda.synchronize()
+
+        # timed region: K steps, bracketed by synchronize
+        torch.cuda.synchronize()
+        start = time.perf_counter()
+        for i in range(args.steps):
+            runners[i % copies]()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - start
+
+        # kernel durations: the same K steps launched eagerly on the launch stream, each kernel carrying
+        # HIP events that its own dispatch stamps with its start and end times (no marker packets in between)
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+               for _ in range(args.steps)]
+        for row in evs:          # create the HIP events (torch creates them on first record)
+            for a, b in row:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(sets[i % copies], stream, evs[i])
+        torch.cuda.synchronize()
+        per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
+                      for j, n in enumerate(names)}
+        del sets, runners
+        return elapsed * 1e3 / args.steps, per_kernel, copies
+
     if args.calib_copy:
         # reference for rocprofv3 FETCH_SIZE / WRITE_SIZE: reads and writes exactly MB MiB
         csrc = torch.empty(args.calib_copy << 20, dtype=torch.uint8, device=dev)
@@ -188,63 +263,9 @@ def main():
         torch.cuda.synchronize()
         del csrc, cdst
 
-    # ---- one HIP graph per input copy: the step's four launches, replayed as one unit
-    # ---- the timed steps: per input copy either three prepared library calls
-    # (arguments marshalled once, one ctypes call each) or one captured HIP graph
-    runners = []
-    if args.launch == "graph":
-        cap = torch.cuda.Stream()
-        for c in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                step(sets[c], torch.cuda.current_stream())
-            runners.append(g.replay)
-            sets[c]["graph"] = g
-    else:
-        for c in range(copies):
-            s_ = sets[c]
-            pw, _ = F.prepare_write_k_pack_q(s_["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, s_["payload"],
-                                             s_["scale"], s_["q"], pos_q, s_["w"], wl.w_scale, s_["q_fp4"],
-                                             s_["q_scale"], s_["w_out"], stream=stream)
-            pl, _ = F.prepare_mqa_logits(s_["q_fp4"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, s_["payload"],
-                                         s_["scale"], wl.max_rows_per_req, wl.max_ctx, logits=s_["logits"],
-                                         stream=stream)
-            pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
-
-            def run(pw=pw, pl=pl, pt=pt):
-                pw()
-                pl()
-                pt()
-            runners.append(run)
-    for c in range(copies):
-        runners[c]()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K steps, bracketed by synchronize
-    torch.cuda.synchronize()
-    start = time.perf_counter()
-    for i in range(args.steps):
-        runners[i % copies]()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - start
-
-    # ---- kernel durations: the same K steps launched eagerly on the launch stream, each kernel carrying
-    # HIP events that its own dispatch stamps with its start and end times (no marker packets in between)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
-           for _ in range(args.steps)]
-    for row in evs:          # create the HIP events (torch creates them on first record)
-        for a, b in row:
-            a.record(stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(sets[i % copies], stream, evs[i])
-    torch.cuda.synchronize()
-    per_kernel_ms = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
-                     for j, n in enumerate(names)}
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step, per_kernel_ms, copies = run_cache(False, dict(payload=payload, scale=scale))
     scores = wl.scores
-    value = scores * args.steps / elapsed
+    value = scores / (ms_per_step * 1e-3)
 
     # ---- roofline of the dominant kernel (algorithmic bytes per launch)
     uniq_tokens = int(np.sum([int(np.max(wl.row_ctx[wl.req_row_indptr[b]:wl.req_row_indptr[b + 1]], initial=0))
@@ -283,6 +304,30 @@ def main():
                             "GB/s": round(r_bytes / (r_ms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del rout
+
+    # ---- the FP8 indexer cache on the same workload (132-byte fused tokens): same step, same timing
+    if not args.no_fp8:
+        pool8 = torch.zeros(wl.num_pages * W.FP8_PAGE_BYTES, dtype=torch.uint8, device=dev)
+        if wl.cached_slots.size:
+            kc = wl.cached_k()
+            for a in range(0, kc.shape[0], 1 << 20):
+                F.write_k_fp8(b16(kc[a:a + (1 << 20)]), t(wl.cached_pos[a:a + (1 << 20)]),
+                              t(wl.cached_slots[a:a + (1 << 20)]), norm_w, wl.eps, tab, pool8)
+            del kc
+        torch.cuda.synchronize()
+        ms8, pk8, copies8 = run_cache(True, dict(pool=pool8))
+        del pool8
+        l8 = 132 * uniq_tokens + 4 * scores + 8704 * T + 4 * ((uniq_tokens + 63) // 64)
+        a8 = l8 / (pk8["mqa_logits"] * 1e-3) / 1e9
+        extras["fp8_cache"] = {
+            "ms_per_step": round(ms8, 4), "scores_per_s": round(scores / (ms8 * 1e-3), 1),
+            "kernels_us": {n: round(v * 1e3, 2) for n, v in pk8.items()},
+            "logits_roofline": {"bound": "hbm", "achieved": round(a8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(a8 / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": l8},
+            "bytes_per_cached_token": 132, "input_copies": copies8,
+            "fp4_vs_fp8_step_speedup": round(ms8 / ms_per_step, 3)}
+        log(f"[bench] fp8 cache: {ms8 * 1e3:.1f} us/step, logits {pk8['mqa_logits'] * 1e3:.1f} us "
+            f"({time.time() - t0:.1f}s)")
 
     # ---- CPU baseline: the oracle on the same workload (bounded sample)
     cpu = None

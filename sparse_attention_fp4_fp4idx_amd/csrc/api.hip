@@ -97,6 +97,20 @@ int check_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_
   return FP4IDX_OK;
 }
 
+// Host checks of the logits calls' scalars shared by both caches.
+int check_logits(int64_t n_rows, int32_t n_heads, int32_t n_reqs, int32_t bt_stride, int64_t num_pages,
+                 int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx) {
+  if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || logits_stride < 0 || max_rows_per_req < 0 ||
+      max_ctx < 0)
+    return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
+  if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
+  if (num_pages == 0) return FP4IDX_E_INVALID;
+  return FP4IDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,7 +125,7 @@ int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_strid
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16,
-                                         payload, scale, static_cast<hipStream_t>(stream)));
+                                         max_pos, payload, scale, num_pages, static_cast<hipStream_t>(stream)));
 }
 
 int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
@@ -123,8 +137,8 @@ int fp4idx_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64
   if (rc != FP4IDX_OK || n_rows == 0) return rc;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
-  return launched(fp4idx::launch_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, w_in, w_scale,
-                                        q_fp4, q_scale, w_out, static_cast<hipStream_t>(stream)));
+  return launched(fp4idx::launch_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, max_pos, w_in,
+                                        w_scale, q_fp4, q_scale, w_out, static_cast<hipStream_t>(stream)));
 }
 
 int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
@@ -144,8 +158,8 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_write_k_pack_q(k_bf16, n_tokens, k_row_stride, pos_k, slot, norm_w_bf16, eps,
-                                                cos_sin_bf16, payload, scale, q_bf16, n_rows, n_heads, q_row_stride,
-                                                pos_q, w_in, w_scale, q_fp4, q_scale, w_out,
+                                                cos_sin_bf16, max_pos, payload, scale, num_pages, q_bf16, n_rows,
+                                                n_heads, q_row_stride, pos_q, w_in, w_scale, q_fp4, q_scale, w_out,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -155,14 +169,8 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
                       int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
                       int64_t max_ctx, void* stream) {
   const TimingScope timing_scope;
-  if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || logits_stride < 0 || max_rows_per_req < 0 ||
-      max_ctx < 0)
-    return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
-  if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
-  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
-  if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
-  if (num_pages == 0) return FP4IDX_E_INVALID;
+  int rc = check_logits(n_rows, n_heads, n_reqs, bt_stride, num_pages, logits_stride, max_rows_per_req, max_ctx);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return rc;
   if (!q_fp4 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !payload || !scale || !logits)
     return FP4IDX_E_INVALID;
   if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
@@ -201,6 +209,75 @@ int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, cons
   if (dev != FP4IDX_OK) return dev;
   return launched(fp4idx::launch_topk(logits, n_rows, logits_stride, row_ctx_len, k, out_idx, max_ctx,
                                       static_cast<hipStream_t>(stream)));
+}
+
+/* ---- FP8 cache ---------------------------------------------------------- */
+
+int fp4idx_write_k_fp8(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                       const int32_t* slot, const uint16_t* norm_w_bf16, float eps, const uint16_t* cos_sin_bf16,
+                       int32_t max_pos, uint8_t* pool, int64_t num_pages, void* stream) {
+  const TimingScope timing_scope;
+  const int rc = check_write_k(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps, cos_sin_bf16, max_pos,
+                               pool, pool, num_pages);
+  if (rc != FP4IDX_OK || n_tokens == 0) return rc;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_write_k_fp8(k_bf16, n_tokens, k_row_stride, pos, slot, norm_w_bf16, eps,
+                                             cos_sin_bf16, max_pos, pool, num_pages,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_pack_q_fp8(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                      const int32_t* pos, const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in,
+                      float w_scale, uint8_t* q_fp8, float* q_scale, float* w_out, void* stream) {
+  const TimingScope timing_scope;
+  const int rc = check_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, max_pos, w_in, q_fp8,
+                              reinterpret_cast<const uint8_t*>(q_scale), w_out);
+  if (rc != FP4IDX_OK || n_rows == 0) return rc;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_pack_q_fp8(q_bf16, n_rows, n_heads, q_row_stride, pos, cos_sin_bf16, max_pos, w_in,
+                                            w_scale, q_fp8, q_scale, w_out, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_write_k_pack_q_fp8(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
+                              const int32_t* slot, const uint16_t* norm_w_bf16, float eps,
+                              const uint16_t* cos_sin_bf16, int32_t max_pos, uint8_t* pool, int64_t num_pages,
+                              const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_t q_row_stride,
+                              const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp8,
+                              float* q_scale, float* w_out, void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_write_k(k_bf16, n_tokens, k_row_stride, pos_k, slot, norm_w_bf16, eps, cos_sin_bf16, max_pos, pool,
+                         pool, num_pages);
+  if (rc != FP4IDX_OK) return rc;
+  rc = check_pack_q(q_bf16, n_rows, n_heads, q_row_stride, pos_q, cos_sin_bf16, max_pos, w_in, q_fp8,
+                    reinterpret_cast<const uint8_t*>(q_scale), w_out);
+  if (rc != FP4IDX_OK) return rc;
+  if (n_tokens == 0 && n_rows == 0) return FP4IDX_OK;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_write_k_pack_q_fp8(k_bf16, n_tokens, k_row_stride, pos_k, slot, norm_w_bf16, eps,
+                                                    cos_sin_bf16, max_pos, pool, num_pages, q_bf16, n_rows, n_heads,
+                                                    q_row_stride, pos_q, w_in, w_scale, q_fp8, q_scale, w_out,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int64_t n_rows,
+                          int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                          const int32_t* block_table, int32_t bt_stride, const uint8_t* pool, int64_t num_pages,
+                          float* logits, int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx,
+                          void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_logits(n_rows, n_heads, n_reqs, bt_stride, num_pages, logits_stride, max_rows_per_req, max_ctx);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return rc;
+  if (!q_fp8 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !pool || !logits)
+    return FP4IDX_E_INVALID;
+  if (!aligned(q_fp8, 16) || !aligned(q_scale, 4) || !aligned(w, 16) || !aligned(pool, 16)) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_mqa_logits_fp8(q_fp8, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+                                                block_table, bt_stride, pool, num_pages, logits, logits_stride,
+                                                max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

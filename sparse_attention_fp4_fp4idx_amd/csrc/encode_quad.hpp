@@ -1,4 +1,4 @@
-// Device helpers of the two FP4 encoders (K writer, Q pack) on gfx950.
+// Device helpers of the K writer and Q pack on gfx950 (FP4 and FP8 caches).
 //
 // A quad of lanes q = 0..3 owns one 128-vector; lane q holds the 32 elements
 //   i = 32*c + 8*q + e,   c = 0..3 (register chunk), e = 0..7.
@@ -33,6 +33,8 @@ constexpr int kRope = 64;
 constexpr int kPageTokens = 64;
 constexpr int kPayloadPage = 4096;  // [1, 4, 64, 16]
 constexpr int kScalePage = 256;     // [1, 4, 64]
+constexpr int kFp8Page = 8448;      // [64][128] e4m3 codes, then [64] fp32 scales
+constexpr int kFp8ScaleOffset = 8192;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -185,6 +187,43 @@ __device__ __forceinline__ void quad_quant(const QuadVec& v, uint32_t (&word)[4]
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.x[c][4], v.x[c][5], sc, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.x[c][6], v.x[c][7], sc, 3);
     word[c] = w;
+  }
+}
+
+// FP8 encode of the whole vector with one power-of-two scale 2^e, e the
+// smallest integer with 448 * 2^e >= amax, clamped to [-127, 127] (448 is the
+// largest finite OCP E4M3 value): amax = m 2^E with m in [1, 2) gives
+// e = E - 8, plus one when m > 1.75; a zero or subnormal amax gives -127.
+// Each code is the e4m3 value nearest to z / 2^e, ties to even, sign kept
+// (the hardware convert divides by the scale exactly and rounds to nearest
+// even).  The scale handed to the convert is kept a normal number: for
+// e < -64 the inputs are first multiplied by 2^64 (exact) and the scale by
+// the same.  codes[c] = the lane's 8 codes of chunk c, i.e. bytes
+// 32c + 8q .. +7 of the vector; scale = 2^e as stored (2^-127 subnormal).
+__device__ __forceinline__ void quad_quant_fp8(const QuadVec& v, uint2 (&codes)[4], float& scale) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v.x[c][e]));
+  amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+  const uint32_t bits = __float_as_uint(amax);
+  int e = (int)(bits >> 23) - 135 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  scale = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+  const bool tiny = e < -64;
+  const float pre = tiny ? __uint_as_float(0x5F800000u) : 1.0f;  // 2^64
+  const float sc = __uint_as_float((uint32_t)((tiny ? e + 64 : e) + 127) << 23);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v2s lo = {0, 0}, hi = {0, 0};
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v.x[c][0] * pre, v.x[c][1] * pre, sc, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v.x[c][2] * pre, v.x[c][3] * pre, sc, true);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, v.x[c][4] * pre, v.x[c][5] * pre, sc, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, v.x[c][6] * pre, v.x[c][7] * pre, sc, true);
+    codes[c] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
   }
 }
 

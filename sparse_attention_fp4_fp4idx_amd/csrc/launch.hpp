@@ -33,23 +33,45 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32
 
 hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
                           const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
-                          uint8_t* payload, uint8_t* scale, hipStream_t stream);
+                          int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages, hipStream_t stream);
 
 hipError_t launch_pack_q(const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride, const int32_t* pos,
-                         const uint16_t* cos_sin, const float* w_in, float w_scale, uint8_t* q_fp4,
+                         const uint16_t* cos_sin, int32_t max_pos, const float* w_in, float w_scale, uint8_t* q_fp4,
                          uint8_t* q_scale, float* w_out, hipStream_t stream);
 
 hipError_t launch_write_k_pack_q(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos_k,
                                  const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
-                                 uint8_t* payload, uint8_t* scale, const uint16_t* q, int64_t n_rows, int n_heads,
-                                 int64_t q_row_stride, const int32_t* pos_q, const float* w_in, float w_scale,
-                                 uint8_t* q_fp4, uint8_t* q_scale, float* w_out, hipStream_t stream);
+                                 int32_t max_pos, uint8_t* payload, uint8_t* scale, int64_t num_pages,
+                                 const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride,
+                                 const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp4,
+                                 uint8_t* q_scale, float* w_out, hipStream_t stream);
+
+hipError_t launch_write_k_fp8(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,
+                              const int32_t* slot, const uint16_t* norm_w, float eps, const uint16_t* cos_sin,
+                              int32_t max_pos, uint8_t* pool, int64_t num_pages, hipStream_t stream);
+
+hipError_t launch_pack_q_fp8(const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride,
+                             const int32_t* pos, const uint16_t* cos_sin, int32_t max_pos, const float* w_in,
+                             float w_scale, uint8_t* q_fp8, float* q_scale, float* w_out, hipStream_t stream);
+
+hipError_t launch_write_k_pack_q_fp8(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride,
+                                     const int32_t* pos_k, const int32_t* slot, const uint16_t* norm_w, float eps,
+                                     const uint16_t* cos_sin, int32_t max_pos, uint8_t* pool, int64_t num_pages,
+                                     const uint16_t* q, int64_t n_rows, int n_heads, int64_t q_row_stride,
+                                     const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp8,
+                                     float* q_scale, float* w_out, hipStream_t stream);
 
 hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
                              const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);
+
+hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int n_heads,
+                                 const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                 const int32_t* block_table, int32_t bt_stride, const uint8_t* pool,
+                                 int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
+                                 int64_t max_ctx, hipStream_t stream);
 
 hipError_t launch_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,
                          int64_t n_tokens, float* out, int64_t out_stride, hipStream_t stream);

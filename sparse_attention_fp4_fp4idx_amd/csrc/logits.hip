@@ -1,8 +1,14 @@
-// Paged-MQA FP4 logits on gfx950 block-scaled MFMA.
+// Paged-MQA indexer logits on gfx950 block-scaled MFMA, for the FP4 cache
+// (split payload/scale pools) and the FP8 cache (one fused pool).
 //
 // Score (DeepSeek lightning indexer, as the FP4 indexer of "[AMD] Enable FP4
-// indexer for Deepseek V4" computes it over the split payload/scale cache):
+// indexer for Deepseek V4" computes it over the split payload/scale cache,
+// and the FP8 indexer it replaces over its fused 132-byte tokens):
 //   logits[t][s] = sum_h w[t][h] * ReLU( qhat[t][h] . khat[s] )
+//
+// One kernel template serves both caches; a format type (Fp4Split, Fp8Fused
+// below) supplies the page loads, the Q operand and the MFMA form, and
+// everything else (work split, prefetch, epilogue) is shared.
 //
 // Work decomposition
 //   work-group (256 threads = 4 waves) = (request, group of up to RW rows,
@@ -11,11 +17,13 @@
 //   Every wave keeps its rows' packed Q (the MFMA A operand) and head weights
 //   in registers and streams K pages: per 16-token tile each lane loads 16
 //   payload bytes (one 128-bit load; the 64 lanes read 4 runs of 256 B) and
-//   one scale byte, straight into the B operand.  D pages are in flight per
-//   wave; the page ids and Q are requested before the context lengths arrive
-//   so the prologue costs one memory latency less.
+//   one scale byte (FP8: 32 code bytes in two 128-bit loads, the 16 tokens'
+//   2 KB contiguous, and a scale word), straight into the B operand.  D
+//   pages are in flight per wave; the page ids and Q are requested before
+//   the context lengths arrive so the prologue costs one memory latency less.
 //
-// MFMA mapping (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands FP4 e2m1):
+// MFMA mapping for FP4 (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands
+// e2m1; FP8 in Fp8Fused below):
 //   A (16 x 128) = 16 heads of one query row; lane l holds head l%16, K
 //   elements 32*(l/16)..+31 and that block's UE8M0 scale (byte mt of a packed
 //   scale register, picked by op_sel).  B (128 x 16) = 16 tokens; lane l holds
@@ -44,20 +52,6 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 }
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int OPA>
-__device__ __forceinline__ v4f mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb) {
-  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  const v4f z = {0.f, 0.f, 0.f, 0.f};
-  // cbsz = blgp = 4: both operands FP4 (e2m1); op_sel picks the scale byte.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 0, (int)sb);
-}
-
-template <int MT>
-__device__ __forceinline__ v4f mfma_tile(uint4 a, uint4 b, uint32_t sa, uint32_t sb) {
-  return mfma_fp4<MT & 3>(a, b, sa, sb);
-}
-
 // ReLU on the bit pattern: every negative float (and -0) is a negative int32,
 // so max(bits, 0) gives +0 for them and leaves non-negative values unchanged.
 // One integer max instead of the quieting and comparing pair fmaxf needs.
@@ -75,34 +69,106 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// One page of B operands: 4 tiles of 16 tokens, 16 payload bytes and one
-// scale byte per lane each.
-struct PageRegs {
-  uint4 b[4];
-  uint32_t s[4];
+// FP4 split pools: payload [page][block][token][16 B], scale [page][block][token].
+// B lane l = (token l%16, block l/16): exactly the 16-byte payload chunk at
+// [page][block][token] and its UE8M0 byte; A lane l = (head l%16, block l/16).
+struct Fp4Split {
+  static constexpr int kDecodeWaves = 4;
+  static constexpr int kMaxRowsWide = 4;  // rows per wave at 128 heads
+  struct Page {  // 4 tiles of 16 tokens
+    uint4 b[4];
+    uint32_t s[4];
+  };
+  typedef uint4 QOp;
+  static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(lg * 1024 + li * 16); }
+  static __device__ __forceinline__ uint32_t lane_sc(int li, int lg) { return (uint32_t)(lg * 64 + li); }
+  static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ payload,
+                                                   const uint8_t* __restrict__ scale, int64_t pid, uint32_t lp,
+                                                   uint32_t ls) {
+    const uint8_t* pp = payload + pid * 4096 + lp;
+    const uint8_t* sp = scale + pid * 256 + ls;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pr.b[t] = ld_stream16(pp + t * 256);
+      pr.s[t] = sp[t * 16];
+    }
+  }
+  static __device__ __forceinline__ QOp load_q(const uint8_t* __restrict__ q, int64_t hrow, int lg) {
+    return *reinterpret_cast<const uint4*>(q + hrow * 64 + lg * 16);
+  }
+  static __device__ __forceinline__ uint32_t q_scale_byte(const uint8_t* __restrict__ qs, int64_t hrow, int lg) {
+    return qs[hrow * 4 + lg];
+  }
+  template <int OPA>
+  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
+    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const v8i bv = {(int)p.b[t].x, (int)p.b[t].y, (int)p.b[t].z, (int)p.b[t].w, 0, 0, 0, 0};
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    // cbsz = blgp = 4: both operands FP4 (e2m1); op_sel picks the scale byte.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 0, (int)p.s[t]);
+  }
 };
 
-__device__ __forceinline__ void load_page(PageRegs& pr, const uint8_t* __restrict__ payload,
-                                          const uint8_t* __restrict__ scale, int64_t pid, uint32_t lane_pay,
-                                          uint32_t lane_sc) {
-  const uint8_t* pp = payload + pid * 4096 + lane_pay;
-  const uint8_t* sp = scale + pid * 256 + lane_sc;
+// FP8 fused pool: page = [64 tokens][128 e4m3 codes] then [64] fp32 scales
+// (powers of two), 8448 bytes.  The fp8 operand holds 32 bytes per lane;
+// A lane l = (head l%16, bytes 32(l/16)..+31 of the head's codes), B lane
+// l = (token l%16, the same bytes of the token): A and B place code i in the
+// same K slot, so the dot product is the plain one whatever order the MFMA
+// gives the 128 slots.  One scale per token and per (row, head) makes all
+// four block scales of an operand row equal: the MFMA scale is the fp32
+// scale's exponent field (an E8M0 byte).
+struct Fp8Fused {
+  static constexpr int kDecodeWaves = 2;
+  static constexpr int kMaxRowsWide = 2;  // 8-register operands: 3+ rows at 128 heads spill
+  struct Page {
+    uint4 lo[4], hi[4];
+    uint32_t s[4];
+  };
+  struct QOp {
+    uint4 lo, hi;
+  };
+  static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(li * 128 + lg * 32); }
+  static __device__ __forceinline__ uint32_t lane_sc(int li, int) { return (uint32_t)(8192 + li * 4); }
+  static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ pool, const uint8_t*,
+                                                   int64_t pid, uint32_t lp, uint32_t ls) {
+    const uint8_t* pp = pool + pid * 8448;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    pr.b[t] = ld_stream16(pp + t * 256);
-    pr.s[t] = sp[t * 16];
+    for (int t = 0; t < 4; ++t) {
+      pr.lo[t] = ld_stream16(pp + lp + t * 2048);
+      pr.hi[t] = ld_stream16(pp + lp + t * 2048 + 16);
+      pr.s[t] = (*reinterpret_cast<const uint32_t*>(pp + ls + t * 64) >> 23) & 0xFFu;
+    }
   }
-}
+  static __device__ __forceinline__ QOp load_q(const uint8_t* __restrict__ q, int64_t hrow, int lg) {
+    const uint4* p = reinterpret_cast<const uint4*>(q + hrow * 128 + lg * 32);
+    return QOp{p[0], p[1]};
+  }
+  static __device__ __forceinline__ uint32_t q_scale_byte(const uint8_t* __restrict__ qs, int64_t hrow, int) {
+    return (reinterpret_cast<const uint32_t*>(qs)[hrow] >> 23) & 0xFFu;
+  }
+  template <int OPA>
+  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
+    const v8i av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
+                    (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+    const v8i bv = {(int)p.lo[t].x, (int)p.lo[t].y, (int)p.lo[t].z, (int)p.lo[t].w,
+                    (int)p.hi[t].x, (int)p.hi[t].y, (int)p.hi[t].z, (int)p.hi[t].w};
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    // cbsz = blgp = 0: both operands FP8 e4m3.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 0, 0, OPA, (int)sa, 0, (int)p.s[t]);
+  }
+};
 
 // RW rows per wave, NMT = heads/16, PPW pages per wave, D pages in flight.
-// Few rows per wave (decode) means little work per wave: keep at least four
-// waves per SIMD resident so memory latency overlaps; more rows keep their
-// register budget.
-template <int RW, int NMT>
-constexpr int kMinWavesPerSimd = (RW == 1 && NMT <= 4) ? 4 : 1;
+// Few rows per wave (decode) means little work per wave: keep several waves
+// per SIMD resident so memory latency overlaps (four for FP4; two for FP8,
+// whose 36-register pages need the larger register budget for four pages in
+// flight, the same bytes in flight per SIMD); more rows keep their register
+// budget.
+template <typename FMT, int RW, int NMT>
+constexpr int kMinWavesPerSimd = (RW == 1 && NMT <= 4) ? FMT::kDecodeWaves : 1;
 
-template <int RW, int NMT, int PPW, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<RW, NMT>))) void mqa_logits_kernel(
+template <typename FMT, int RW, int NMT, int PPW, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void mqa_logits_kernel(
     // the first arguments are preloaded into SGPRs: those the prologue needs
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
@@ -132,8 +198,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   if (page_begin >= bt_stride) return;
   const int li = lane & 15;  // token within tile (B, D) / head within M-tile (A)
   const int lg = lane >> 4;  // K block (A, B) / head quad (D)
-  const uint32_t lane_pay = (uint32_t)(lg * 1024 + li * 16);
-  const uint32_t lane_sc = (uint32_t)(lg * 64 + li);
+  const uint32_t lane_pay = FMT::lane_pay(li, lg);
+  const uint32_t lane_sc = FMT::lane_sc(li, lg);
 
   // Memory round trip 1: the wave's page ids (one vector load, lane i reads
   // entry i, clamped into the table) and the request's row range.  No branch
@@ -170,14 +236,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // Branch-free from here, so all loads issue back to back: another id
   // outside the pool (past the request's pages) re-reads the first page and
   // its tile is never stored.
-  PageRegs nxt[D];
+  typename FMT::Page nxt[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
-    load_page(nxt[i], payload, scale, pg, lane_pay, lane_sc);
+    FMT::load_page(nxt[i], payload, scale, pg, lane_pay, lane_sc);
   }
 
-  uint4 aq[RW][NMT];
+  typename FMT::QOp aq[RW][NMT];
   uint32_t asc[RW][NSC];
   float wv[RW][NMT][4];
 #pragma unroll
@@ -188,8 +254,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int64_t hrow = (int64_t)row * H + mt * 16 + li;
-      aq[r][mt] = *reinterpret_cast<const uint4*>(q_fp4 + hrow * 64 + lg * 16);
-      asc[r][mt >> 2] |= (uint32_t)q_scale[hrow * 4 + lg] << (8 * (mt & 3));
+      aq[r][mt] = FMT::load_q(q_fp4, hrow, lg);
+      asc[r][mt >> 2] |= FMT::q_scale_byte(q_scale, hrow, lg) << (8 * (mt & 3));
       const float4 w4 = *reinterpret_cast<const float4*>(w + (int64_t)row * H + mt * 16 + lg * 4);
       const bool live = r < nrows;
       wv[r][mt][0] = live ? w4.x : 0.f;
@@ -199,11 +265,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
     }
   }
 
+  // a context length beyond the row or the table (a broken contract) is cut
+  // to what both hold, so no store leaves the row
+  const int ctx_cap = (int)min(min((int64_t)bt_stride * 64, logits_stride), (int64_t)0x7FFFFFFF);
   int ctx_r[4] = {0, 0, 0, 0};
   int gmax = 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    ctx_r[r] = r < nrows ? __builtin_amdgcn_readlane(my_ctx, r) : 0;
+    ctx_r[r] = r < nrows ? min(__builtin_amdgcn_readlane(my_ctx, r), ctx_cap) : 0;
     gmax = max(gmax, ctx_r[r]);
   }
   const int pages_needed = (gmax + 63) >> 6;
@@ -213,14 +282,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
   for (int g0 = 0; g0 < PPW; g0 += D) {
     if (g0 >= n_pages) break;
-    PageRegs cur[D];
+    typename FMT::Page cur[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) cur[i] = nxt[i];
     if (g0 + D < PPW) {
 #pragma unroll
       for (int i = 0; i < D; ++i)
         if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
-          load_page(nxt[i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
+          FMT::load_page(nxt[i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
     }
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -237,10 +306,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
               switch (mt & 3) {
-                case 0: d[mt] = mfma_tile<0>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
-                case 1: d[mt] = mfma_tile<1>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
-                case 2: d[mt] = mfma_tile<2>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
-                default: d[mt] = mfma_tile<3>(aq[r][mt], cur[i].b[t], asc[r][mt >> 2], cur[i].s[t]); break;
+                case 0: d[mt] = FMT::template mfma<0>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
+                case 1: d[mt] = FMT::template mfma<1>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
+                case 2: d[mt] = FMT::template mfma<2>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
+                default: d[mt] = FMT::template mfma<3>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
               }
             }
             // two fixed-order chains (even / odd M-tiles), then their sum
@@ -270,8 +339,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   }
 }
 
-template <int RW, int NMT, int PPW, int D>
-static hipError_t launch_rw(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+template <typename FMT, int RW, int NMT, int PPW, int D>
+static hipError_t launch_rw(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                             int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
                             const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
                             int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
@@ -280,27 +349,56 @@ static hipError_t launch_rw(const uint8_t* q_fp4, const uint8_t* q_scale, const 
   const int64_t n_groups = (max_rows_per_req + RW - 1) / RW;
   if (n_chunks == 0 || n_groups == 0 || n_reqs == 0) return hipSuccess;
   if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
-  return launch(mqa_logits_kernel<RW, NMT, PPW, D>, dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs),
-                dim3(256), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q_fp4, q_scale,
-                w, logits, logits_stride);
+  return launch(mqa_logits_kernel<FMT, RW, NMT, PPW, D>,
+                dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs), dim3(256), 0, stream, block_table,
+                indptr, row_ctx, payload, scale, num_pages, bt_stride, q, q_scale, w, logits, logits_stride);
 }
 
-template <int NMT>
-static hipError_t launch_nmt(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+template <typename FMT, int NMT>
+static hipError_t launch_nmt(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                              int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
                              int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
   if (max_rows_per_req <= 1)
-    return launch_rw<1, NMT, 4, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 1, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
   if (max_rows_per_req == 2)
-    return launch_rw<2, NMT, 4, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-  if (max_rows_per_req == 3 || max_rows_per_req == 6)
-    return launch_rw<3, NMT, 8, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-  return launch_rw<4, NMT, 8, 2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                           num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 2, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  if constexpr (NMT == 8 && FMT::kMaxRowsWide == 2) {
+    return launch_rw<FMT, 2, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  } else {
+    if (max_rows_per_req == 3 || max_rows_per_req == 6)
+      return launch_rw<FMT, 3, NMT, 8, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                          scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 4, NMT, 8, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  }
+}
+
+template <typename FMT>
+static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const float* w, int n_heads,
+                               const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                               const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                               const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                               int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  switch (n_heads) {
+    case 16:
+      return launch_nmt<FMT, 1>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 32:
+      return launch_nmt<FMT, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 64:
+      return launch_nmt<FMT, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    case 128:
+      return launch_nmt<FMT, 8>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
+                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
@@ -308,22 +406,18 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
-  switch (n_heads) {
-    case 16:
-      return launch_nmt<1>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
-                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 32:
-      return launch_nmt<2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
-                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 64:
-      return launch_nmt<4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
-                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 128:
-      return launch_nmt<8>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale, num_pages,
-                           logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    default:
-      return hipErrorInvalidValue;
-  }
+  return launch_heads<Fp4Split>(q_fp4, q_scale, w, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
+                                scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+}
+
+hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int n_heads,
+                                 const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                 const int32_t* block_table, int32_t bt_stride, const uint8_t* pool,
+                                 int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
+                                 int64_t max_ctx, hipStream_t stream) {
+  return launch_heads<Fp8Fused>(q_fp8, reinterpret_cast<const uint8_t*>(q_scale), w, n_heads, indptr, n_reqs,
+                                row_ctx, block_table, bt_stride, pool, pool, num_pages, logits, logits_stride,
+                                max_rows_per_req, max_ctx, stream);
 }
 
 }  // namespace fp4idx

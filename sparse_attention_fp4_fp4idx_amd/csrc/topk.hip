@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(const float* __
   uint32_t* keys = smem + kBins;    // [ctx] when KEYS_IN_LDS
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ctx = row_ctx[row];
+  const int ctx = (int)min<int64_t>(max(row_ctx[row], 0), stride);  // in-row reads whatever the value
   const float* src = logits + row * stride;
   int32_t* o = out_idx + row * (int64_t)k;
   const int K = min(k, ctx);

@@ -24,10 +24,13 @@ ROPE_DIM = 64
 PAGE_TOKENS = 64
 PAYLOAD_PAGE_BYTES = 4096
 SCALE_PAGE_BYTES = 256
+FP8_PAGE_BYTES = 8448
 MAX_TOPK = 2048
 
-EXPORTS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
-           "fp4idx_read_k", "fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
+_CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
+          "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
+          "fp4idx_mqa_logits_fp8")
+EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
 class Fp4idxError(RuntimeError):
@@ -55,8 +58,12 @@ def load():
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
-    for name in ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
-                 "fp4idx_read_k"):
+    lib.fp4idx_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64, P]
+    lib.fp4idx_pack_q_fp8.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
+    lib.fp4idx_write_k_pack_q_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64,
+                                              P, i64, i32, i64, P, P, f32, P, P, P, P]
+    lib.fp4idx_mqa_logits_fp8.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, i64, P, i64, i32, i64, P]
+    for name in _CALLS:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp4idx_time_next_call.argtypes = [P, P]
     lib.fp4idx_time_next_call.restype = ctypes.c_int
@@ -149,6 +156,23 @@ def _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale):
             _ptr(scale, _U8, "scale"), num_pages]
 
 
+def _write_k_fp8_args(k, pos, slot, norm_w, eps, cos_sin, pool):
+    if not (pos.is_contiguous() and slot.is_contiguous() and pool.is_contiguous() and cos_sin.is_contiguous()
+            and norm_w.is_contiguous()):
+        raise Fp4idxError("write_k_fp8: pos, slot, norm_w, cos_sin and the pool must be contiguous")
+    n = int(k.shape[0])
+    if pos.numel() != n or slot.numel() != n:
+        raise Fp4idxError("write_k_fp8: pos/slot length must equal the number of K rows")
+    num_pages = pool.numel() // FP8_PAGE_BYTES
+    if pool.numel() != num_pages * FP8_PAGE_BYTES:
+        raise Fp4idxError("write_k_fp8: the pool must be num_pages*8448 bytes")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != ROPE_DIM:
+        raise Fp4idxError("write_k_fp8: cos_sin must be [max_pos, 64]")
+    return [_ptr(k, _BF16, "k"), n, _rowstride(k, "k") if n else HEAD_DIM, _ptr(pos, _I32, "pos"),
+            _ptr(slot, _I32, "slot"), _ptr(norm_w, _BF16, "norm_w"), ctypes.c_float(eps),
+            _ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0]), _ptr(pool, _U8, "pool"), num_pages]
+
+
 def fp4idx_write_k(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor, eps: float,
                    cos_sin: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
     """Encode K rows [N, >=128] bf16 and scatter them into the split pool."""
@@ -161,23 +185,28 @@ def prepare_write_k(k, pos, slot, norm_w, eps, cos_sin, payload, scale, stream=N
                     + [_stream(stream)], keep=(k, pos, slot, norm_w, cos_sin, payload, scale))
 
 
-def _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp4, q_scale, w_out, with_table=True):
+def _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_out, q_scale, w_out, with_table=True, fp8=False):
+    what = "pack_q_fp8" if fp8 else "pack_q"
     T, H = int(q.shape[0]), int(q.shape[1])
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or (T and (q.stride(2) != 1 or q.stride(1) != HEAD_DIM)):
-        raise Fp4idxError("pack_q: q must be [T, H, 128] with heads packed inside a row")
+        raise Fp4idxError(f"{what}: q must be [T, H, 128] with heads packed inside a row")
     dev = q.device
-    q_fp4 = q_fp4 if q_fp4 is not None else torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
-    q_scale = q_scale if q_scale is not None else torch.empty((T, H, 4), dtype=torch.uint8, device=dev)
+    if fp8:
+        q_out = q_out if q_out is not None else torch.empty((T, H, HEAD_DIM), dtype=torch.uint8, device=dev)
+        q_scale = q_scale if q_scale is not None else torch.empty((T, H), dtype=torch.float32, device=dev)
+    else:
+        q_out = q_out if q_out is not None else torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
+        q_scale = q_scale if q_scale is not None else torch.empty((T, H, 4), dtype=torch.uint8, device=dev)
     w_out = w_out if w_out is not None else torch.empty((T, H), dtype=torch.float32, device=dev)
-    for t, name in ((pos, "pos"), (w_in, "w_in"), (q_fp4, "q_fp4"), (q_scale, "q_scale"), (w_out, "w_out"),
+    for t, name in ((pos, "pos"), (w_in, "w_in"), (q_out, "q codes"), (q_scale, "q_scale"), (w_out, "w_out"),
                     (cos_sin, "cos_sin")):
         if not t.is_contiguous():
-            raise Fp4idxError(f"pack_q: {name} must be contiguous")
+            raise Fp4idxError(f"{what}: {name} must be contiguous")
     head = [_ptr(q, _BF16, "q"), T, H, int(q.stride(0)) if T else H * HEAD_DIM, _ptr(pos, _I32, "pos")]
     table = [_ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0])] if with_table else []
-    tail = [_ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_fp4, _U8, "q_fp4"),
-            _ptr(q_scale, _U8, "q_scale"), _ptr(w_out, _F32, "w_out")]
-    return head + table + tail, (q_fp4, q_scale, w_out)
+    tail = [_ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_out, _U8, "q codes"),
+            _ptr(q_scale, _F32 if fp8 else _U8, "q_scale"), _ptr(w_out, _F32, "w_out")]
+    return head + table + tail, (q_out, q_scale, w_out)
 
 
 def fp4idx_pack_q(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_in: torch.Tensor,
@@ -321,10 +350,107 @@ def _event_handle(ev):
 def fp4idx_time_next_call(start_event, stop_event) -> None:
     """Arm two timing events (torch.cuda.Event with enable_timing=True, already
     recorded once so that the HIP event exists, or raw hipEvent_t handles) for
-    this thread's next write_k / pack_q / mqa_logits / topk call: they receive
+    this thread's next library call (each launches one kernel): they receive
     that call's kernel start and end timestamps."""
     _check(load().fp4idx_time_next_call(_event_handle(start_event), _event_handle(stop_event)),
            "fp4idx_time_next_call")
+
+
+# ---- FP8 cache (132-byte fused tokens) ----------------------------------------
+
+def fp4idx_write_k_fp8(k: torch.Tensor, pos: torch.Tensor, slot: torch.Tensor, norm_w: torch.Tensor, eps: float,
+                       cos_sin: torch.Tensor, pool: torch.Tensor, stream=None) -> None:
+    """Encode K rows [N, >=128] bf16 into the fused FP8 pool [num_pages * 8448] u8."""
+    _run("fp4idx_write_k_fp8", _write_k_fp8_args(k, pos, slot, norm_w, eps, cos_sin, pool) + [_stream(stream)])
+
+
+def prepare_write_k_fp8(k, pos, slot, norm_w, eps, cos_sin, pool, stream=None) -> "Prepared":
+    """fp4idx_write_k_fp8 with its arguments marshalled once (see Prepared)."""
+    return Prepared("fp4idx_write_k_fp8", _write_k_fp8_args(k, pos, slot, norm_w, eps, cos_sin, pool)
+                    + [_stream(stream)], keep=(k, pos, slot, norm_w, cos_sin, pool))
+
+
+def fp4idx_pack_q_fp8(q: torch.Tensor, pos: torch.Tensor, cos_sin: torch.Tensor, w_in: torch.Tensor,
+                      w_scale: float = 1.0, q_fp8: torch.Tensor = None, q_scale: torch.Tensor = None,
+                      w_out: torch.Tensor = None, stream=None):
+    """q: [T, H, 128] bf16 -> (q_fp8 [T,H,128] u8, q_scale [T,H] f32, w [T,H] f32)."""
+    args, outs = _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp8, q_scale, w_out, fp8=True)
+    _run("fp4idx_pack_q_fp8", args + [_stream(stream)])
+    return outs
+
+
+def prepare_pack_q_fp8(q, pos, cos_sin, w_in, w_scale=1.0, q_fp8=None, q_scale=None, w_out=None, stream=None):
+    """fp4idx_pack_q_fp8 with its arguments marshalled once: (Prepared, outputs)."""
+    args, outs = _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_fp8, q_scale, w_out, fp8=True)
+    return Prepared("fp4idx_pack_q_fp8", args + [_stream(stream)], keep=(q, pos, cos_sin, w_in) + outs), outs
+
+
+def _write_k_pack_q_fp8_args(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, pos_q, w_in, w_scale, q_fp8, q_scale,
+                             w_out, stream):
+    kargs = _write_k_fp8_args(k, pos_k, slot, norm_w, eps, cos_sin, pool)
+    qargs, outs = _pack_q_args(q, pos_q, cos_sin, w_in, w_scale, q_fp8, q_scale, w_out, with_table=False, fp8=True)
+    return kargs + qargs + [_stream(stream)], outs
+
+
+def fp4idx_write_k_pack_q_fp8(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, pos_q, w_in, w_scale=1.0, q_fp8=None,
+                              q_scale=None, w_out=None, stream=None):
+    """write_k_fp8 and pack_q_fp8 in one launch; returns (q_fp8, q_scale, w_out)."""
+    args, outs = _write_k_pack_q_fp8_args(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, pos_q, w_in, w_scale,
+                                          q_fp8, q_scale, w_out, stream)
+    _run("fp4idx_write_k_pack_q_fp8", args)
+    return outs
+
+
+def prepare_write_k_pack_q_fp8(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, pos_q, w_in, w_scale=1.0,
+                               q_fp8=None, q_scale=None, w_out=None, stream=None):
+    """fp4idx_write_k_pack_q_fp8 with its arguments marshalled once: (Prepared, outputs)."""
+    args, outs = _write_k_pack_q_fp8_args(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, pos_q, w_in, w_scale,
+                                          q_fp8, q_scale, w_out, stream)
+    keep = (k, pos_k, slot, norm_w, cos_sin, pool, q, pos_q, w_in) + outs
+    return Prepared("fp4idx_write_k_pack_q_fp8", args, keep=keep), outs
+
+
+def _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool, max_rows_per_req, max_ctx,
+                         logits, stream):
+    T, H = int(q_fp8.shape[0]), int(q_fp8.shape[1])
+    n_reqs = int(req_row_indptr.numel()) - 1
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise Fp4idxError("mqa_logits_fp8: block_table must be [n_reqs, stride] with unit inner stride")
+    if logits is None:
+        logits = torch.empty((T, max(1, int(max_ctx))), dtype=torch.float32, device=q_fp8.device)
+    if logits.stride(-1) != 1:
+        raise Fp4idxError("mqa_logits_fp8: logits must have unit inner stride")
+    for t, name in ((q_fp8, "q_fp8"), (q_scale, "q_scale"), (w, "w"), (req_row_indptr, "indptr"),
+                    (row_ctx, "row_ctx"), (pool, "pool")):
+        if not t.is_contiguous():
+            raise Fp4idxError(f"mqa_logits_fp8: {name} must be contiguous")
+    num_pages = pool.numel() // FP8_PAGE_BYTES
+    args = [_ptr(q_fp8, _U8, "q_fp8"), _ptr(q_scale, _F32, "q_scale"), _ptr(w, _F32, "w"), T, H,
+            _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
+            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(pool, _U8, "pool"), num_pages,
+            _ptr(logits, _F32, "logits"), int(logits.stride(0)), int(max_rows_per_req), int(max_ctx),
+            _stream(stream)]
+    return args, logits
+
+
+def fp4idx_mqa_logits_fp8(q_fp8: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor,
+                          req_row_indptr: torch.Tensor, row_ctx: torch.Tensor, block_table: torch.Tensor,
+                          pool: torch.Tensor, max_rows_per_req: int, max_ctx: int, logits: torch.Tensor = None,
+                          stream=None) -> torch.Tensor:
+    """Paged logits over the FP8 pool [T, stride] fp32; only [0, ctx[t]) of each row is written."""
+    args, logits = _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool,
+                                        max_rows_per_req, max_ctx, logits, stream)
+    _run("fp4idx_mqa_logits_fp8", args)
+    return logits
+
+
+def prepare_mqa_logits_fp8(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool, max_rows_per_req,
+                           max_ctx, logits=None, stream=None):
+    """fp4idx_mqa_logits_fp8 with its arguments marshalled once: (Prepared, logits)."""
+    args, logits = _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool,
+                                        max_rows_per_req, max_ctx, logits, stream)
+    keep = (q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool, logits)
+    return Prepared("fp4idx_mqa_logits_fp8", args, keep=keep), logits
 
 
 write_k = fp4idx_write_k
@@ -334,3 +460,7 @@ topk = fp4idx_topk
 write_k_pack_q = fp4idx_write_k_pack_q
 read_k = fp4idx_read_k
 time_next_call = fp4idx_time_next_call
+write_k_fp8 = fp4idx_write_k_fp8
+pack_q_fp8 = fp4idx_pack_q_fp8
+write_k_pack_q_fp8 = fp4idx_write_k_pack_q_fp8
+mqa_logits_fp8 = fp4idx_mqa_logits_fp8

@@ -73,6 +73,34 @@ def random_pool(rng: np.random.Generator, num_pages: int, scale_lo: int = 124, s
     return payload, scale
 
 
+FP8_PAGE_BYTES = 8448   # 64 x 128 code bytes, then 64 fp32 scales
+
+
+def _fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform E4M3 bytes with the two NaN codes (0x7F, 0xFF) moved to the
+    neighbouring finite code."""
+    c = rng.integers(0, 256, shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)
+
+
+def random_pool_fp8(rng: np.random.Generator, num_pages: int, e_lo: int = -9, e_hi: int = -5) -> np.ndarray:
+    """A fused FP8 pool filled directly: uniform E4M3 codes and per-token
+    scales 2^e, e uniform in [e_lo, e_hi] (an RMS-normalised, rotated N(0,1)
+    row has its largest element near 3.5, i.e. e near -7)."""
+    pool = np.empty((num_pages, FP8_PAGE_BYTES), np.uint8)
+    pool[:, :8192] = _fp8_codes(rng, (num_pages, 8192))
+    pool[:, 8192:].view(np.float32)[:] = np.ldexp(np.float32(1.0), rng.integers(e_lo, e_hi + 1, (num_pages, 64)))
+    return pool.reshape(-1)
+
+
+def random_q_fp8(rng: np.random.Generator, n_rows: int, heads: int = 64, e_lo: int = -9, e_hi: int = -5):
+    """Packed FP8 Q drawn directly: codes [T, H, 128], scales 2^e [T, H], weights U(0, 1)."""
+    qf = _fp8_codes(rng, (n_rows, heads, 128))
+    qs = np.ldexp(np.float32(1.0), rng.integers(e_lo, e_hi + 1, (n_rows, heads))).astype(np.float32)
+    w = rng.uniform(0, 1, (n_rows, heads)).astype(np.float32)
+    return qf, qs, w
+
+
 @dataclass
 class Workload:
     name: str

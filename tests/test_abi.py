@@ -94,6 +94,46 @@ def test_host_validation_rejects_before_any_launch(F):
                                  None) == 0
 
 
+def test_fp8_calls_validate_like_their_fp4_twins(F):
+    lib = F.load()
+    E = -1
+    fake = ctypes.c_void_p(0x1000)
+    # write_k_fp8: nulls, bad stride, unaligned pool, negative eps; empty batch is a no-op
+    assert lib.fp4idx_write_k_fp8(None, 5, 128, None, None, None, 1e-6, None, 10, None, 1, None) == E
+    assert lib.fp4idx_write_k_fp8(fake, 5, 120, fake, fake, fake, 1e-6, fake, 10, fake, 1, None) == E
+    assert lib.fp4idx_write_k_fp8(fake, 5, 128, fake, fake, fake, 1e-6, fake, 10, ctypes.c_void_p(0x1008), 1,
+                                  None) == E
+    assert lib.fp4idx_write_k_fp8(fake, 5, 128, fake, fake, fake, -1.0, fake, 10, fake, 1, None) == E
+    assert lib.fp4idx_write_k_fp8(None, 0, 128, None, None, None, 1e-6, None, 10, None, 0, None) == 0
+    # pack_q_fp8: head counts, stride, unaligned code output
+    for h in (0, 8, 48, 256):
+        assert lib.fp4idx_pack_q_fp8(fake, 2, h, 128 * 64, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
+    assert lib.fp4idx_pack_q_fp8(fake, 2, 64, 100, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
+    assert lib.fp4idx_pack_q_fp8(fake, 2, 64, 128 * 64, fake, fake, 10, fake, 1.0, ctypes.c_void_p(0x1004), fake,
+                                 fake, None) == E
+    # one-launch pair: each half checked as its own call
+    wk = [fake, 5, 128, fake, fake, fake, 1e-6, fake, 10, fake, 1]
+    pq = [fake, 2, 64, 128 * 64, fake, fake, 1.0, fake, fake, fake]
+    assert lib.fp4idx_write_k_pack_q_fp8(*wk[:2], 100, *wk[3:], *pq, None) == E
+    assert lib.fp4idx_write_k_pack_q_fp8(*wk, fake, 2, 48, *pq[3:], None) == E
+    assert lib.fp4idx_write_k_pack_q_fp8(None, 0, 128, None, None, None, 1e-6, None, 10, None, 0,
+                                         None, 0, 64, 128 * 64, None, None, 1.0, None, None, None, None) == 0
+    # logits_fp8: ctx bound beyond the table / the row, head count, unaligned scale, empty pool
+    args = [fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, 4, fake, 4096, 4, 128, None]
+    a = list(args); a[15] = 129
+    assert lib.fp4idx_mqa_logits_fp8(*a) == E
+    a = list(args); a[13] = 100
+    assert lib.fp4idx_mqa_logits_fp8(*a) == E
+    a = list(args); a[4] = 40
+    assert lib.fp4idx_mqa_logits_fp8(*a) == E
+    a = list(args); a[1] = ctypes.c_void_p(0x1002)
+    assert lib.fp4idx_mqa_logits_fp8(*a) == E
+    a = list(args); a[11] = 0
+    assert lib.fp4idx_mqa_logits_fp8(*a) == E
+    assert lib.fp4idx_mqa_logits_fp8(None, None, None, 0, 64, None, 0, None, None, 0, None, 0, None, 0, 0, 0,
+                                     None) == 0
+
+
 def test_binding_imports_no_oracle():
     import sparse_attention_fp4_fp4idx_amd.fp4idx as m
     src = open(m.__file__).read()

@@ -98,6 +98,30 @@ def test_write_k_edges_strided_skip_extremes(F, orc, n):
         assert np.array_equal(po, pg) and np.array_equal(so, sg), eps
 
 
+def test_write_k_skips_tokens_outside_pool_or_table(F, orc):
+    """A slot past the pool or a position outside the table skips the token
+    (the kernel's own range checks): the pools equal the oracle's with those
+    tokens marked as padding."""
+    rng = np.random.default_rng(24)
+    n, pages, max_pos = 200, 5, 512
+    tab = W.rope_table(max_pos)
+    k = W.bf16_normal(rng, (n, 128))
+    slot = rng.permutation(pages * 64)[:n].astype(np.int32)
+    pos = rng.integers(0, max_pos, n).astype(np.int32)
+    gslot, gpos = slot.copy(), pos.copy()
+    gslot[[3, 50]] = [pages * 64, 2 ** 31 - 1]
+    gpos[[7, 90]] = [max_pos, -2]
+    oslot = slot.copy()
+    oslot[[3, 50, 7, 90]] = -1
+    nw = W.norm_weight(rng)
+    pay_o = np.full(pages * 4096, 0xA5, np.uint8); sc_o = np.full(pages * 256, 0x5A, np.uint8)
+    orc.write_k(k, pos, oslot, nw, 1e-6, tab, pay_o, sc_o)
+    pay_g = dev(np.full(pages * 4096, 0xA5, np.uint8)); sc_g = dev(np.full(pages * 256, 0x5A, np.uint8))
+    F.write_k(bf16(k), dev(gpos), dev(gslot), bf16(nw), 1e-6, bf16(tab), pay_g, sc_g)
+    torch.cuda.synchronize()
+    assert np.array_equal(pay_g.cpu().numpy(), pay_o) and np.array_equal(sc_g.cpu().numpy(), sc_o)
+
+
 def test_write_k_bulk_65536_bit_exact(F, orc):
     wl = W.make(4, with_q=False)
     say("write_k bulk:", wl.k_new.shape[0], "tokens into", wl.num_pages, "pages")
@@ -141,6 +165,27 @@ def test_pack_q_edges_zero_and_tiny_rows(F, orc):
     o, g = _pack_both(F, orc, q, pos, tab, w, 1.0)
     for a, b in zip(o, g):
         assert np.array_equal(a, b)
+
+
+def test_pack_q_position_outside_table_encodes_zero(F, orc):
+    """Rows whose position is outside the table come out as the encoding of
+    the +0 vector (the oracle's quantiser on zeros); the other rows as usual."""
+    rng = np.random.default_rng(25)
+    T, heads, max_pos = 9, 16, 256
+    tab = W.rope_table(max_pos)
+    q = W.bf16_normal(rng, (T, heads, 128))
+    pos = rng.integers(0, max_pos, T).astype(np.int32)
+    gpos = pos.copy()
+    gpos[[2, 5]] = [max_pos, -1]
+    w = rng.uniform(0, 1, (T, heads)).astype(np.float32)
+    qf, qs, wo = orc.pack_q(q, pos, tab, w, 1.0)
+    zc, zs = orc.quant128(np.zeros(128, np.float32))
+    qf[[2, 5]] = zc
+    qs[[2, 5]] = zs
+    g = F.pack_q(bf16(q), dev(gpos), bf16(tab), dev(w), 1.0)
+    torch.cuda.synchronize()
+    for a, b in zip((qf, qs, wo), g):
+        assert np.array_equal(a.view(np.uint8), b.cpu().numpy().view(np.uint8))
 
 
 @pytest.mark.parametrize("n_tok,n_rows", [(64, 64), (1000, 7), (0, 5), (300, 0)])
