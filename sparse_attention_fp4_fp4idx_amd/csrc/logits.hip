@@ -73,8 +73,14 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
 // B lane l = (token l%16, block l/16): exactly the 16-byte payload chunk at
 // [page][block][token] and its UE8M0 byte; A lane l = (head l%16, block l/16).
 struct Fp4Split {
-  static constexpr int kDecodeWaves = 4;
-  static constexpr int kMaxRowsWide = 4;  // rows per wave at 128 heads
+  // Launch shapes (64 heads or fewer for the wave counts): rows per wave
+  // at most (kRowsCapWide at 128 heads), and per rows-per-wave class the
+  // resident waves per SIMD asked of the compiler, the pages per wave and
+  // the pages in flight.
+  static constexpr int kRowsCap = 4, kRowsCapWide = 4;
+  static constexpr int kWaves1 = 4, kPpw1 = 4, kD1 = 4;  // one row per wave (decode)
+  static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;  // two rows
+  static constexpr int kPpwMany = 8, kDMany = 2;         // three or four rows
   struct Page {  // 4 tiles of 16 tokens
     uint4 b[4];
     uint32_t s[4];
@@ -118,8 +124,12 @@ struct Fp4Split {
 // four block scales of an operand row equal: the MFMA scale is the fp32
 // scale's exponent field (an E8M0 byte).
 struct Fp8Fused {
-  static constexpr int kDecodeWaves = 2;
-  static constexpr int kMaxRowsWide = 2;  // 8-register operands: 3+ rows at 128 heads spill
+  // launch shapes as for Fp4Split; 8-register operands and 36-register pages
+  // need more registers per row and per page in flight
+  static constexpr int kRowsCap = 4, kRowsCapWide = 2;   // 3+ rows at 128 heads spill
+  static constexpr int kWaves1 = 2, kPpw1 = 4, kD1 = 4;
+  static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;
+  static constexpr int kPpwMany = 8, kDMany = 2;
   struct Page {
     uint4 lo[4], hi[4];
     uint32_t s[4];
@@ -165,7 +175,7 @@ struct Fp8Fused {
 // flight, the same bytes in flight per SIMD); more rows keep their register
 // budget.
 template <typename FMT, int RW, int NMT>
-constexpr int kMinWavesPerSimd = (RW == 1 && NMT <= 4) ? FMT::kDecodeWaves : 1;
+constexpr int kMinWavesPerSimd = NMT > 4 ? 1 : RW == 1 ? FMT::kWaves1 : RW == 2 ? FMT::kWaves2 : 1;
 
 template <typename FMT, int RW, int NMT, int PPW, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void mqa_logits_kernel(
@@ -299,10 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
       for (int r = 0; r < RW; ++r) {
         if (r < nrows) {
           // partial sums of this lane's 16 heads for the page's 4 tiles
-          float p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v4f d[NMT];
+          auto tile_mfma = [&](int t, v4f(&d)[NMT]) {
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
               switch (mt & 3) {
@@ -312,7 +319,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
                 default: d[mt] = FMT::template mfma<3>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
               }
             }
-            // two fixed-order chains (even / odd M-tiles), then their sum
+          };
+          // two fixed-order chains (even / odd M-tiles), then their sum
+          auto tile_sum = [&](const v4f(&d)[NMT]) {
             float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
             for (int mt = 0; mt < NMT; ++mt) {
@@ -323,7 +332,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
                 else acc0 = __builtin_fmaf(wv[r][mt][e], rl, acc0);
               }
             }
-            p[t] = acc0 + acc1;
+            return acc0 + acc1;
+          };
+          float p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v4f d[NMT];
+            tile_mfma(t, d);
+            p[t] = tile_sum(d);
             // one row per wave: keep a single tile's MFMA results live at a
             // time (register budget for four waves per SIMD)
             if (RW == 1) __builtin_amdgcn_sched_barrier(0);
@@ -359,21 +375,27 @@ static hipError_t launch_nmt(const uint8_t* q, const uint8_t* q_scale, const flo
                              int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
                              int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  constexpr int cap = NMT == 8 ? FMT::kRowsCapWide : FMT::kRowsCap;
   if (max_rows_per_req <= 1)
-    return launch_rw<FMT, 1, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-  if (max_rows_per_req == 2)
-    return launch_rw<FMT, 2, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-  if constexpr (NMT == 8 && FMT::kMaxRowsWide == 2) {
-    return launch_rw<FMT, 2, NMT, 4, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 1, NMT, FMT::kPpw1, FMT::kD1>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
+                                                        bt_stride, payload, scale, num_pages, logits, logits_stride,
+                                                        max_rows_per_req, max_ctx, stream);
+  if constexpr (cap <= 2) {
+    return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
+                                                        bt_stride, payload, scale, num_pages, logits, logits_stride,
+                                                        max_rows_per_req, max_ctx, stream);
   } else {
+    if (max_rows_per_req == 2)
+      return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
+                                                          bt_stride, payload, scale, num_pages, logits, logits_stride,
+                                                          max_rows_per_req, max_ctx, stream);
     if (max_rows_per_req == 3 || max_rows_per_req == 6)
-      return launch_rw<FMT, 3, NMT, 8, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                          scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    return launch_rw<FMT, 4, NMT, 8, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                        scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+      return launch_rw<FMT, 3, NMT, FMT::kPpwMany, FMT::kDMany>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
+                                                                bt_stride, payload, scale, num_pages, logits,
+                                                                logits_stride, max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 4, NMT, FMT::kPpwMany, FMT::kDMany>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
+                                                              bt_stride, payload, scale, num_pages, logits,
+                                                              logits_stride, max_rows_per_req, max_ctx, stream);
   }
 }
 
