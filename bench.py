@@ -323,7 +323,8 @@ def main():
             "ms_per_step": round(ms8, 4), "scores_per_s": round(scores / (ms8 * 1e-3), 1),
             "kernels_us": {n: round(v * 1e3, 2) for n, v in pk8.items()},
             "logits_roofline": {"bound": "hbm", "achieved": round(a8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(a8 / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": l8},
+                                "frac": round(a8 / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": l8,
+                                "traffic": measured_traffic(f"config{args.config}:fp8_mqa_logits")},
             "bytes_per_cached_token": 132, "input_copies": copies8,
             "fp4_vs_fp8_step_speedup": round(ms8 / ms_per_step, 3)}
         log(f"[bench] fp8 cache: {ms8 * 1e3:.1f} us/step, logits {pk8['mqa_logits'] * 1e3:.1f} us "
