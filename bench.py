@@ -21,7 +21,9 @@ where each kernel carries HIP events that its own dispatch stamps with its
 start and end times (fp4idx_time_next_call -> hipExtLaunchKernel); they feed
 the roofline figures.
 
-The same step is then timed on the FP8 indexer cache (132-byte fused tokens,
+The same step is also timed with the logits and the top-k as one fused call
+(fp4idx_mqa_logits_topk, no logits in memory; extras.fused_logits_topk) and
+on the FP8 indexer cache (132-byte fused tokens,
 the layout the FP4 cache replaces) and reported under extras.fp8_cache; the
 headline value is the FP4 path's.
 
@@ -87,6 +89,7 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = decode batch 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache comparison leg")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused logits + top-k leg")
     ap.add_argument("--launch", choices=("prepared", "graph"), default="prepared",
                     help="timed steps as prepared library calls (default) or as HIP graph replays")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to defeat the cache)")
@@ -143,10 +146,11 @@ def main():
     pos_q, indptr, ctx, bt = t(wl.pos_q), t(wl.req_row_indptr), t(wl.row_ctx), t(wl.block_table)
     names = ("write_k", "pack_q", "mqa_logits", "topk")
 
-    def run_cache(fp8: bool, pools: dict):
+    def run_cache(fp8: bool, pools: dict, fused: bool = False):
         """Time the step on one cache format: rotating input copies, the timed
         prepared calls (or graph replays), then the per-kernel event pass.
-        Returns (ms_per_step, per-kernel ms, copies)."""
+        With fused, the logits and the top-k are one fp4idx_mqa_logits_topk
+        call (FP4 cache).  Returns (ms_per_step, per-kernel ms, copies)."""
         qcode_b = 128 if fp8 else 64
         base = dict(pools, q=b16(wl.q), w=t(wl.w), k_new=b16(wl.k_new))
         step_bytes = sum(v.numel() * v.element_size() for v in base.values()) + T * wl.max_ctx * 4 * 2
@@ -188,6 +192,10 @@ def main():
                 (F.pack_q_fp8 if fp8 else F.pack_q)(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_code"],
                                                     s["q_scale"], s["w_out"], stream=strm)
             arm(2)
+            if fused:
+                F.mqa_logits_topk(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt, *pool_args(s), k,
+                                  wl.max_rows_per_req, wl.max_ctx, out_idx=s["top"], stream=strm)
+                return
             (F.mqa_logits_fp8 if fp8 else F.mqa_logits)(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt,
                                                         *pool_args(s), wl.max_rows_per_req, wl.max_ctx,
                                                         logits=s["logits"], stream=strm)
@@ -215,10 +223,16 @@ def main():
                 pw, _ = (F.prepare_write_k_pack_q_fp8 if fp8 else F.prepare_write_k_pack_q)(
                     s_["k_new"], pos_new, slot_new, norm_w, wl.eps, tab, *pool_args(s_), s_["q"], pos_q, s_["w"],
                     wl.w_scale, s_["q_code"], s_["q_scale"], s_["w_out"], stream=stream)
-                pl, _ = (F.prepare_mqa_logits_fp8 if fp8 else F.prepare_mqa_logits)(
-                    s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, *pool_args(s_), wl.max_rows_per_req,
-                    wl.max_ctx, logits=s_["logits"], stream=stream)
-                pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
+                if fused:
+                    pl, _ = F.prepare_mqa_logits_topk(s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt,
+                                                      *pool_args(s_), k, wl.max_rows_per_req, wl.max_ctx,
+                                                      out_idx=s_["top"], stream=stream)
+                    pt = lambda: None  # noqa: E731
+                else:
+                    pl, _ = (F.prepare_mqa_logits_fp8 if fp8 else F.prepare_mqa_logits)(
+                        s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, *pool_args(s_),
+                        wl.max_rows_per_req, wl.max_ctx, logits=s_["logits"], stream=stream)
+                    pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
 
                 def run(pw=pw, pl=pl, pt=pt):
                     pw()
@@ -249,8 +263,12 @@ def main():
         for i in range(args.steps):
             step(sets[i % copies], stream, evs[i])
         torch.cuda.synchronize()
+        used = names[:3] if fused else names
         per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
-                      for j, n in enumerate(names)}
+                      for j, n in enumerate(used)}
+        if fused:
+            per_kernel = {"write_k": per_kernel["write_k"], "pack_q": per_kernel["pack_q"],
+                          "mqa_logits_topk": per_kernel["mqa_logits"]}
         del sets, runners
         return elapsed * 1e3 / args.steps, per_kernel, copies
 
@@ -328,6 +346,17 @@ def main():
             "bytes_per_cached_token": 132, "input_copies": copies8,
             "fp4_vs_fp8_step_speedup": round(ms8 / ms_per_step, 3)}
         log(f"[bench] fp8 cache: {ms8 * 1e3:.1f} us/step, logits {pk8['mqa_logits'] * 1e3:.1f} us "
+            f"({time.time() - t0:.1f}s)")
+
+    # ---- the fused logits + top-k call on the same workload (FP4 cache, no logits in memory)
+    if not args.no_fused and wl.heads <= 64 and wl.max_ctx <= F.FUSED_MAX_CTX:
+        msf, pkf, copiesf = run_cache(False, dict(payload=payload, scale=scale), fused=True)
+        extras["fused_logits_topk"] = {
+            "ms_per_step": round(msf, 4), "scores_per_s": round(scores / (msf * 1e-3), 1),
+            "kernels_us": {n: round(v * 1e3, 2) for n, v in pkf.items()},
+            "two_call_logits_plus_topk_us": round((per_kernel_ms["mqa_logits"] + per_kernel_ms["topk"]) * 1e3, 2),
+            "step_speedup_vs_two_calls": round(ms_per_step / msf, 3), "input_copies": copiesf}
+        log(f"[bench] fused logits+top-k: {msf * 1e3:.1f} us/step, kernel {pkf['mqa_logits_topk'] * 1e3:.1f} us "
             f"({time.time() - t0:.1f}s)")
 
     # ---- CPU baseline: the oracle on the same workload (bounded sample)

@@ -53,6 +53,7 @@ extern "C" {
 #define FP4IDX_SCALE_PAGE_BYTES 256    /* [1, 4, 64]     */
 #define FP4IDX_FP8_PAGE_BYTES 8448     /* [64][128] codes + [64] fp32 scales */
 #define FP4IDX_MAX_TOPK 2048
+#define FP4IDX_FUSED_MAX_CTX 32768     /* longest row of fp4idx_mqa_logits_topk */
 
 /*
  * Fused K writer.  [P2] Modifications / fp4_indexer_hip.py and compress.py:
@@ -186,6 +187,27 @@ int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, cons
                 int32_t* out_idx, int64_t max_ctx, void* stream);
 
 /*
+ * Fused logits + top-k: the top-k positions of every row without writing the
+ * logits to memory.  [P3] Changes (sorted top-k selection) over the FP4
+ * paged-MQA logits of [P2] Modifications (decode logits dispatch).
+ *
+ * Arguments as fp4idx_mqa_logits (without the logits buffer) plus k and
+ * out_idx as fp4idx_topk; n_heads 16, 32 or 64; max_ctx <=
+ * FP4IDX_FUSED_MAX_CTX (the row is held in LDS); max_rows_per_req >= 1 when
+ * n_rows > 0.  out_idx [n_rows, k] int32 receives exactly what
+ * fp4idx_mqa_logits followed by fp4idx_topk would write (same logits bit
+ * for bit, same selection and order), including the -1 padding and rows of
+ * context 0.  One work-group per row scores every page of its row, so the
+ * call suits batches of single-row requests (decode); rows of one request
+ * each read the request's pages, where the two-call path shares them.
+ */
+int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                           int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                           const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                           const uint8_t* payload, const uint8_t* scale, int64_t num_pages, int32_t k,
+                           int32_t* out_idx, int32_t max_rows_per_req, int64_t max_ctx, void* stream);
+
+/*
  * Split-pool reader: pool tokens back to their values.  [P1] Summary (split
  * writer and reader for the FP4 pool); [P2] Device memory.
  *
@@ -266,8 +288,9 @@ int fp4idx_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const floa
 /*
  * Kernel timing (measurement support, not part of the method).  Arms two HIP
  * events for the calling thread's next call of fp4idx_write_k, fp4idx_pack_q,
- * fp4idx_write_k_pack_q, fp4idx_mqa_logits, fp4idx_topk, fp4idx_read_k or
- * one of the *_fp8 calls; each of these launches exactly one kernel.
+ * fp4idx_write_k_pack_q, fp4idx_mqa_logits, fp4idx_topk, fp4idx_mqa_logits_topk,
+ * fp4idx_read_k or one of the *_fp8 calls; each of these launches exactly one
+ * kernel.
  * That kernel is then dispatched with hipExtLaunchKernel, which stamps the
  * events with the dispatch's own start and end times, so
  * hipEventElapsedTime(start, stop) is the kernel's execution time with no

@@ -181,6 +181,32 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
                                             max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }
 
+int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                           int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                           const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                           const uint8_t* payload, const uint8_t* scale, int64_t num_pages, int32_t k,
+                           int32_t* out_idx, int32_t max_rows_per_req, int64_t max_ctx, void* stream) {
+  const TimingScope timing_scope;
+  if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || max_rows_per_req < 0 || max_ctx < 0)
+    return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64) return FP4IDX_E_INVALID;
+  if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;
+  if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > FP4IDX_FUSED_MAX_CTX) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
+  if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
+  if (max_rows_per_req < 1) return FP4IDX_E_INVALID;  // every row's k outputs are written
+  if (max_ctx > 0 && num_pages == 0) return FP4IDX_E_INVALID;
+  if (!q_fp4 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !out_idx ||
+      (max_ctx > 0 && (!payload || !scale)))
+    return FP4IDX_E_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_mqa_logits_topk(q_fp4, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+                                                 block_table, bt_stride, payload, scale, num_pages, k, out_idx,
+                                                 max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
+}
+
 int fp4idx_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,
                   int64_t n_tokens, float* out, int64_t out_row_stride, void* stream) {
   const TimingScope timing_scope;

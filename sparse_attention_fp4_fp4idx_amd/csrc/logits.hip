@@ -40,133 +40,9 @@
 // Each (row, token) is computed by exactly one lane in a fixed order, so the
 // result does not depend on batch composition, page placement or grid shape.
 #include "launch.hpp"
+#include "logits_core.hpp"
 
 namespace fp4idx {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ld_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-// ReLU on the bit pattern: every negative float (and -0) is a negative int32,
-// so max(bits, 0) gives +0 for them and leaves non-negative values unchanged.
-// One integer max instead of the quieting and comparing pair fmaxf needs.
-__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// Sum p[j] over the four 16-lane groups; afterwards lane l holds slot
-// (l/16)'s total.  permlane32_swap(a, b): a <- [a.lo32, b.lo32], b <- [a.hi32, b.hi32];
-// permlane16_swap(a, b): swaps rows 1 and 3 of a with rows 0 and 2 of b.
-__device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3) {
-  auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
-  auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
-  const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
-  const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
-  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// FP4 split pools: payload [page][block][token][16 B], scale [page][block][token].
-// B lane l = (token l%16, block l/16): exactly the 16-byte payload chunk at
-// [page][block][token] and its UE8M0 byte; A lane l = (head l%16, block l/16).
-struct Fp4Split {
-  // Launch shapes (64 heads or fewer for the wave counts): rows per wave
-  // at most (kRowsCapWide at 128 heads), and per rows-per-wave class the
-  // resident waves per SIMD asked of the compiler, the pages per wave and
-  // the pages in flight.
-  static constexpr int kRowsCap = 4, kRowsCapWide = 4;
-  static constexpr int kWaves1 = 4, kPpw1 = 4, kD1 = 4;  // one row per wave (decode)
-  static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;  // two rows
-  static constexpr int kPpwMany = 8, kDMany = 2;         // three or four rows
-  struct Page {  // 4 tiles of 16 tokens
-    uint4 b[4];
-    uint32_t s[4];
-  };
-  typedef uint4 QOp;
-  static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(lg * 1024 + li * 16); }
-  static __device__ __forceinline__ uint32_t lane_sc(int li, int lg) { return (uint32_t)(lg * 64 + li); }
-  static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ payload,
-                                                   const uint8_t* __restrict__ scale, int64_t pid, uint32_t lp,
-                                                   uint32_t ls) {
-    const uint8_t* pp = payload + pid * 4096 + lp;
-    const uint8_t* sp = scale + pid * 256 + ls;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pr.b[t] = ld_stream16(pp + t * 256);
-      pr.s[t] = sp[t * 16];
-    }
-  }
-  static __device__ __forceinline__ QOp load_q(const uint8_t* __restrict__ q, int64_t hrow, int lg) {
-    return *reinterpret_cast<const uint4*>(q + hrow * 64 + lg * 16);
-  }
-  static __device__ __forceinline__ uint32_t q_scale_byte(const uint8_t* __restrict__ qs, int64_t hrow, int lg) {
-    return qs[hrow * 4 + lg];
-  }
-  template <int OPA>
-  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
-    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-    const v8i bv = {(int)p.b[t].x, (int)p.b[t].y, (int)p.b[t].z, (int)p.b[t].w, 0, 0, 0, 0};
-    const v4f z = {0.f, 0.f, 0.f, 0.f};
-    // cbsz = blgp = 4: both operands FP4 (e2m1); op_sel picks the scale byte.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 0, (int)p.s[t]);
-  }
-};
-
-// FP8 fused pool: page = [64 tokens][128 e4m3 codes] then [64] fp32 scales
-// (powers of two), 8448 bytes.  The fp8 operand holds 32 bytes per lane;
-// A lane l = (head l%16, bytes 32(l/16)..+31 of the head's codes), B lane
-// l = (token l%16, the same bytes of the token): A and B place code i in the
-// same K slot, so the dot product is the plain one whatever order the MFMA
-// gives the 128 slots.  One scale per token and per (row, head) makes all
-// four block scales of an operand row equal: the MFMA scale is the fp32
-// scale's exponent field (an E8M0 byte).
-struct Fp8Fused {
-  // launch shapes as for Fp4Split; 8-register operands and 36-register pages
-  // need more registers per row and per page in flight
-  static constexpr int kRowsCap = 4, kRowsCapWide = 2;   // 3+ rows at 128 heads spill
-  static constexpr int kWaves1 = 2, kPpw1 = 4, kD1 = 4;
-  static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;
-  static constexpr int kPpwMany = 8, kDMany = 2;
-  struct Page {
-    uint4 lo[4], hi[4];
-    uint32_t s[4];
-  };
-  struct QOp {
-    uint4 lo, hi;
-  };
-  static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(li * 128 + lg * 32); }
-  static __device__ __forceinline__ uint32_t lane_sc(int li, int) { return (uint32_t)(8192 + li * 4); }
-  static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ pool, const uint8_t*,
-                                                   int64_t pid, uint32_t lp, uint32_t ls) {
-    const uint8_t* pp = pool + pid * 8448;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pr.lo[t] = ld_stream16(pp + lp + t * 2048);
-      pr.hi[t] = ld_stream16(pp + lp + t * 2048 + 16);
-      pr.s[t] = (*reinterpret_cast<const uint32_t*>(pp + ls + t * 64) >> 23) & 0xFFu;
-    }
-  }
-  static __device__ __forceinline__ QOp load_q(const uint8_t* __restrict__ q, int64_t hrow, int lg) {
-    const uint4* p = reinterpret_cast<const uint4*>(q + hrow * 128 + lg * 32);
-    return QOp{p[0], p[1]};
-  }
-  static __device__ __forceinline__ uint32_t q_scale_byte(const uint8_t* __restrict__ qs, int64_t hrow, int) {
-    return (reinterpret_cast<const uint32_t*>(qs)[hrow] >> 23) & 0xFFu;
-  }
-  template <int OPA>
-  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
-    const v8i av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
-                    (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
-    const v8i bv = {(int)p.lo[t].x, (int)p.lo[t].y, (int)p.lo[t].z, (int)p.lo[t].w,
-                    (int)p.hi[t].x, (int)p.hi[t].y, (int)p.hi[t].z, (int)p.hi[t].w};
-    const v4f z = {0.f, 0.f, 0.f, 0.f};
-    // cbsz = blgp = 0: both operands FP8 e4m3.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 0, 0, OPA, (int)sa, 0, (int)p.s[t]);
-  }
-};
 
 // RW rows per wave, NMT = heads/16, PPW pages per wave, D pages in flight.
 // Few rows per wave (decode) means little work per wave: keep several waves
@@ -308,44 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         if (r < nrows) {
-          // partial sums of this lane's 16 heads for the page's 4 tiles
-          auto tile_mfma = [&](int t, v4f(&d)[NMT]) {
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
-              switch (mt & 3) {
-                case 0: d[mt] = FMT::template mfma<0>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
-                case 1: d[mt] = FMT::template mfma<1>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
-                case 2: d[mt] = FMT::template mfma<2>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
-                default: d[mt] = FMT::template mfma<3>(aq[r][mt], cur[i], t, asc[r][mt >> 2]); break;
-              }
-            }
-          };
-          // two fixed-order chains (even / odd M-tiles), then their sum
-          auto tile_sum = [&](const v4f(&d)[NMT]) {
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float rl = relu(d[mt][e]);
-                if (mt & 1) acc1 = __builtin_fmaf(wv[r][mt][e], rl, acc1);
-                else acc0 = __builtin_fmaf(wv[r][mt][e], rl, acc0);
-              }
-            }
-            return acc0 + acc1;
-          };
-          float p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v4f d[NMT];
-            tile_mfma(t, d);
-            p[t] = tile_sum(d);
-            // one row per wave: keep a single tile's MFMA results live at a
-            // time (register budget for four waves per SIMD)
-            if (RW == 1) __builtin_amdgcn_sched_barrier(0);
-          }
-          // lane l now gets tile l/16's total for token l%16: 64 consecutive tokens
-          const float tot = reduce4(p[0], p[1], p[2], p[3]);
+          const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], cur[i]);
           const int tok = pg * 64 + lane;
           const int c = r == 0 ? ctx_r[0] : r == 1 ? ctx_r[1] : r == 2 ? ctx_r[2] : ctx_r[3];
           if (tok < c) logits[(int64_t)(row0 + r) * logits_stride + tok] = tot;

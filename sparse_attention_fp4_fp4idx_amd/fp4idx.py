@@ -26,9 +26,10 @@ PAYLOAD_PAGE_BYTES = 4096
 SCALE_PAGE_BYTES = 256
 FP8_PAGE_BYTES = 8448
 MAX_TOPK = 2048
+FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
-          "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
+          "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
           "fp4idx_mqa_logits_fp8")
 EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
@@ -58,6 +59,7 @@ def load():
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
+    lib.fp4idx_mqa_logits_topk.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, i32, P, i32, i64, P]
     lib.fp4idx_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64, P]
     lib.fp4idx_pack_q_fp8.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
     lib.fp4idx_write_k_pack_q_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64,
@@ -294,6 +296,47 @@ def prepare_mqa_logits(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, 
     return Prepared("fp4idx_mqa_logits", args, keep=keep), logits
 
 
+def _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, k,
+                          max_rows_per_req, max_ctx, out_idx, stream):
+    T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
+    n_reqs = int(req_row_indptr.numel()) - 1
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise Fp4idxError("mqa_logits_topk: block_table must be [n_reqs, stride] with unit inner stride")
+    if out_idx is None:
+        out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=q_fp4.device)
+    for t, name in ((q_fp4, "q_fp4"), (q_scale, "q_scale"), (w, "w"), (req_row_indptr, "indptr"),
+                    (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale"), (out_idx, "out_idx")):
+        if not t.is_contiguous():
+            raise Fp4idxError(f"mqa_logits_topk: {name} must be contiguous")
+    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
+            _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
+            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
+            _ptr(scale, _U8, "scale"), num_pages, int(k), _ptr(out_idx, _I32, "out_idx"), int(max_rows_per_req),
+            int(max_ctx), _stream(stream)]
+    return args, out_idx
+
+
+def fp4idx_mqa_logits_topk(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor,
+                           req_row_indptr: torch.Tensor, row_ctx: torch.Tensor, block_table: torch.Tensor,
+                           payload: torch.Tensor, scale: torch.Tensor, k: int, max_rows_per_req: int, max_ctx: int,
+                           out_idx: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """[T, k] int32: the top-k positions of every row (as mqa_logits then topk), logits never written."""
+    args, out_idx = _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                          k, max_rows_per_req, max_ctx, out_idx, stream)
+    _run("fp4idx_mqa_logits_topk", args)
+    return out_idx
+
+
+def prepare_mqa_logits_topk(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, k,
+                            max_rows_per_req, max_ctx, out_idx=None, stream=None):
+    """fp4idx_mqa_logits_topk with its arguments marshalled once: (Prepared, out_idx)."""
+    args, out_idx = _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                          k, max_rows_per_req, max_ctx, out_idx, stream)
+    keep = (q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, out_idx)
+    return Prepared("fp4idx_mqa_logits_topk", args, keep=keep), out_idx
+
+
 def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
     T = int(logits.shape[0])
     if logits.stride(-1) != 1:
@@ -464,3 +507,4 @@ write_k_fp8 = fp4idx_write_k_fp8
 pack_q_fp8 = fp4idx_pack_q_fp8
 write_k_pack_q_fp8 = fp4idx_write_k_pack_q_fp8
 mqa_logits_fp8 = fp4idx_mqa_logits_fp8
+mqa_logits_topk = fp4idx_mqa_logits_topk

@@ -134,6 +134,31 @@ def test_fp8_calls_validate_like_their_fp4_twins(F):
                                      None) == 0
 
 
+def test_fused_logits_topk_validates_its_host_arguments(F):
+    lib = F.load()
+    E = -1
+    fake = ctypes.c_void_p(0x1000)
+    #          q     qs    w     T  H   ind   B  ctx   bt    bts pay   sc    P  k   out   mr  mc   stream
+    base = [fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, 16, fake, 4, 128, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.fp4idx_mqa_logits_topk(*a)
+    assert call(a4=128) == E            # 128 heads: not served by the fused call
+    assert call(a4=40) == E
+    for k in (0, -1, 2049):
+        assert call(a13=k) == E
+    assert call(a16=129) == E           # ctx bound beyond the block table
+    assert call(a9=1024, a16=32769) == E  # beyond the fused row
+    assert call(a15=0) == E             # rows exist but no row per request
+    assert call(a15=5) == E             # more rows per request than rows
+    assert call(a0=ctypes.c_void_p(0x1004)) == E
+    assert call(a14=None) == E
+    assert call(a3=0, a15=0) == 0 and call(a6=0) == 0   # empty batch: nothing launched
+
+
 def test_binding_imports_no_oracle():
     import sparse_attention_fp4_fp4idx_amd.fp4idx as m
     src = open(m.__file__).read()
