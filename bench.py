@@ -45,7 +45,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # fp32 lane-ops/s, packed fp32 disabled: 39.3 T
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # fp32 lane-ops/s (256 CUs x 64 lanes x 2.4 GHz), packed fp32 off: 39.3 T
 CACHE_BYTES = 256 << 20
 
 
@@ -295,11 +295,22 @@ def main():
            "pack_q": 21380 * T}
     dom = max(per_kernel_ms, key=per_kernel_ms.get)
     dom_ms = per_kernel_ms[dom]
-    achieved = alg[dom] / (dom_ms * 1e-3) / 1e9
+    # the dominant kernel against each resource it uses; the binding one is the
+    # resource with the largest fraction of its peak (the roofline's limit):
+    # HBM bytes; FP4 MFMA flop (2*128*heads per score); fp32 VALU lane-ops
+    # (ReLU + FMA per head per score, 2*heads; packed fp32 is off)
+    fractions = {"hbm": alg[dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if dom == "mqa_logits":
+        fractions["mfma"] = 2 * 128 * H * scores / (dom_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS
+        fractions["alu"] = 2 * H * scores / (dom_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS
+    bound = max(fractions, key=fractions.get)
+    peak, unit = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_FP4_PEAK_TFLOPS, "TFLOP/s"),
+                  "alu": (VALU_PEAK_TOPS, "T lane-ops/s")}[bound]
     traffic = measured_traffic(f"config{args.config}:{dom}")
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2)}
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(fractions[bound] * peak, 1), "peak": peak,
+                "unit": unit, "frac": round(fractions[bound], 4), "traffic": traffic,
+                "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2),
+                "fractions": {k: round(v, 4) for k, v in fractions.items()}}
 
     # ---- split-pool reader: every cached token of the workload back to fp32, one launch (not part of the step)
     extras = {}
