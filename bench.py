@@ -90,6 +90,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache comparison leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused logits + top-k leg")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak microbenchmarks")
     ap.add_argument("--launch", choices=("prepared", "graph"), default="prepared",
                     help="timed steps as prepared library calls (default) or as HIP graph replays")
     ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to defeat the cache)")
@@ -140,6 +141,37 @@ def main():
         del kc
     torch.cuda.synchronize()
     log(f"[bench] pool filled ({time.time() - t0:.1f}s)")
+
+    # ---- measured peaks (the library's microbenchmarks): FP4 MFMA and streaming HBM read
+    measured = None
+    if not args.no_peaks:
+        sink_f = torch.zeros(1, dtype=torch.float32, device=dev)
+        sink_u = torch.zeros(1, dtype=torch.int32, device=dev)
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        big.fill_(1)
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+        for a_, b_ in pev:
+            a_.record(stream)
+            b_.record(stream)
+        F.peak_mfma_fp4(64, sink_f, stream=stream)
+        F.peak_read(big, sink_u, stream=stream)
+        torch.cuda.synchronize()
+        flop = [0] * 4
+        nbytes = [0] * 4
+        for i in range(4):
+            F.time_next_call(*pev[i])
+            flop[i] = F.peak_mfma_fp4(2048, sink_f, stream=stream)
+            F.time_next_call(*pev[4 + i])
+            nbytes[i] = F.peak_read(big, sink_u, stream=stream)
+        torch.cuda.synchronize()
+        mf = float(np.median([flop[i] / (pev[i][0].elapsed_time(pev[i][1]) * 1e-3) / 1e12 for i in range(4)]))
+        rd = float(np.median([nbytes[i] / (pev[4 + i][0].elapsed_time(pev[4 + i][1]) * 1e-3) / 1e9
+                              for i in range(4)]))
+        measured = {"mfma_fp4_TFLOPs": round(mf, 1), "hbm_read_GBs": round(rd, 1),
+                    "note": "fp4idx_peak_mfma_fp4 (4,096 waves of dependent-free 16x16x128 FP4 MFMA chains) and "
+                            "fp4idx_peak_read (1 GiB streaming read), dispatch-stamped, median of 4"}
+        del big
+        log(f"[bench] measured peaks: FP4 MFMA {mf:.0f} TFLOP/s, HBM read {rd:.0f} GB/s ({time.time() - t0:.1f}s)")
 
     T, H, k = wl.n_rows, wl.heads, wl.topk
     pos_new, slot_new = t(wl.pos_new), t(wl.slot_new)
@@ -311,6 +343,13 @@ def main():
                 "unit": unit, "frac": round(fractions[bound], 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2),
                 "fractions": {k: round(v, 4) for k, v in fractions.items()}}
+    if measured:
+        # the same achieved figures against the measured peaks
+        mp = {"hbm": measured["hbm_read_GBs"], "mfma": measured["mfma_fp4_TFLOPs"]}
+        roofline["frac_vs_measured_peak"] = {r: round(fractions[r] * {"hbm": HBM_PEAK_GBS,
+                                                                    "mfma": MFMA_FP4_PEAK_TFLOPS}[r] / mp[r], 4)
+                                             for r in mp if r in fractions}
+        roofline["measured_peaks"] = measured
 
     # ---- split-pool reader: every cached token of the workload back to fp32, one launch (not part of the step)
     extras = {}

@@ -289,8 +289,8 @@ int fp4idx_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const floa
  * Kernel timing (measurement support, not part of the method).  Arms two HIP
  * events for the calling thread's next call of fp4idx_write_k, fp4idx_pack_q,
  * fp4idx_write_k_pack_q, fp4idx_mqa_logits, fp4idx_topk, fp4idx_mqa_logits_topk,
- * fp4idx_read_k or one of the *_fp8 calls; each of these launches exactly one
- * kernel.
+ * fp4idx_read_k, one of the *_fp8 calls or a peak microbenchmark; each of
+ * these launches exactly one kernel.
  * That kernel is then dispatched with hipExtLaunchKernel, which stamps the
  * events with the dispatch's own start and end times, so
  * hipEventElapsedTime(start, stop) is the kernel's execution time with no
@@ -306,6 +306,24 @@ int fp4idx_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const floa
  * graph capture.  Returns FP4IDX_OK.
  */
 int fp4idx_time_next_call(void* start_event, void* stop_event);
+
+/*
+ * Peak microbenchmarks (measurement support, not part of the method): the
+ * roofline fractions are stated against vendor peaks and against these
+ * measured ones.  Time a call with fp4idx_time_next_call.
+ *
+ * fp4idx_peak_mfma_fp4: 4,096 waves (four per SIMD of a 256-CU device) each
+ *   run 4 * iterations V_MFMA_SCALE_F32_16X16X128_F8F6F4 instructions with
+ *   e2m1 operands (the logits kernel's instruction), 65,536 flop each:
+ *   flop = 4096 * 4 * iterations * 65536.  sink: one device float (never
+ *   written in practice).
+ * fp4idx_peak_read: reads every byte of buf[0, bytes) once with 16-byte
+ *   non-temporal loads; bytes a positive multiple of 16, buf 16-byte
+ *   aligned; sink: one device uint32 (never written in practice).  Use a
+ *   buffer well above the 256 MB last-level cache.
+ */
+int fp4idx_peak_mfma_fp4(int32_t iterations, float* sink, void* stream);
+int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* fp4idx_status_string(int status);

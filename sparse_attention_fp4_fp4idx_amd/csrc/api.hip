@@ -222,6 +222,22 @@ int fp4idx_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_page
                                         static_cast<hipStream_t>(stream)));
 }
 
+int fp4idx_peak_mfma_fp4(int32_t iterations, float* sink, void* stream) {
+  const TimingScope timing_scope;
+  if (iterations < 1 || !sink) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_peak_mfma_fp4(iterations, sink, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  const TimingScope timing_scope;
+  if (bytes <= 0 || (bytes % 16) != 0 || !buf || !sink || !aligned(buf, 16)) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_peak_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
                 int32_t* out_idx, int64_t max_ctx, void* stream) {
   const TimingScope timing_scope;

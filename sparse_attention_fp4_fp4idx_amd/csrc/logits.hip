@@ -165,6 +165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   if (nrows == 0 || page_begin >= pages_needed) return;
   const int n_pages = min(PPW, pages_needed - page_begin);
 
+  // groups of D pages: the current group is scored while the next one loads
 #pragma unroll
   for (int g0 = 0; g0 < PPW; g0 += D) {
     if (g0 >= n_pages) break;

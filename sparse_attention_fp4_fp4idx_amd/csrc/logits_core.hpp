@@ -8,6 +8,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fp4idx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -97,13 +100,16 @@ struct Fp8Fused {
   static constexpr int kWaves1 = 2, kPpw1 = 4, kD1 = 4;
   static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;
   static constexpr int kPpwMany = 8, kDMany = 2;
+  // operands are held as native 8-register vectors (a two-member struct read
+  // as one vector keeps the compiler from splitting it into registers)
   struct Page {
-    uint4 lo[4], hi[4];
+    v8i b[4];
     uint32_t s[4];
   };
-  struct QOp {
-    uint4 lo, hi;
-  };
+  typedef v8i QOp;
+  static __device__ __forceinline__ v8i join(uint4 lo, uint4 hi) {
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
   static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(li * 128 + lg * 32); }
   static __device__ __forceinline__ uint32_t lane_sc(int li, int) { return (uint32_t)(8192 + li * 4); }
   static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ pool, const uint8_t*,
@@ -111,29 +117,36 @@ struct Fp8Fused {
     const uint8_t* pp = pool + pid * 8448;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      pr.lo[t] = ld_stream16(pp + lp + t * 2048);
-      pr.hi[t] = ld_stream16(pp + lp + t * 2048 + 16);
+      pr.b[t] = join(ld_stream16(pp + lp + t * 2048), ld_stream16(pp + lp + t * 2048 + 16));
       pr.s[t] = (*reinterpret_cast<const uint32_t*>(pp + ls + t * 64) >> 23) & 0xFFu;
     }
   }
   static __device__ __forceinline__ QOp load_q(const uint8_t* __restrict__ q, int64_t hrow, int lg) {
     const uint4* p = reinterpret_cast<const uint4*>(q + hrow * 128 + lg * 32);
-    return QOp{p[0], p[1]};
+    return join(p[0], p[1]);
   }
   static __device__ __forceinline__ uint32_t q_scale_byte(const uint8_t* __restrict__ qs, int64_t hrow, int) {
     return (reinterpret_cast<const uint32_t*>(qs)[hrow] >> 23) & 0xFFu;
   }
   template <int OPA>
   static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
-    const v8i av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
-                    (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
-    const v8i bv = {(int)p.lo[t].x, (int)p.lo[t].y, (int)p.lo[t].z, (int)p.lo[t].w,
-                    (int)p.hi[t].x, (int)p.hi[t].y, (int)p.hi[t].z, (int)p.hi[t].w};
     const v4f z = {0.f, 0.f, 0.f, 0.f};
     // cbsz = blgp = 0: both operands FP8 e4m3.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 0, 0, OPA, (int)sa, 0, (int)p.s[t]);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, p.b[t], z, 0, 0, OPA, (int)sa, 0, (int)p.s[t]);
   }
 };
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1: loop indices
+// known at compile time, so the register arrays they index (pages, page ids,
+// rows) stay in registers whatever the unroller decides.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // The logits of one query row for one page, token `lane` of the page in
 // lane `lane`: per 16-token tile NMT MFMAs, then the ReLU / weight epilogue
@@ -146,7 +159,12 @@ template <typename FMT, int NMT, bool ONE_TILE>
 __device__ __forceinline__ float row_page_logits(const typename FMT::QOp (&aq)[NMT],
                                                  const uint32_t (&asc)[(NMT + 3) / 4], const float (&wv)[NMT][4],
                                                  const typename FMT::Page& pg) {
-  auto tile_mfma = [&](int t, v4f(&d)[NMT]) {
+  // the tile index is a compile-time constant (tile<0..3>), so the page's
+  // registers are always indexed statically (a runtime index would put the
+  // page in scratch memory)
+  auto tile = [&](auto tc) __attribute__((always_inline)) {
+    constexpr int t = decltype(tc)::value;
+    v4f d[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       switch (mt & 3) {
@@ -156,8 +174,7 @@ __device__ __forceinline__ float row_page_logits(const typename FMT::QOp (&aq)[N
         default: d[mt] = FMT::template mfma<3>(aq[mt], pg, t, asc[mt >> 2]); break;
       }
     }
-  };
-  auto tile_sum = [&](const v4f(&d)[NMT]) {
+    // two fixed-order chains (even / odd M-tiles), then their sum
     float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -168,18 +185,16 @@ __device__ __forceinline__ float row_page_logits(const typename FMT::QOp (&aq)[N
         else acc0 = __builtin_fmaf(wv[mt][e], rl, acc0);
       }
     }
-    return acc0 + acc1;
-  };
-  float p[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    v4f d[NMT];
-    tile_mfma(t, d);
-    p[t] = tile_sum(d);
+    const float r = acc0 + acc1;
     if constexpr (ONE_TILE) __builtin_amdgcn_sched_barrier(0);
-  }
+    return r;
+  };
+  const float p0 = tile(std::integral_constant<int, 0>{});
+  const float p1 = tile(std::integral_constant<int, 1>{});
+  const float p2 = tile(std::integral_constant<int, 2>{});
+  const float p3 = tile(std::integral_constant<int, 3>{});
   // lane l now gets tile l/16's total for token l%16: 64 consecutive tokens
-  return reduce4(p[0], p[1], p[2], p[3]);
+  return reduce4(p0, p1, p2, p3);
 }
 
 }  // namespace fp4idx

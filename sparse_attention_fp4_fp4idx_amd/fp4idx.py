@@ -30,7 +30,7 @@ FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
-          "fp4idx_mqa_logits_fp8")
+          "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_read")
 EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
@@ -59,6 +59,8 @@ def load():
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
+    lib.fp4idx_peak_mfma_fp4.argtypes = [i32, P, P]
+    lib.fp4idx_peak_read.argtypes = [P, i64, P, P]
     lib.fp4idx_mqa_logits_topk.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, i32, P, i32, i64, P]
     lib.fp4idx_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64, P]
     lib.fp4idx_pack_q_fp8.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
@@ -381,6 +383,24 @@ def fp4idx_read_k(payload: torch.Tensor, scale: torch.Tensor, slot: torch.Tensor
     return out
 
 
+PEAK_MFMA_WAVES = 4096
+
+
+def fp4idx_peak_mfma_fp4(iterations: int, sink: torch.Tensor, stream=None) -> int:
+    """Launch the FP4 MFMA peak microbenchmark; returns the flop it performs."""
+    _run("fp4idx_peak_mfma_fp4", [int(iterations), _ptr(sink, _F32, "sink"), _stream(stream)])
+    return PEAK_MFMA_WAVES * 4 * int(iterations) * 65536
+
+
+def fp4idx_peak_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """Launch the streaming-read microbenchmark over buf (uint8, contiguous); returns the bytes it reads."""
+    if not buf.is_contiguous():
+        raise Fp4idxError("peak_read: buf must be contiguous")
+    n = buf.numel() // 16 * 16
+    _run("fp4idx_peak_read", [_ptr(buf, _U8, "buf"), n, _ptr(sink, (torch.int32,), "sink"), _stream(stream)])
+    return n
+
+
 def _event_handle(ev):
     if ev is None:
         return None
@@ -508,3 +528,5 @@ pack_q_fp8 = fp4idx_pack_q_fp8
 write_k_pack_q_fp8 = fp4idx_write_k_pack_q_fp8
 mqa_logits_fp8 = fp4idx_mqa_logits_fp8
 mqa_logits_topk = fp4idx_mqa_logits_topk
+peak_mfma_fp4 = fp4idx_peak_mfma_fp4
+peak_read = fp4idx_peak_read

@@ -159,6 +159,17 @@ def test_fused_logits_topk_validates_its_host_arguments(F):
     assert call(a3=0, a15=0) == 0 and call(a6=0) == 0   # empty batch: nothing launched
 
 
+def test_peak_microbenchmarks_validate_their_arguments(F):
+    lib = F.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.fp4idx_peak_mfma_fp4(0, fake, None) == -1
+    assert lib.fp4idx_peak_mfma_fp4(8, None, None) == -1
+    assert lib.fp4idx_peak_read(fake, 100, fake, None) == -1          # not a multiple of 16
+    assert lib.fp4idx_peak_read(fake, 0, fake, None) == -1
+    assert lib.fp4idx_peak_read(ctypes.c_void_p(0x1008), 4096, fake, None) == -1
+    assert lib.fp4idx_peak_read(None, 4096, fake, None) == -1
+
+
 def test_binding_imports_no_oracle():
     import sparse_attention_fp4_fp4idx_amd.fp4idx as m
     src = open(m.__file__).read()
