@@ -122,11 +122,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // Branch-free from here, so all loads issue back to back: another id
   // outside the pool (past the request's pages) re-reads the first page and
   // its tile is never stored.
-  typename FMT::Page nxt[D];
+  // two page buffers used in turn (group g is scored from buf[g & 1] while
+  // group g + 1 loads into the other): the unrolled groups index them
+  // statically, so no registers are copied between groups
+  typename FMT::Page buf[2][D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
-    FMT::load_page(nxt[i], payload, scale, pg, lane_pay, lane_sc);
+    FMT::load_page(buf[0][i], payload, scale, pg, lane_pay, lane_sc);
   }
 
   typename FMT::QOp aq[RW][NMT];
@@ -165,34 +168,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   if (nrows == 0 || page_begin >= pages_needed) return;
   const int n_pages = min(PPW, pages_needed - page_begin);
 
-  // groups of D pages: the current group is scored while the next one loads
+  // per row: the (wave-uniform) logits address of token page_begin*64 and
+  // the in-row limit relative to it; a page's 64 logits are then stored at
+  // base + lane + an immediate offset
+  float* rowp[RW];
+  int lim[RW];
 #pragma unroll
-  for (int g0 = 0; g0 < PPW; g0 += D) {
-    if (g0 >= n_pages) break;
-    typename FMT::Page cur[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) cur[i] = nxt[i];
-    if (g0 + D < PPW) {
-#pragma unroll
-      for (int i = 0; i < D; ++i)
-        if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
-          FMT::load_page(nxt[i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
-    }
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      if (g0 + i >= n_pages) break;
-      const int pg = page_begin + g0 + i;
-#pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        if (r < nrows) {
-          const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], cur[i]);
-          const int tok = pg * 64 + lane;
-          const int c = r == 0 ? ctx_r[0] : r == 1 ? ctx_r[1] : r == 2 ? ctx_r[2] : ctx_r[3];
-          if (tok < c) logits[(int64_t)(row0 + r) * logits_stride + tok] = tot;
-        }
-      }
-    }
+  for (int r = 0; r < RW; ++r) {
+    rowp[r] = logits + (int64_t)(row0 + (r < nrows ? r : 0)) * logits_stride + (int64_t)page_begin * 64;
+    lim[r] = r < nrows ? ctx_r[r] - page_begin * 64 : 0;
   }
+  // groups of D pages: the current group is scored while the next one loads
+  static_for<PPW / D>([&](auto gc) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value, g0 = g * D;
+    if (g0 >= n_pages) return;
+    if constexpr (g0 + D < PPW) {
+      static_for<D>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
+          FMT::load_page(buf[(g + 1) & 1][i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
+      });
+    }
+    static_for<D>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if (g0 + i >= n_pages) return;
+      static_for<RW>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        if (r < nrows) {
+          const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], buf[g & 1][i]);
+          if (lane + (g0 + i) * 64 < lim[r]) rowp[r][lane + (g0 + i) * 64] = tot;
+        }
+      });
+    });
+  });
 }
 
 template <typename FMT, int RW, int NMT, int PPW, int D>
