@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kFusedThreads) void mqa_logits_topk_kernel(
         const int32_t id = bt[p];
         // an id outside the pool (a broken contract) reads page 0; its
         // tokens' results are then unspecified but every access in bounds
-        FMT::load_page(pg[d], payload, scale, (id >= 0 && id < num_pages) ? id : 0, lane_pay, lane_sc);
+        FMT::template load_page<true>(pg[d], payload, scale, (id >= 0 && id < num_pages) ? id : 0, lane_pay, lane_sc);
       }
     }
 #pragma unroll

@@ -64,6 +64,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   static_assert(PPW % D == 0, "pages per wave must be a multiple of the prefetch depth");
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;  // packed A-scale registers per row
+  // one row per wave means one row group per request, so every page is read
+  // once (non-temporal); with more rows, other row groups re-read the pages
+  constexpr bool kPageNT = RW == 1;
 
   // grid: x = page chunk, y = row group, z = request.  Work-groups go to the
   // eight XCDs round robin by linear id, so with the chunk count a multiple
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
-    FMT::load_page(buf[0][i], payload, scale, pg, lane_pay, lane_sc);
+    FMT::template load_page<kPageNT>(buf[0][i], payload, scale, pg, lane_pay, lane_sc);
   }
 
   typename FMT::QOp aq[RW][NMT];
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
       static_for<D>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
-          FMT::load_page(buf[(g + 1) & 1][i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
+          FMT::template load_page<kPageNT>(buf[(g + 1) & 1][i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
       });
     }
     static_for<D>([&](auto ic) __attribute__((always_inline)) {

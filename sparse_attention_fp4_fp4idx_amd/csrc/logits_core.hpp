@@ -16,8 +16,15 @@ namespace fp4idx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint4 ld_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// 16-byte page load: non-temporal (NT) where each page is read once, plain
+// where other work-groups re-read it soon and it should stay in L2.
+template <bool NT>
+__device__ __forceinline__ uint4 ld_page16(const void* p) {
+  u32x4 v;
+  if constexpr (NT)
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    v = *reinterpret_cast<const u32x4*>(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -58,6 +65,7 @@ struct Fp4Split {
   typedef uint4 QOp;
   static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(lg * 1024 + li * 16); }
   static __device__ __forceinline__ uint32_t lane_sc(int li, int lg) { return (uint32_t)(lg * 64 + li); }
+  template <bool NT>
   static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ payload,
                                                    const uint8_t* __restrict__ scale, int64_t pid, uint32_t lp,
                                                    uint32_t ls) {
@@ -65,7 +73,7 @@ struct Fp4Split {
     const uint8_t* sp = scale + pid * 256 + ls;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      pr.b[t] = ld_stream16(pp + t * 256);
+      pr.b[t] = ld_page16<NT>(pp + t * 256);
       pr.s[t] = sp[t * 16];
     }
   }
@@ -112,12 +120,13 @@ struct Fp8Fused {
   }
   static __device__ __forceinline__ uint32_t lane_pay(int li, int lg) { return (uint32_t)(li * 128 + lg * 32); }
   static __device__ __forceinline__ uint32_t lane_sc(int li, int) { return (uint32_t)(8192 + li * 4); }
+  template <bool NT>
   static __device__ __forceinline__ void load_page(Page& pr, const uint8_t* __restrict__ pool, const uint8_t*,
                                                    int64_t pid, uint32_t lp, uint32_t ls) {
     const uint8_t* pp = pool + pid * 8448;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      pr.b[t] = join(ld_stream16(pp + lp + t * 2048), ld_stream16(pp + lp + t * 2048 + 16));
+      pr.b[t] = join(ld_page16<NT>(pp + lp + t * 2048), ld_page16<NT>(pp + lp + t * 2048 + 16));
       pr.s[t] = (*reinterpret_cast<const uint32_t*>(pp + ls + t * 64) >> 23) & 0xFFu;
     }
   }
