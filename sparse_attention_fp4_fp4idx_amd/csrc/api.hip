@@ -173,10 +173,10 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
   if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return rc;
   if (!q_fp4 || !q_scale || !w || !req_row_indptr || !row_ctx_len || !block_table || !payload || !scale || !logits)
     return FP4IDX_E_INVALID;
-  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16) || !aligned(scale, 4)) return FP4IDX_E_INVALID;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
-  return launched(fp4idx::launch_mqa_logits(q_fp4, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+  return launched(fp4idx::launch_mqa_logits(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len,
                                             block_table, bt_stride, payload, scale, num_pages, logits, logits_stride,
                                             max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }

@@ -61,8 +61,8 @@ hipError_t launch_write_k_pack_q_fp8(const uint16_t* k, int64_t n_tokens, int64_
                                      const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp8,
                                      float* q_scale, float* w_out, hipStream_t stream);
 
-hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
-                             const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                             int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);

@@ -39,6 +39,8 @@
 // as one 256-byte row segment.
 // Each (row, token) is computed by exactly one lane in a fixed order, so the
 // result does not depend on batch composition, page placement or grid shape.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "logits_core.hpp"
 
@@ -206,6 +208,207 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   });
 }
 
+// Page ids one shared-page work-group stages in LDS (its chunk of pages),
+// and the bytes of one FP4 page in the payload and scale pools.
+constexpr int kSharedMaxChunk = 512;
+constexpr int kPayBytes = 4096, kScBytes = 256;
+// Pages x rows one wave of a shared-page work-group scores at most.
+constexpr int kSharedPageRows = 64;
+
+// Requests with several rows (FP4 cache): a work-group of NW waves takes a
+// block of NW*RW rows of one request and a chunk of that request's pages;
+// each page is read from memory once per work-group and shared by its waves
+// through LDS, and each wave scores its RW rows.  Page i's bytes are loaded
+// into registers two pages ahead, written to LDS slot i&1 just before page
+// i is scored, and one barrier per page publishes the slot (the barrier
+// also proves every wave has finished page i-2, the slot's previous page).
+// Per lane and tile the B operand is a 16-byte LDS read in the pool's own
+// layout; the page's scale bytes are written transposed so one word read
+// gives a lane its four tiles' scales.  Each (row, token) goes through
+// row_page_logits exactly as in mqa_logits_kernel, so the logits are the
+// same bits whichever kernel computes them.
+// One FP4 page in flight in a shared-page work-group of NT threads: thread
+// t holds 16-byte payload pieces t, t + NT, ... (as one native vector, so the
+// pieces stay in registers) and, in the first wave, scale word t.
+template <int NPAY>
+struct SharedPageRegs {
+  typedef uint32_t Vec __attribute__((ext_vector_type(4 * NPAY)));
+  Vec p;
+  uint32_t s;
+};
+
+template <int NT, int NPAY>
+__device__ __forceinline__ void fetch_shared_page(SharedPageRegs<NPAY>& r, const uint8_t* __restrict__ payload,
+                                                  const uint8_t* __restrict__ scale, int64_t pid, int tid) {
+  const uint8_t* pp = payload + pid * kPayBytes;
+  static_for<NPAY>([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    const uint4 v = *reinterpret_cast<const uint4*>(pp + 16 * (tid + NT * m));
+    r.p[4 * m + 0] = v.x;
+    r.p[4 * m + 1] = v.y;
+    r.p[4 * m + 2] = v.z;
+    r.p[4 * m + 3] = v.w;
+  });
+  if (tid < 64) r.s = *reinterpret_cast<const uint32_t*>(scale + pid * kScBytes + 4 * tid);
+}
+
+// registers -> an LDS slot.  Scale word t holds block j = t/16, tokens
+// 4*(t%16) + b; token 16*tile + l's byte goes to [j][l][tile], so a lane's
+// four tiles' scales are one word.
+template <int NT, int NPAY>
+__device__ __forceinline__ void stage_shared_page(const SharedPageRegs<NPAY>& r, uint8_t* slot, int tid) {
+  static_for<NPAY>([&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    *reinterpret_cast<uint4*>(slot + 16 * (tid + NT * m)) =
+        make_uint4(r.p[4 * m + 0], r.p[4 * m + 1], r.p[4 * m + 2], r.p[4 * m + 3]);
+  });
+  if (tid < 64) {
+    uint8_t* d = slot + kPayBytes + (tid >> 4) * 64 + ((tid & 15) >> 2);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) d[(4 * (tid & 3) + b) * 4] = (uint8_t)(r.s >> (8 * b));
+  }
+}
+
+template <int NW, int RW, int NMT>
+__global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
+    const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
+    int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
+    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t chunk_pages) {
+  constexpr int NT = NW * 64;
+  constexpr int H = NMT * 16;
+  constexpr int NSC = (NMT + 3) / 4;
+  constexpr int ROWS = NW * RW;
+  constexpr int NPAY = 256 / NT;  // 16-byte payload pieces per thread and page
+  static_assert(NW == 1 || NW == 2 || NW == 4, "waves per work-group");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2][kPayBytes + kScBytes];
+  __shared__ int32_t pid_s[kSharedMaxChunk];
+  __shared__ int32_t ctx_s[ROWS];
+
+  // chunks rotated per request across the XCDs, as in mqa_logits_kernel
+  const int n_chunks = gridDim.x;
+  const int req = blockIdx.z;
+  int rot = req & 7;
+  if (rot >= n_chunks) rot %= n_chunks;
+  int chunk = (int)blockIdx.x + rot;
+  if (chunk >= n_chunks) chunk -= n_chunks;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+
+  const int ip0 = indptr[req], ip1 = indptr[req + 1];
+  const int row0 = ip0 + (int)blockIdx.y * ROWS;
+  const int nrows = max(0, min(ROWS, ip1 - row0));
+  if (nrows == 0) return;  // the whole work-group
+  // a context length beyond the row or the table (a broken contract) is cut
+  // to what both hold, so no store leaves the row
+  const int ctx_cap = (int)min(min((int64_t)bt_stride * 64, logits_stride), (int64_t)0x7FFFFFFF);
+  if (tid < ROWS) ctx_s[tid] = tid < nrows ? min(max(row_ctx[row0 + tid], 0), ctx_cap) : 0;
+  __syncthreads();
+  int gmax = 0;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) gmax = max(gmax, ctx_s[r]);
+  const int pb = chunk * chunk_pages;
+  const int n = min(chunk_pages, ((gmax + 63) >> 6) - pb);
+  if (n <= 0) return;  // the whole work-group: no row needs these pages
+  // page ids of the chunk; an id outside the pool (a broken table) reads
+  // page 0, so every load stays in the pool
+  const int32_t* bt = block_table + (int64_t)req * bt_stride + pb;
+  for (int k = tid; k < n; k += NT) {
+    const int32_t p = bt[k];
+    pid_s[k] = (p >= 0 && p < num_pages) ? p : 0;
+  }
+
+  // the wave's rows: Q operands, scales and weights stay in registers
+  const int nr = max(0, min(RW, nrows - wave * RW));  // wave-uniform
+  const int wrow0 = row0 + wave * RW;
+  uint4 aq[RW][NMT];
+  uint32_t asc[RW][NSC];
+  float wv[RW][NMT][4];
+  float* rowp[RW];
+  int lim[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r < nr ? wrow0 + r : row0;
+#pragma unroll
+    for (int c = 0; c < NSC; ++c) asc[r][c] = 0;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int64_t hrow = (int64_t)row * H + mt * 16 + li;
+      aq[r][mt] = *reinterpret_cast<const uint4*>(q_fp4 + hrow * 64 + lg * 16);
+      asc[r][mt >> 2] |= (uint32_t)q_scale[hrow * 4 + lg] << (8 * (mt & 3));
+      const float4 w4 = *reinterpret_cast<const float4*>(w + (int64_t)row * H + mt * 16 + lg * 4);
+      wv[r][mt][0] = w4.x;
+      wv[r][mt][1] = w4.y;
+      wv[r][mt][2] = w4.z;
+      wv[r][mt][3] = w4.w;
+    }
+    rowp[r] = logits + (int64_t)row * logits_stride + (int64_t)pb * 64;
+    lim[r] = r < nr ? ctx_s[wave * RW + r] - pb * 64 : 0;
+  }
+  __syncthreads();  // page ids staged
+
+  // page bytes in flight: two register sets, used in turn
+  SharedPageRegs<NPAY> set0, set1;
+  auto score = [&](const uint8_t* slot, int i) __attribute__((always_inline)) {
+    if (nr == 0) return;  // wave-uniform: a wave past the block's rows only loads
+    Fp4Lds::Page pg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pg.b[t] = *reinterpret_cast<const uint4*>(slot + lg * 1024 + (16 * t + li) * 16);
+    pg.s = *reinterpret_cast<const uint32_t*>(slot + kPayBytes + lg * 64 + li * 4);
+    static_for<RW>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
+      if (r < nr) {
+        const float tot = row_page_logits<Fp4Lds, NMT, false>(aq[r], asc[r], wv[r], pg);
+        if (lane + i * 64 < lim[r]) rowp[r][lane + i * 64] = tot;
+      }
+    });
+  };
+  fetch_shared_page<NT>(set0, payload, scale, pid_s[0], tid);
+  if (n > 1) fetch_shared_page<NT>(set1, payload, scale, pid_s[1], tid);
+  for (int i = 0; i < n; i += 2) {
+    stage_shared_page<NT>(set0, ring[0], tid);
+    __syncthreads();
+    if (i + 2 < n) fetch_shared_page<NT>(set0, payload, scale, pid_s[i + 2], tid);
+    score(ring[0], i);
+    if (i + 1 < n) {
+      stage_shared_page<NT>(set1, ring[1], tid);
+      __syncthreads();
+      if (i + 3 < n) fetch_shared_page<NT>(set1, payload, scale, pid_s[i + 3], tid);
+      score(ring[1], i + 1);
+    }
+  }
+}
+
+template <int NW, int RW, int NMT>
+static hipError_t launch_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+                                int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
+                                int32_t bt_stride, const uint8_t* payload, const uint8_t* scale, int64_t num_pages,
+                                float* logits, int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx,
+                                hipStream_t stream) {
+  constexpr int ROWS = NW * RW;
+  const int64_t pages = (max_ctx + 63) / 64;
+  const int64_t blocks = (max_rows_per_req + ROWS - 1) / ROWS;
+  if (pages == 0 || blocks == 0 || n_reqs == 0) return hipSuccess;
+  if (blocks > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
+  // Page chunks: at least about two waves for each of the 1,024 SIMDs, and
+  // no work-group longer than about kSharedPageRows page-rows per wave (a
+  // request's block whose rows are long must not become the critical path:
+  // the hardware balances many short work-groups across the CUs), and not
+  // shorter than 8 pages (a work-group's set-up is paid per chunk).
+  const int64_t want = 2048 / NW;
+  int64_t chunks = (want + n_reqs * blocks - 1) / (n_reqs * blocks);
+  chunks = std::max<int64_t>(chunks, (pages * RW + kSharedPageRows - 1) / kSharedPageRows);
+  chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, (pages + 7) / 8));
+  int64_t chunk_pages = std::min<int64_t>((pages + chunks - 1) / chunks, kSharedMaxChunk);
+  chunks = (pages + chunk_pages - 1) / chunk_pages;
+  if (chunks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  return launch(mqa_logits_shared_kernel<NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)n_reqs),
+                dim3(NW * 64), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q,
+                q_scale, w, logits, logits_stride, (int32_t)chunk_pages);
+}
+
 template <typename FMT, int RW, int NMT, int PPW, int D>
 static hipError_t launch_rw(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                             int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
@@ -274,13 +477,59 @@ static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const f
   }
 }
 
-hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
-                             const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+// FP4 batches of requests with three or more rows each, all about the same
+// count: the shared-page kernel, NW waves of RW rows per work-group (at 128
+// heads two rows per wave keep the Q operands in registers).
+template <int NMT>
+static hipError_t launch_fp4_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
+                                    int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
+                                    int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                                    int64_t num_pages, float* logits, int64_t logits_stride,
+                                    int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+#define FP4IDX_SHARED(NW, RW)                                                                                       \
+  launch_shared<NW, RW, NMT>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,       \
+                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream)
+  const int r = max_rows_per_req;
+  if constexpr (NMT == 8) {
+    return r <= 4 ? FP4IDX_SHARED(2, 2) : FP4IDX_SHARED(4, 2);
+  } else {
+    if (r <= 4) return FP4IDX_SHARED(2, 2);
+    if (r <= 6) return FP4IDX_SHARED(2, 3);
+    if (r <= 8) return FP4IDX_SHARED(2, 4);
+    if (r <= 12) return FP4IDX_SHARED(4, 3);
+    return FP4IDX_SHARED(4, 4);
+  }
+#undef FP4IDX_SHARED
+}
+
+hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                             int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
-  return launch_heads<Fp4Split>(q_fp4, q_scale, w, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  // The shared-page kernel splits a request's rows among a work-group's
+  // waves, so a request with fewer rows than the work-group holds leaves
+  // waves idle; the per-wave kernel splits pages instead.  Shared pages pay
+  // (about 5 % on the prefill and 256 x 6 decode batches) only when the
+  // requests' row counts are near-uniform: on average at least 3/4 of the
+  // largest.  Both kernels give the same bits.
+  const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
+  if (max_rows_per_req <= 2 || !uniform)
+    return launch_heads<Fp4Split>(q_fp4, q_scale, w, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride,
+                                  payload, scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  switch (n_heads) {
+#define FP4IDX_HEADS(H, NMT)                                                                                        \
+  case H:                                                                                                           \
+    return launch_fp4_shared<NMT>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,     \
+                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+    FP4IDX_HEADS(16, 1)
+    FP4IDX_HEADS(32, 2)
+    FP4IDX_HEADS(64, 4)
+    FP4IDX_HEADS(128, 8)
+#undef FP4IDX_HEADS
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int n_heads,

@@ -93,6 +93,30 @@ struct Fp4Split {
   }
 };
 
+// An FP4 page staged in LDS by the shared-page logits kernel: the payload in
+// pool order, the scale bytes of a lane's four tiles in one word (byte t =
+// tile t, picked by the MFMA's B op_sel).  The MFMA operands are those of
+// Fp4Split, so every logit is computed by the same operations.
+struct Fp4Lds {
+  struct Page {
+    uint4 b[4];
+    uint32_t s;
+  };
+  typedef uint4 QOp;
+  template <int OPA>
+  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
+    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const v8i bv = {(int)p.b[t].x, (int)p.b[t].y, (int)p.b[t].z, (int)p.b[t].w, 0, 0, 0, 0};
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    switch (t) {  // t is a compile-time constant at every call
+      case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 0, (int)p.s);
+      case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 1, (int)p.s);
+      case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 2, (int)p.s);
+      default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, 4, 4, OPA, (int)sa, 3, (int)p.s);
+    }
+  }
+};
+
 // FP8 fused pool: page = [64 tokens][128 e4m3 codes] then [64] fp32 scales
 // (powers of two), 8448 bytes.  The fp8 operand holds 32 bytes per lane;
 // A lane l = (head l%16, bytes 32(l/16)..+31 of the head's codes), B lane

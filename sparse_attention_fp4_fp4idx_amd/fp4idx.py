@@ -136,10 +136,22 @@ _U8 = (torch.uint8,)
 _F32 = (torch.float32,)
 
 
+def _pitch(t: torch.Tensor) -> int:
+    """Elements between consecutive rows (dim 0).  With a single row any
+    stride is valid for dim 0 (numpy and torch may report 0 for an inserted
+    axis), so the row's own length is passed instead."""
+    if t.shape[0] == 1:
+        n = 1
+        for d in t.shape[1:]:
+            n *= int(d)
+        return n
+    return int(t.stride(0))
+
+
 def _rowstride(t: torch.Tensor, name: str) -> int:
     if t.dim() < 2 or t.stride(-1) != 1:
         raise Fp4idxError(f"{name} must be 2-D (or more) with unit last stride")
-    return int(t.stride(0))
+    return _pitch(t)
 
 
 def _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale):
@@ -206,7 +218,7 @@ def _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_out, q_scale, w_out, with_tab
                     (cos_sin, "cos_sin")):
         if not t.is_contiguous():
             raise Fp4idxError(f"{what}: {name} must be contiguous")
-    head = [_ptr(q, _BF16, "q"), T, H, int(q.stride(0)) if T else H * HEAD_DIM, _ptr(pos, _I32, "pos")]
+    head = [_ptr(q, _BF16, "q"), T, H, _pitch(q) if T else H * HEAD_DIM, _ptr(pos, _I32, "pos")]
     table = [_ptr(cos_sin, _BF16, "cos_sin"), int(cos_sin.shape[0])] if with_table else []
     tail = [_ptr(w_in, _F32, "w_in"), ctypes.c_float(w_scale), _ptr(q_out, _U8, "q codes"),
             _ptr(q_scale, _F32 if fp8 else _U8, "q_scale"), _ptr(w_out, _F32, "w_out")]
@@ -273,8 +285,8 @@ def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, pa
     num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
     args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
-            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
-            _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"), int(logits.stride(0)),
+            _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
+            _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"), _pitch(logits),
             int(max_rows_per_req), int(max_ctx), _stream(stream)]
     return args, logits
 
@@ -313,7 +325,7 @@ def _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_tabl
     num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
     args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
-            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(payload, _U8, "payload"),
+            _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
             _ptr(scale, _U8, "scale"), num_pages, int(k), _ptr(out_idx, _I32, "out_idx"), int(max_rows_per_req),
             int(max_ctx), _stream(stream)]
     return args, out_idx
@@ -347,7 +359,7 @@ def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
         out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
     if not out_idx.is_contiguous() or not row_ctx.is_contiguous():
         raise Fp4idxError("topk: out_idx and row_ctx must be contiguous")
-    args = [_ptr(logits, _F32, "logits"), T, int(logits.stride(0)), _ptr(row_ctx, _I32, "row_ctx"), int(k),
+    args = [_ptr(logits, _F32, "logits"), T, _pitch(logits), _ptr(row_ctx, _I32, "row_ctx"), int(k),
             _ptr(out_idx, _I32, "out_idx"), int(max_ctx), _stream(stream)]
     return args, out_idx
 
@@ -490,8 +502,8 @@ def _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table
     num_pages = pool.numel() // FP8_PAGE_BYTES
     args = [_ptr(q_fp8, _U8, "q_fp8"), _ptr(q_scale, _F32, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
-            _ptr(block_table, _I32, "block_table"), int(block_table.stride(0)), _ptr(pool, _U8, "pool"), num_pages,
-            _ptr(logits, _F32, "logits"), int(logits.stride(0)), int(max_rows_per_req), int(max_ctx),
+            _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(pool, _U8, "pool"), num_pages,
+            _ptr(logits, _F32, "logits"), _pitch(logits), int(max_rows_per_req), int(max_ctx),
             _stream(stream)]
     return args, logits
 

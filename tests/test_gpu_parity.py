@@ -277,6 +277,90 @@ def test_logits_rows_per_request_variants(F, orc):
             assert np.all(np.isnan(gpu[t, c:]))
 
 
+@pytest.mark.parametrize("rows,heads", [((3, 3), 64), ((4, 4, 3), 64), ((5, 5), 64), ((8, 7), 64), ((10, 9), 64),
+                                        ((12, 12), 64), ((13, 13), 64), ((16, 14), 32), ((4, 4), 128),
+                                        ((7, 7), 128), ((6, 5), 16)])
+def test_logits_shared_page_kernel_every_shape(F, orc, rows, heads):
+    """Batches whose requests all have about the same number (three or more)
+    of rows go to the shared-page kernel; each rows-per-work-group shape it
+    picks, every head count, ragged contexts (a row block whose rows need
+    different pages, a zero-context row)."""
+    ctxs = tuple(64 * 3 + 17 * (i + 1) for i in range(len(rows)))
+    wl = W.small(seed=sum(rows) * heads, rows=rows, ctxs=ctxs, heads=heads)
+    wl.row_ctx[wl.req_row_indptr[0] + 1] = 0
+    wl.row_ctx[wl.req_row_indptr[0]] = 1
+    qf, qs, w, pay, sc = _encoded_small(orc, wl)
+    gpu = _gpu_logits(F, qf, qs, w, wl, pay, sc)
+    ref, f64, T, A = orc.logits(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay, sc,
+                                logits_stride=gpu.shape[1], want_f64=True)
+    for t in range(wl.n_rows):
+        c = wl.row_ctx[t]
+        check_logits(gpu[t, :c], f64[t, :c], T[t, :c], A[t, :c], f"rows {rows} heads {heads} row {t}")
+        assert np.all(np.isnan(gpu[t, c:]))
+
+
+def test_logits_same_bits_from_every_kernel(F, orc):
+    """A 16-row request (shared-page kernel, long enough for several page
+    chunks) gives the same bits as its rows scored one per request (per-wave
+    kernel, one row per wave) and as the same request next to a one-row
+    request (a non-uniform batch: per-wave kernel, four rows per wave)."""
+    rng = np.random.default_rng(17)
+    ctx = 40_000  # 625 pages: many page chunks
+    pages = (ctx + 63) // 64
+    pay, sc = W.random_pool(rng, pages + 3)
+    qf, qs, w = _random_q(rng, 16)
+    table = rng.permutation(pages + 3)[:pages].astype(np.int32)[None, :]
+    row_ctx = (ctx - np.arange(16)[::-1] * 7).astype(np.int32)
+    out_many = torch.full((16, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(np.array([0, 16], np.int32)), dev(row_ctx), dev(table), dev(pay),
+                 dev(sc), 16, ctx, logits=out_many)
+    out_one = torch.full((16, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(np.arange(17, dtype=np.int32)), dev(row_ctx),
+                 dev(np.repeat(table, 16, axis=0)), dev(pay), dev(sc), 1, ctx, logits=out_one)
+    out_mixed = torch.full((17, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    F.mqa_logits(dev(np.concatenate([qf, qf[:1]])), dev(np.concatenate([qs, qs[:1]])), dev(np.concatenate([w, w[:1]])),
+                 dev(np.array([0, 16, 17], np.int32)), dev(np.concatenate([row_ctx, row_ctx[:1]])),
+                 dev(np.repeat(table, 2, axis=0)), dev(pay), dev(sc), 16, ctx, logits=out_mixed)
+    torch.cuda.synchronize()
+    a, b, c = out_many.cpu().numpy(), out_one.cpu().numpy(), out_mixed.cpu().numpy()[:16]
+    assert np.array_equal(np.nan_to_num(a, nan=7.0).view(np.uint32), np.nan_to_num(b, nan=7.0).view(np.uint32))
+    assert np.array_equal(np.nan_to_num(a, nan=7.0).view(np.uint32), np.nan_to_num(c, nan=7.0).view(np.uint32))
+    rows, toks = np.arange(16).repeat(40), (rng.random(640) * row_ctx.repeat(40)).astype(np.int64)
+    f64, T, A = orc.logits_sampled(qf, qs, w, np.array([0, 16], np.int32), table, pay, sc, rows, toks)
+    check_logits(a[rows, toks], f64, T, A, "16-row request")
+
+
+def test_logits_multi_row_broken_inputs_stay_in_bounds(F, orc):
+    """Broken contract on a multi-row request: a context length past the
+    logits row is cut to the row (the next row stays untouched), and a page
+    id outside the pool reads page 0 (its tokens are garbage, no other token
+    changes, nothing outside the buffers is touched)."""
+    wl = W.small(seed=43, rows=(5, 1), ctxs=(300, 60))
+    qf, qs, w, pay, sc = _encoded_small(orc, wl)
+    stride = 320
+    bad_ctx = wl.row_ctx.copy()
+    bad_ctx[2] = 1 << 20
+    table = wl.block_table.copy()
+    table[0, 2] = wl.num_pages + 5  # tokens 128..191 of request 0
+    out = torch.full((wl.n_rows + 1, stride), float("nan"), dtype=torch.float32, device=DEV)
+    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(bad_ctx), dev(table), dev(pay), dev(sc),
+                 wl.max_rows_per_req, wl.max_ctx, logits=out[:wl.n_rows])
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    _, f64, T, A = orc.logits(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay, sc,
+                              logits_stride=stride, want_f64=True)
+    for t in range(wl.n_rows):
+        c = min(int(bad_ctx[t]), stride)
+        good = np.ones(c, bool)
+        if t < 5:
+            good[128:192] = False
+        cc = min(c, int(wl.row_ctx[t]))
+        check_logits(g[t, :cc][good[:cc]], f64[t, :cc][good[:cc]], T[t, :cc][good[:cc]], A[t, :cc][good[:cc]],
+                     f"row {t}")
+        assert not np.any(np.isnan(g[t, :c])) and np.all(np.isnan(g[t, c:]))
+    assert np.all(np.isnan(g[wl.n_rows]))
+
+
 def _random_q(rng, T, H=64):
     qf = rng.integers(0, 256, (T, H, 64)).astype(np.uint8)
     qs = rng.integers(124, 129, (T, H, 4)).astype(np.uint8)
