@@ -45,7 +45,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # fp32 lane-ops/s (256 CUs x 64 lanes x 2.4 GHz), packed fp32 off: 39.3 T
+# fp32 VALU lane-ops/s with packed fp32 off: 256 CUs x 4 SIMDs x 16 lanes per clock x
+# 2.4 GHz = 39.3 T (the published 157.3 TFLOP/s fp32 vector rate counts an FMA as two flop
+# and a packed instruction as two FMAs per lane); fp4idx_peak_valu_fp32 measures it
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20
 
 
@@ -156,22 +159,33 @@ def main():
         F.peak_mfma_fp4(64, sink_f, stream=stream)
         F.peak_read(big, sink_u, stream=stream)
         torch.cuda.synchronize()
+        vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+        for a_, b_ in vev:
+            a_.record(stream)
+            b_.record(stream)
+        F.peak_valu_fp32(64, sink_f, stream=stream)
         flop = [0] * 4
         nbytes = [0] * 4
+        lops = [0] * 4
         for i in range(4):
             F.time_next_call(*pev[i])
             flop[i] = F.peak_mfma_fp4(2048, sink_f, stream=stream)
             F.time_next_call(*pev[4 + i])
             nbytes[i] = F.peak_read(big, sink_u, stream=stream)
+            F.time_next_call(*vev[i])
+            lops[i] = F.peak_valu_fp32(4096, sink_f, stream=stream)
         torch.cuda.synchronize()
         mf = float(np.median([flop[i] / (pev[i][0].elapsed_time(pev[i][1]) * 1e-3) / 1e12 for i in range(4)]))
         rd = float(np.median([nbytes[i] / (pev[4 + i][0].elapsed_time(pev[4 + i][1]) * 1e-3) / 1e9
                               for i in range(4)]))
-        measured = {"mfma_fp4_TFLOPs": round(mf, 1), "hbm_read_GBs": round(rd, 1),
-                    "note": "fp4idx_peak_mfma_fp4 (4,096 waves of dependent-free 16x16x128 FP4 MFMA chains) and "
-                            "fp4idx_peak_read (1 GiB streaming read), dispatch-stamped, median of 4"}
+        va = float(np.median([lops[i] / (vev[i][0].elapsed_time(vev[i][1]) * 1e-3) / 1e12 for i in range(4)]))
+        measured = {"mfma_fp4_TFLOPs": round(mf, 1), "hbm_read_GBs": round(rd, 1), "valu_fp32_Tlane_ops": round(va, 1),
+                    "note": "fp4idx_peak_mfma_fp4 (4,096 waves of dependent-free 16x16x128 FP4 MFMA chains), "
+                            "fp4idx_peak_read (1 GiB streaming read) and fp4idx_peak_valu_fp32 (4,096 waves of "
+                            "16 independent fp32 FMA chains), dispatch-stamped, median of 4"}
         del big
-        log(f"[bench] measured peaks: FP4 MFMA {mf:.0f} TFLOP/s, HBM read {rd:.0f} GB/s ({time.time() - t0:.1f}s)")
+        log(f"[bench] measured peaks: FP4 MFMA {mf:.0f} TFLOP/s, HBM read {rd:.0f} GB/s, "
+            f"fp32 VALU {va:.1f} T lane-ops/s ({time.time() - t0:.1f}s)")
 
     T, H, k = wl.n_rows, wl.heads, wl.topk
     pos_new, slot_new = t(wl.pos_new), t(wl.slot_new)
@@ -332,9 +346,14 @@ def main():
     # HBM bytes; FP4 MFMA flop (2*128*heads per score); fp32 VALU lane-ops
     # (ReLU + FMA per head per score, 2*heads; packed fp32 is off)
     fractions = {"hbm": alg[dom] / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    serial = None
     if dom == "mqa_logits":
         fractions["mfma"] = 2 * 128 * H * scores / (dom_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS
         fractions["alu"] = 2 * H * scores / (dom_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS
+        # on gfx950 a SIMD's matrix and vector work do not overlap (measured), so the
+        # contraction and its ReLU/weight epilogue bound the kernel together: their
+        # times at peak, summed, over the kernel's time
+        serial = fractions["mfma"] + fractions["alu"]
     bound = max(fractions, key=fractions.get)
     peak, unit = {"hbm": (HBM_PEAK_GBS, "GB/s"), "mfma": (MFMA_FP4_PEAK_TFLOPS, "TFLOP/s"),
                   "alu": (VALU_PEAK_TOPS, "T lane-ops/s")}[bound]
@@ -343,12 +362,17 @@ def main():
                 "unit": unit, "frac": round(fractions[bound], 4), "traffic": traffic,
                 "alg_bytes_per_launch": alg[dom], "avg_launch_us": round(dom_ms * 1e3, 2),
                 "fractions": {k: round(v, 4) for k, v in fractions.items()}}
+    if serial is not None:
+        roofline["frac_mfma_plus_alu"] = round(serial, 4)
     if measured:
         # the same achieved figures against the measured peaks
-        mp = {"hbm": measured["hbm_read_GBs"], "mfma": measured["mfma_fp4_TFLOPs"]}
-        roofline["frac_vs_measured_peak"] = {r: round(fractions[r] * {"hbm": HBM_PEAK_GBS,
-                                                                    "mfma": MFMA_FP4_PEAK_TFLOPS}[r] / mp[r], 4)
-                                             for r in mp if r in fractions}
+        mp = {"hbm": measured["hbm_read_GBs"], "mfma": measured["mfma_fp4_TFLOPs"],
+              "alu": measured["valu_fp32_Tlane_ops"]}
+        vendor = {"hbm": HBM_PEAK_GBS, "mfma": MFMA_FP4_PEAK_TFLOPS, "alu": VALU_PEAK_TOPS}
+        fm = {r: fractions[r] * vendor[r] / mp[r] for r in mp if r in fractions}
+        roofline["frac_vs_measured_peak"] = {r: round(v, 4) for r, v in fm.items()}
+        if serial is not None:
+            roofline["frac_vs_measured_peak"]["mfma_plus_alu"] = round(fm["mfma"] + fm["alu"], 4)
         roofline["measured_peaks"] = measured
 
     # ---- split-pool reader: every cached token of the workload back to fp32, one launch (not part of the step)

@@ -317,12 +317,16 @@ int fp4idx_time_next_call(void* start_event, void* stop_event);
  *   e2m1 operands (the logits kernel's instruction), 65,536 flop each:
  *   flop = 4096 * 4 * iterations * 65536.  sink: one device float (never
  *   written in practice).
+ * fp4idx_peak_valu_fp32: 4,096 waves each run 16 * iterations fp32 FMAs per
+ *   lane on 16 independent chains: FMA lane-ops = 4096 * 64 * 16 * iterations
+ *   (two flop each).  sink: one device float (never written in practice).
  * fp4idx_peak_read: reads every byte of buf[0, bytes) once with 16-byte
  *   non-temporal loads; bytes a positive multiple of 16, buf 16-byte
  *   aligned; sink: one device uint32 (never written in practice).  Use a
  *   buffer well above the 256 MB last-level cache.
  */
 int fp4idx_peak_mfma_fp4(int32_t iterations, float* sink, void* stream);
+int fp4idx_peak_valu_fp32(int32_t iterations, float* sink, void* stream);
 int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable name of a status code (static storage). */

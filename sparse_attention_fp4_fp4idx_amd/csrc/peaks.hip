@@ -1,7 +1,8 @@
 // Microbenchmarks of the peaks the roofline fractions are taken against
 // (measurement support, not part of the method): FP4 block-scaled MFMA
-// throughput and streaming HBM read bandwidth on the current device, so that
-// a kernel's fraction can be stated against measured as well as vendor peaks.
+// throughput, fp32 VALU FMA throughput and streaming HBM read bandwidth on the
+// current device, so that a kernel's fraction can be stated against measured
+// as well as vendor peaks.
 #include "launch.hpp"
 
 namespace fp4idx {
@@ -26,6 +27,23 @@ __global__ __launch_bounds__(256) void peak_mfma_fp4_kernel(int iters, float* si
     c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, 4, 4, 0, 127, 0, 127);
   }
   const float s = c0[0] + c1[1] + c2[2] + c3[3];
+  if (s == -1.2345e-37f) sink[0] = s;
+}
+
+// Every lane runs `iters` rounds of 16 independent fp32 FMA chains
+// (acc = acc * a + 0.5 with a uniform `a`: one vector register read per
+// instruction, so no register-bank conflicts), i.e. 16 * iters FMA lane-ops.
+__global__ __launch_bounds__(256) void peak_valu_fp32_kernel(int iters, float a, float* sink) {
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = (float)(threadIdx.x + j);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = __builtin_fmaf(acc[j], a, 0.5f);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += acc[j];
   if (s == -1.2345e-37f) sink[0] = s;
 }
 
@@ -56,6 +74,10 @@ constexpr int kPeakReadBlocks = 2048;
 
 hipError_t launch_peak_mfma_fp4(int32_t iters, float* sink, hipStream_t stream) {
   return launch(peak_mfma_fp4_kernel, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, sink);
+}
+
+hipError_t launch_peak_valu_fp32(int32_t iters, float* sink, hipStream_t stream) {
+  return launch(peak_valu_fp32_kernel, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, 0.999f, sink);
 }
 
 hipError_t launch_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {

@@ -30,7 +30,7 @@ FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
-          "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_read")
+          "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_read")
 EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
@@ -60,6 +60,7 @@ def load():
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
     lib.fp4idx_peak_mfma_fp4.argtypes = [i32, P, P]
+    lib.fp4idx_peak_valu_fp32.argtypes = [i32, P, P]
     lib.fp4idx_peak_read.argtypes = [P, i64, P, P]
     lib.fp4idx_mqa_logits_topk.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, i32, P, i32, i64, P]
     lib.fp4idx_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64, P]
@@ -404,6 +405,12 @@ def fp4idx_peak_mfma_fp4(iterations: int, sink: torch.Tensor, stream=None) -> in
     return PEAK_MFMA_WAVES * 4 * int(iterations) * 65536
 
 
+def fp4idx_peak_valu_fp32(iterations: int, sink: torch.Tensor, stream=None) -> int:
+    """Launch the fp32 VALU FMA peak microbenchmark; returns the FMA lane-ops it performs."""
+    _run("fp4idx_peak_valu_fp32", [int(iterations), _ptr(sink, _F32, "sink"), _stream(stream)])
+    return PEAK_MFMA_WAVES * 64 * 16 * int(iterations)
+
+
 def fp4idx_peak_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
     """Launch the streaming-read microbenchmark over buf (uint8, contiguous); returns the bytes it reads."""
     if not buf.is_contiguous():
@@ -541,4 +548,5 @@ write_k_pack_q_fp8 = fp4idx_write_k_pack_q_fp8
 mqa_logits_fp8 = fp4idx_mqa_logits_fp8
 mqa_logits_topk = fp4idx_mqa_logits_topk
 peak_mfma_fp4 = fp4idx_peak_mfma_fp4
+peak_valu_fp32 = fp4idx_peak_valu_fp32
 peak_read = fp4idx_peak_read
