@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
     int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
     const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride) {
   static_assert(RW >= 1 && RW <= 4, "rows per wave");
-  static_assert(PPW % D == 0, "pages per wave must be a multiple of the prefetch depth");
+  static_assert(PPW % D == 0 && PPW <= 64, "pages per wave: a multiple of the prefetch depth, one id per lane");
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;  // packed A-scale registers per row
   // one row per wave means one row group per request, so every page is read
@@ -114,9 +114,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // for the pages)
   const int32_t my_ctx = row_ctx[min(row0 + (lane & 3), row_hi)];
   __builtin_amdgcn_sched_barrier(0);  // issued before the exit test below
-  int32_t pid[PPW];
+  int32_t pid[D];  // the first D page ids; later ones are read from my_pid when they are loaded
 #pragma unroll
-  for (int i = 0; i < PPW; ++i)
+  for (int i = 0; i < D; ++i)
     pid[i] = (nrows > 0 && page_begin + i < bt_stride) ? __builtin_amdgcn_readlane(my_pid, i) : -1;
   // A wave whose first page id is outside [0, num_pages) has nothing to
   // store: the table only promises valid ids for pages some row needs, and
@@ -127,14 +127,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // Branch-free from here, so all loads issue back to back: another id
   // outside the pool (past the request's pages) re-reads the first page and
   // its tile is never stored.
-  // two page buffers used in turn (group g is scored from buf[g & 1] while
-  // group g + 1 loads into the other): the unrolled groups index them
-  // statically, so no registers are copied between groups
-  typename FMT::Page buf[2][D];
+  // D page buffers; page p is scored from buf[p % D], which then loads page
+  // p + D (a rolling prefetch: D pages in flight, D pages of registers)
+  typename FMT::Page buf[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
-    FMT::template load_page<kPageNT>(buf[0][i], payload, scale, pg, lane_pay, lane_sc);
+    FMT::template load_page<kPageNT>(buf[i], payload, scale, pg, lane_pay, lane_sc);
   }
 
   typename FMT::QOp aq[RW][NMT];
@@ -183,29 +182,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
     rowp[r] = logits + (int64_t)(row0 + (r < nrows ? r : 0)) * logits_stride + (int64_t)page_begin * 64;
     lim[r] = r < nrows ? ctx_r[r] - page_begin * 64 : 0;
   }
-  // groups of D pages: the current group is scored while the next one loads
-  static_for<PPW / D>([&](auto gc) __attribute__((always_inline)) {
-    constexpr int g = decltype(gc)::value, g0 = g * D;
-    if (g0 >= n_pages) return;
-    if constexpr (g0 + D < PPW) {
-      static_for<D>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        if (g0 + D + i < n_pages && pid[g0 + D + i] >= 0 && pid[g0 + D + i] < num_pages)
-          FMT::template load_page<kPageNT>(buf[(g + 1) & 1][i], payload, scale, pid[g0 + D + i], lane_pay, lane_sc);
-      });
-    }
+  // groups of D pages (a runtime loop; within a group the buffer index is a
+  // compile-time constant, so the pages stay in registers)
+  for (int g0 = 0; g0 < n_pages; g0 += D) {
     static_for<D>([&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if (g0 + i >= n_pages) return;
+      const int p = g0 + i;
+      if (p >= n_pages) return;
       static_for<RW>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         if (r < nrows) {
-          const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], buf[g & 1][i]);
-          if (lane + (g0 + i) * 64 < lim[r]) rowp[r][lane + (g0 + i) * 64] = tot;
+          const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], buf[i]);
+          if (lane + p * 64 < lim[r]) rowp[r][lane + p * 64] = tot;
         }
       });
+      const int pn = p + D;  // < PPW <= 64: lane pn of my_pid holds its id
+      if (pn < n_pages) {
+        const int32_t id = __builtin_amdgcn_readlane(my_pid, pn);
+        if (id >= 0 && id < num_pages)
+          FMT::template load_page<kPageNT>(buf[i], payload, scale, id, lane_pay, lane_sc);
+      }
     });
-  });
+  }
 }
 
 // Page ids one shared-page work-group stages in LDS (its chunk of pages),

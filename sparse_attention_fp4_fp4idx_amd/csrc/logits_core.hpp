@@ -57,7 +57,7 @@ struct Fp4Split {
   static constexpr int kRowsCap = 4, kRowsCapWide = 4;
   static constexpr int kWaves1 = 4, kPpw1 = 4, kD1 = 4;  // one row per wave (decode)
   static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;  // two rows
-  static constexpr int kPpwMany = 8, kDMany = 2;         // three or four rows
+  static constexpr int kPpwMany = 8, kDMany = 4;         // three or four rows
   struct Page {  // 4 tiles of 16 tokens
     uint4 b[4];
     uint32_t s[4];
@@ -131,7 +131,7 @@ struct Fp8Fused {
   static constexpr int kRowsCap = 4, kRowsCapWide = 2;   // 3+ rows at 128 heads spill
   static constexpr int kWaves1 = 2, kPpw1 = 4, kD1 = 4;
   static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;
-  static constexpr int kPpwMany = 8, kDMany = 2;
+  static constexpr int kPpwMany = 8, kDMany = 4;
   // operands are held as native 8-register vectors (a two-member struct read
   // as one vector keeps the compiler from splitting it into registers)
   struct Page {
