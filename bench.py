@@ -164,6 +164,14 @@ def main():
             a_.record(stream)
             b_.record(stream)
         F.peak_valu_fp32(64, sink_f, stream=stream)
+        mev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+               for _ in range(3)]
+        for row in mev:
+            for a_, b_ in row:
+                a_.record(stream)
+                b_.record(stream)
+        for m in range(3):
+            F.peak_mfma_valu(m, 16, sink_f, stream=stream)
         flop = [0] * 4
         nbytes = [0] * 4
         lops = [0] * 4
@@ -174,18 +182,29 @@ def main():
             nbytes[i] = F.peak_read(big, sink_u, stream=stream)
             F.time_next_call(*vev[i])
             lops[i] = F.peak_valu_fp32(4096, sink_f, stream=stream)
+            for m in range(3):
+                F.time_next_call(*mev[m][i])
+                F.peak_mfma_valu(m, 1024, sink_f, stream=stream)
         torch.cuda.synchronize()
         mf = float(np.median([flop[i] / (pev[i][0].elapsed_time(pev[i][1]) * 1e-3) / 1e12 for i in range(4)]))
         rd = float(np.median([nbytes[i] / (pev[4 + i][0].elapsed_time(pev[4 + i][1]) * 1e-3) / 1e9
                               for i in range(4)]))
         va = float(np.median([lops[i] / (vev[i][0].elapsed_time(vev[i][1]) * 1e-3) / 1e12 for i in range(4)]))
+        # MFMA alone, fp32 FMAs alone, both interleaved: overlap 1 = the pipes run in
+        # parallel (mix = the longer part), 0 = they take turns (mix = the sum)
+        tm = [float(np.median([mev[m][i][0].elapsed_time(mev[m][i][1]) * 1e3 for i in range(4)])) for m in range(3)]
+        overlap = (tm[0] + tm[1] - tm[2]) / min(tm[0], tm[1])
         measured = {"mfma_fp4_TFLOPs": round(mf, 1), "hbm_read_GBs": round(rd, 1), "valu_fp32_Tlane_ops": round(va, 1),
+                    "mfma_valu_overlap": round(overlap, 3),
+                    "mfma_valu_us": {"mfma": round(tm[0], 1), "valu": round(tm[1], 1), "both": round(tm[2], 1)},
                     "note": "fp4idx_peak_mfma_fp4 (4,096 waves of dependent-free 16x16x128 FP4 MFMA chains), "
-                            "fp4idx_peak_read (1 GiB streaming read) and fp4idx_peak_valu_fp32 (4,096 waves of "
-                            "16 independent fp32 FMA chains), dispatch-stamped, median of 4"}
+                            "fp4idx_peak_read (1 GiB streaming read), fp4idx_peak_valu_fp32 (4,096 waves of "
+                            "16 independent fp32 FMA chains) and fp4idx_peak_mfma_valu (the MFMA and FMA chains "
+                            "alone and interleaved; overlap = (alone + alone - both) / shorter alone, 1 = the "
+                            "pipes overlap, 0 = they take turns), dispatch-stamped, median of 4"}
         del big
         log(f"[bench] measured peaks: FP4 MFMA {mf:.0f} TFLOP/s, HBM read {rd:.0f} GB/s, "
-            f"fp32 VALU {va:.1f} T lane-ops/s ({time.time() - t0:.1f}s)")
+            f"fp32 VALU {va:.1f} T lane-ops/s, MFMA/VALU overlap {overlap:.2f} ({time.time() - t0:.1f}s)")
 
     T, H, k = wl.n_rows, wl.heads, wl.topk
     pos_new, slot_new = t(wl.pos_new), t(wl.slot_new)

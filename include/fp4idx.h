@@ -320,6 +320,13 @@ int fp4idx_time_next_call(void* start_event, void* stop_event);
  * fp4idx_peak_valu_fp32: 4,096 waves each run 16 * iterations fp32 FMAs per
  *   lane on 16 independent chains: FMA lane-ops = 4096 * 64 * 16 * iterations
  *   (two flop each).  sink: one device float (never written in practice).
+ * fp4idx_peak_mfma_valu: whether a SIMD's matrix and vector pipes overlap.
+ *   4,096 waves each run `iterations` rounds of, by mode, 8 FP4 MFMAs (mode
+ *   0), 32 fp32 FMAs (mode 1) or both interleaved one MFMA : four FMAs (mode
+ *   2), every chain carried across rounds.  Compare the three durations:
+ *   mode 2 near the longer of modes 0 and 1 means the pipes overlap, near
+ *   their sum that they take turns.  mode outside 0..2 is FP4IDX_E_INVALID.
+ *   sink: one device float (never written in practice).
  * fp4idx_peak_read: reads every byte of buf[0, bytes) once with 16-byte
  *   non-temporal loads; bytes a positive multiple of 16, buf 16-byte
  *   aligned; sink: one device uint32 (never written in practice).  Use a
@@ -327,6 +334,7 @@ int fp4idx_time_next_call(void* start_event, void* stop_event);
  */
 int fp4idx_peak_mfma_fp4(int32_t iterations, float* sink, void* stream);
 int fp4idx_peak_valu_fp32(int32_t iterations, float* sink, void* stream);
+int fp4idx_peak_mfma_valu(int32_t mode, int32_t iterations, float* sink, void* stream);
 int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable name of a status code (static storage). */

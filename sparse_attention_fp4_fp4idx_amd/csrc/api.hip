@@ -238,6 +238,14 @@ int fp4idx_peak_valu_fp32(int32_t iterations, float* sink, void* stream) {
   return launched(fp4idx::launch_peak_valu_fp32(iterations, sink, static_cast<hipStream_t>(stream)));
 }
 
+int fp4idx_peak_mfma_valu(int32_t mode, int32_t iterations, float* sink, void* stream) {
+  const TimingScope timing_scope;
+  if (mode < 0 || mode > 2 || iterations < 1 || !sink) return FP4IDX_E_INVALID;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_peak_mix(mode, iterations, sink, static_cast<hipStream_t>(stream)));
+}
+
 int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* stream) {
   const TimingScope timing_scope;
   if (bytes <= 0 || (bytes % 16) != 0 || !buf || !sink || !aligned(buf, 16)) return FP4IDX_E_INVALID;

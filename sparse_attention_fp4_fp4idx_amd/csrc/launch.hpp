@@ -84,6 +84,7 @@ hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, 
 
 hipError_t launch_peak_mfma_fp4(int32_t iters, float* sink, hipStream_t stream);
 hipError_t launch_peak_valu_fp32(int32_t iters, float* sink, hipStream_t stream);
+hipError_t launch_peak_mix(int32_t mode, int32_t iters, float* sink, hipStream_t stream);
 hipError_t launch_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 hipError_t launch_read_k(const uint8_t* payload, const uint8_t* scale, int64_t num_pages, const int32_t* slot,

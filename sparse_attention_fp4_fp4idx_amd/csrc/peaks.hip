@@ -47,6 +47,45 @@ __global__ __launch_bounds__(256) void peak_valu_fp32_kernel(int iters, float a,
   if (s == -1.2345e-37f) sink[0] = s;
 }
 
+// MFMA / VALU co-execution: per round a wave issues 8 block-scaled FP4 MFMAs
+// (8 accumulator chains, the peak kernel's form) and/or 32 fp32 FMAs (8
+// chains of the VALU peak kernel's form), MODE 0 the MFMAs only, 1 the FMAs
+// only, 2 both, interleaved one MFMA : four FMAs.  Every chain carries across
+// rounds, so nothing can be hoisted.  If the matrix and vector pipes of a SIMD
+// overlapped, mode 2 would take about the longer of modes 0 and 1; if they
+// take turns, about their sum.
+template <int MODE>
+__global__ __launch_bounds__(256) void peak_mix_kernel(int iters, float a, float* sink) {
+  const int l = threadIdx.x;
+  const v8i_p av = {l, l ^ 0x5A5A, l * 3, l + 7, 0, 0, 0, 0};
+  const v8i_p bv = {l * 5, l ^ 0x3C3C, l + 11, l * 9, 0, 0, 0, 0};
+  v4f_p c[8];
+  float x[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    c[m] = v4f_p{0.f, 0.f, 0.f, 0.f};
+    x[m] = (float)(l + m);
+  }
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if constexpr (MODE != 1) c[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c[m], 4, 4, 0, 127, 0, 127);
+      if constexpr (MODE != 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[(4 * m + u) & 7] = __builtin_fmaf(x[(4 * m + u) & 7], a, 0.5f);
+      }
+      if constexpr (MODE == 2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) s += c[m][m & 3] + x[m];
+  if (s == -1.2345e-37f) sink[0] = s;
+}
+
 // Grid-stride read of `n16` 16-byte units (non-temporal loads, eight in
 // flight per lane), folded into one word per thread that reaches memory only
 // for an impossible value.
@@ -78,6 +117,14 @@ hipError_t launch_peak_mfma_fp4(int32_t iters, float* sink, hipStream_t stream) 
 
 hipError_t launch_peak_valu_fp32(int32_t iters, float* sink, hipStream_t stream) {
   return launch(peak_valu_fp32_kernel, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, 0.999f, sink);
+}
+
+hipError_t launch_peak_mix(int32_t mode, int32_t iters, float* sink, hipStream_t stream) {
+  switch (mode) {
+    case 0: return launch(peak_mix_kernel<0>, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, 0.999f, sink);
+    case 1: return launch(peak_mix_kernel<1>, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, 0.999f, sink);
+    default: return launch(peak_mix_kernel<2>, dim3(kPeakMfmaBlocks), dim3(256), 0, stream, iters, 0.999f, sink);
+  }
 }
 
 hipError_t launch_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {

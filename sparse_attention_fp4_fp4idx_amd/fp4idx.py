@@ -30,7 +30,8 @@ FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
-          "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_read")
+          "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_mfma_valu",
+          "fp4idx_peak_read")
 EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
 
 
@@ -61,6 +62,7 @@ def load():
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
     lib.fp4idx_peak_mfma_fp4.argtypes = [i32, P, P]
     lib.fp4idx_peak_valu_fp32.argtypes = [i32, P, P]
+    lib.fp4idx_peak_mfma_valu.argtypes = [i32, i32, P, P]
     lib.fp4idx_peak_read.argtypes = [P, i64, P, P]
     lib.fp4idx_mqa_logits_topk.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, i32, P, i32, i64, P]
     lib.fp4idx_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64, P]
@@ -411,6 +413,11 @@ def fp4idx_peak_valu_fp32(iterations: int, sink: torch.Tensor, stream=None) -> i
     return PEAK_MFMA_WAVES * 64 * 16 * int(iterations)
 
 
+def fp4idx_peak_mfma_valu(mode: int, iterations: int, sink: torch.Tensor, stream=None) -> None:
+    """Launch the MFMA / VALU co-execution microbenchmark (mode 0: MFMAs, 1: FMAs, 2: both)."""
+    _run("fp4idx_peak_mfma_valu", [int(mode), int(iterations), _ptr(sink, _F32, "sink"), _stream(stream)])
+
+
 def fp4idx_peak_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
     """Launch the streaming-read microbenchmark over buf (uint8, contiguous); returns the bytes it reads."""
     if not buf.is_contiguous():
@@ -549,4 +556,5 @@ mqa_logits_fp8 = fp4idx_mqa_logits_fp8
 mqa_logits_topk = fp4idx_mqa_logits_topk
 peak_mfma_fp4 = fp4idx_peak_mfma_fp4
 peak_valu_fp32 = fp4idx_peak_valu_fp32
+peak_mfma_valu = fp4idx_peak_mfma_valu
 peak_read = fp4idx_peak_read

@@ -166,6 +166,10 @@ def test_peak_microbenchmarks_validate_their_arguments(F):
     assert lib.fp4idx_peak_mfma_fp4(8, None, None) == -1
     assert lib.fp4idx_peak_valu_fp32(0, fake, None) == -1
     assert lib.fp4idx_peak_valu_fp32(8, None, None) == -1
+    assert lib.fp4idx_peak_mfma_valu(3, 8, fake, None) == -1
+    assert lib.fp4idx_peak_mfma_valu(-1, 8, fake, None) == -1
+    assert lib.fp4idx_peak_mfma_valu(2, 0, fake, None) == -1
+    assert lib.fp4idx_peak_mfma_valu(0, 8, None, None) == -1
     assert lib.fp4idx_peak_read(fake, 100, fake, None) == -1          # not a multiple of 16
     assert lib.fp4idx_peak_read(fake, 0, fake, None) == -1
     assert lib.fp4idx_peak_read(ctypes.c_void_p(0x1008), 4096, fake, None) == -1
