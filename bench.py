@@ -329,13 +329,14 @@ def main():
             step(sets[i % copies], stream, evs[i])
         torch.cuda.synchronize()
         used = names[:3] if fused else names
-        per_kernel = {n: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]))
-                      for j, n in enumerate(used)}
+        times = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)] for j, n in enumerate(used)}
         if fused:
-            per_kernel = {"write_k": per_kernel["write_k"], "pack_q": per_kernel["pack_q"],
-                          "mqa_logits_topk": per_kernel["mqa_logits"]}
+            times = {"write_k": times["write_k"], "pack_q": times["pack_q"], "mqa_logits_topk": times["mqa_logits"]}
+        per_kernel = {n: float(np.mean(v)) for n, v in times.items()}
+        # median and minimum over the K steps as well (the mean feeds the roofline)
+        per_kernel_stats = {n: (float(np.median(v)), float(np.min(v))) for n, v in times.items()}
         del sets, runners
-        return elapsed * 1e3 / args.steps, per_kernel, copies
+        return elapsed * 1e3 / args.steps, per_kernel, copies, per_kernel_stats
 
     if args.calib_copy:
         # reference for rocprofv3 FETCH_SIZE / WRITE_SIZE: reads and writes exactly MB MiB
@@ -346,7 +347,7 @@ def main():
         torch.cuda.synchronize()
         del csrc, cdst
 
-    ms_per_step, per_kernel_ms, copies = run_cache(False, dict(payload=payload, scale=scale))
+    ms_per_step, per_kernel_ms, copies, per_kernel_stats = run_cache(False, dict(payload=payload, scale=scale))
     scores = wl.scores
     value = scores / (ms_per_step * 1e-3)
 
@@ -426,7 +427,7 @@ def main():
                               t(wl.cached_slots[a:a + (1 << 20)]), norm_w, wl.eps, tab, pool8)
             del kc
         torch.cuda.synchronize()
-        ms8, pk8, copies8 = run_cache(True, dict(pool=pool8))
+        ms8, pk8, copies8, _ = run_cache(True, dict(pool=pool8))
         del pool8
         l8 = 132 * uniq_tokens + 4 * scores + 8704 * T + 4 * ((uniq_tokens + 63) // 64)
         a8 = l8 / (pk8["mqa_logits"] * 1e-3) / 1e9
@@ -443,7 +444,7 @@ def main():
 
     # ---- the fused logits + top-k call on the same workload (FP4 cache, no logits in memory)
     if not args.no_fused and wl.heads <= 64 and wl.max_ctx <= F.FUSED_MAX_CTX:
-        msf, pkf, copiesf = run_cache(False, dict(payload=payload, scale=scale), fused=True)
+        msf, pkf, copiesf, _ = run_cache(False, dict(payload=payload, scale=scale), fused=True)
         extras["fused_logits_topk"] = {
             "ms_per_step": round(msf, 4), "scores_per_s": round(scores / (msf * 1e-3), 1),
             "kernels_us": {n: round(v * 1e3, 2) for n, v in pkf.items()},
@@ -498,11 +499,27 @@ def main():
             reps += 1
         secs /= reps
         cpu_s = secs[0] * (n_rows_s / T) + secs[1:].sum()
+        # the same sampled step once more on one host thread
+        threads = orc.get_threads()
+        orc.set_threads(1)
+        c0 = time.perf_counter()
+        orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tabn, pay_np, sc_np)
+        c1 = time.perf_counter()
+        qf, qs, wo = orc.pack_q(wl.q[rows], wl.pos_q[rows], tabn, wl.w[rows], wl.w_scale)
+        lg1 = orc.logits(qf, qs, wo, ind, wl.row_ctx[rows], wl.block_table[:nb], pay_np, sc_np,
+                         logits_stride=wl.max_ctx)
+        orc.topk(np.nan_to_num(lg1), wl.row_ctx[rows], k)
+        c2 = time.perf_counter()
+        orc.set_threads(threads)
+        cpu1_s = (c1 - c0) * (n_rows_s / T) + (c2 - c1)
+        del lg1
         cpu = {"value": round(s_scores / cpu_s, 1), "unit": "scores/s", "cores": orc.get_threads(), "kind": "oracle",
                "sample": f"{n_rows_s} of {T} rows ({s_scores} scores): the step's K write (pro rata), pack_q, "
                          f"logits and top-k on the oracle, run {reps} times ({reps * cpu_s:.1f}s of CPU wall time); "
                          f"value = scores / mean time per run",
-               "seconds_per_run": {n: round(float(v), 4) for n, v in zip(names, secs)}}
+               "seconds_per_run": {n: round(float(v), 4) for n, v in zip(names, secs)},
+               "single_thread": {"value": round(s_scores / cpu1_s, 1), "cores": 1,
+                                 "sample": "the same sampled step, run once on one host thread"}}
         del pay_np, sc_np, lg
 
     out = {
@@ -524,6 +541,7 @@ def main():
                    "pool_pages": wl.num_pages, "input_copies": copies},
         "k_write_tokens_per_s": round(wl.k_new.shape[0] / (per_kernel_ms["write_k"] * 1e-3), 1),
         "kernels_us": {n: round(v * 1e3, 2) for n, v in per_kernel_ms.items()},
+        "kernels_us_median_min": {n: [round(a * 1e3, 2), round(b * 1e3, 2)] for n, (a, b) in per_kernel_stats.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
