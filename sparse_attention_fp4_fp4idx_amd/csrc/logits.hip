@@ -21,6 +21,9 @@
 //   2 KB contiguous, and a scale word), straight into the B operand.  D
 //   pages are in flight per wave; the page ids and Q are requested before
 //   the context lengths arrive so the prologue costs one memory latency less.
+//   FP4 batches whose requests all have about the same number (three or
+//   more) of rows use mqa_logits_shared_kernel instead: its waves split a
+//   block of rows and share each page through LDS (see that kernel).
 //
 // MFMA mapping for FP4 (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands
 // e2m1; FP8 in Fp8Fused below):
