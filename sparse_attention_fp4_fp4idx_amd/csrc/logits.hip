@@ -321,9 +321,12 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
     pid_s[k] = (p >= 0 && p < num_pages) ? p : 0;
   }
 
-  // the wave's rows: Q operands, scales and weights stay in registers
-  const int nr = max(0, min(RW, nrows - wave * RW));  // wave-uniform
-  const int wrow0 = row0 + wave * RW;
+  // the wave's rows, the block's rows spread evenly over the waves (a block
+  // short of ROWS rows leaves no wave with more than ceil(nrows / NW)): Q
+  // operands, scales and weights stay in registers
+  const int per = (nrows + NW - 1) / NW;  // <= RW
+  const int nr = max(0, min(per, nrows - wave * per));  // wave-uniform
+  const int wrow0 = row0 + wave * per;
   uint4 aq[RW][NMT];
   uint32_t asc[RW][NSC];
   float wv[RW][NMT][4];
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
       wv[r][mt][3] = w4.w;
     }
     rowp[r] = logits + (int64_t)row * logits_stride + (int64_t)pb * 64;
-    lim[r] = r < nr ? ctx_s[wave * RW + r] - pb * 64 : 0;
+    lim[r] = r < nr ? ctx_s[wave * per + r] - pb * 64 : 0;
   }
   __syncthreads();  // page ids staged
 
@@ -387,20 +390,20 @@ static hipError_t launch_shared(const uint8_t* q, const uint8_t* q_scale, const 
                                 int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
                                 int32_t bt_stride, const uint8_t* payload, const uint8_t* scale, int64_t num_pages,
                                 float* logits, int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx,
-                                hipStream_t stream) {
+                                int page_rows, hipStream_t stream) {
   constexpr int ROWS = NW * RW;
   const int64_t pages = (max_ctx + 63) / 64;
   const int64_t blocks = (max_rows_per_req + ROWS - 1) / ROWS;
   if (pages == 0 || blocks == 0 || n_reqs == 0) return hipSuccess;
   if (blocks > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
   // Page chunks: at least about two waves for each of the 1,024 SIMDs, and
-  // no work-group longer than about kSharedPageRows page-rows per wave (a
+  // no work-group longer than about page_rows page-rows per wave (a
   // request's block whose rows are long must not become the critical path:
   // the hardware balances many short work-groups across the CUs), and not
   // shorter than 8 pages (a work-group's set-up is paid per chunk).
   const int64_t want = 2048 / NW;
   int64_t chunks = (want + n_reqs * blocks - 1) / (n_reqs * blocks);
-  chunks = std::max<int64_t>(chunks, (pages * RW + kSharedPageRows - 1) / kSharedPageRows);
+  chunks = std::max<int64_t>(chunks, (pages * RW + page_rows - 1) / page_rows);
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, (pages + 7) / 8));
   int64_t chunk_pages = std::min<int64_t>((pages + chunks - 1) / chunks, kSharedMaxChunk);
   chunks = (pages + chunk_pages - 1) / chunk_pages;
@@ -478,19 +481,29 @@ static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const f
   }
 }
 
-// FP4 batches of requests with three or more rows each, all about the same
-// count: the shared-page kernel, NW waves of RW rows per work-group (at 128
-// heads two rows per wave keep the Q operands in registers).
+// FP4 batches of requests with three or more rows each on average: the
+// shared-page kernel, NW waves of RW rows per work-group (at 128 heads two
+// rows per wave keep the Q operands in registers).  The work-group's row count
+// follows `rows`, the largest request's rows when the counts are near-uniform
+// and the average otherwise (a larger work-group than the typical request
+// leaves its waves idle).  A non-uniform batch also takes shorter page chunks:
+// its work-groups' lengths vary with their requests' rows and contexts, and
+// the last ones to finish set the kernel's time (measured on 48 requests of
+// 1-16 rows over 8k-32k tokens: 81 us against 111 us with the near-uniform
+// shape and chunks; on the near-uniform batches the shorter chunks change
+// nothing).
 template <int NMT>
 static hipError_t launch_fp4_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                                     int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
                                     int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
                                     int64_t num_pages, float* logits, int64_t logits_stride,
-                                    int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+                                    int32_t max_rows_per_req, int64_t max_ctx, int64_t rows, bool uniform,
+                                    hipStream_t stream) {
+  const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 2;
 #define FP4IDX_SHARED(NW, RW)                                                                                       \
   launch_shared<NW, RW, NMT>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,       \
-                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream)
-  const int r = max_rows_per_req;
+                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, page_rows, stream)
+  const int64_t r = rows;
   if constexpr (NMT == 8) {
     return r <= 4 ? FP4IDX_SHARED(2, 2) : FP4IDX_SHARED(4, 2);
   } else {
@@ -509,20 +522,23 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
   // The shared-page kernel splits a request's rows among a work-group's
-  // waves, so a request with fewer rows than the work-group holds leaves
-  // waves idle; the per-wave kernel splits pages instead.  Shared pages pay
-  // (about 5 % on the prefill and 256 x 6 decode batches) only when the
-  // requests' row counts are near-uniform: on average at least 3/4 of the
+  // waves and stages each page once for all of them; the per-wave kernel
+  // splits pages instead and reads each page once per wave.  Shared pages
+  // pay from three rows per request on average (about 5 % on the prefill and
+  // 256 x 6 decode batches, 20 % on a batch of 1-16 rows per request).
+  // Near-uniform: the requests' average row count is at least 3/4 of the
   // largest.  Both kernels give the same bits.
   const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
-  if (max_rows_per_req <= 2 || !uniform)
+  const int64_t avg_rows = n_reqs > 0 ? (n_rows + n_reqs - 1) / n_reqs : 0;
+  if (max_rows_per_req <= 2 || avg_rows < 3)
     return launch_heads<Fp4Split>(q_fp4, q_scale, w, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride,
                                   payload, scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
   switch (n_heads) {
 #define FP4IDX_HEADS(H, NMT)                                                                                        \
   case H:                                                                                                           \
     return launch_fp4_shared<NMT>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,     \
-                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx,              \
+                                  uniform ? (int64_t)max_rows_per_req : avg_rows, uniform, stream);
     FP4IDX_HEADS(16, 1)
     FP4IDX_HEADS(32, 2)
     FP4IDX_HEADS(64, 4)

@@ -302,8 +302,10 @@ def test_logits_shared_page_kernel_every_shape(F, orc, rows, heads):
 def test_logits_same_bits_from_every_kernel(F, orc):
     """A 16-row request (shared-page kernel, long enough for several page
     chunks) gives the same bits as its rows scored one per request (per-wave
-    kernel, one row per wave) and as the same request next to a one-row
-    request (a non-uniform batch: per-wave kernel, four rows per wave)."""
+    kernel, one row per wave), as the same request next to a one-row request
+    (a non-uniform batch: shared-page kernel, shorter chunks) and as the same
+    request next to fifteen one-row requests (under three rows per request
+    on average: per-wave kernel, four rows per wave)."""
     rng = np.random.default_rng(17)
     ctx = 40_000  # 625 pages: many page chunks
     pages = (ctx + 63) // 64
@@ -321,10 +323,19 @@ def test_logits_same_bits_from_every_kernel(F, orc):
     F.mqa_logits(dev(np.concatenate([qf, qf[:1]])), dev(np.concatenate([qs, qs[:1]])), dev(np.concatenate([w, w[:1]])),
                  dev(np.array([0, 16, 17], np.int32)), dev(np.concatenate([row_ctx, row_ctx[:1]])),
                  dev(np.repeat(table, 2, axis=0)), dev(pay), dev(sc), 16, ctx, logits=out_mixed)
+    out_sparse = torch.full((31, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    pick = np.concatenate([np.arange(16), np.arange(15)])
+    F.mqa_logits(dev(qf[pick]), dev(qs[pick]), dev(w[pick]),
+                 dev(np.concatenate([[0], np.arange(16, 32)]).astype(np.int32)), dev(row_ctx[pick]),
+                 dev(np.repeat(table, 16, axis=0)), dev(pay), dev(sc), 16, ctx, logits=out_sparse)
     torch.cuda.synchronize()
     a, b, c = out_many.cpu().numpy(), out_one.cpu().numpy(), out_mixed.cpu().numpy()[:16]
-    assert np.array_equal(np.nan_to_num(a, nan=7.0).view(np.uint32), np.nan_to_num(b, nan=7.0).view(np.uint32))
-    assert np.array_equal(np.nan_to_num(a, nan=7.0).view(np.uint32), np.nan_to_num(c, nan=7.0).view(np.uint32))
+    d = out_sparse.cpu().numpy()
+    bits = lambda x: np.nan_to_num(x, nan=7.0).view(np.uint32)
+    assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(bits(a), bits(c))
+    assert np.array_equal(bits(a), bits(d[:16]))
+    assert np.array_equal(bits(a[:15]), bits(d[16:]))
     rows, toks = np.arange(16).repeat(40), (rng.random(640) * row_ctx.repeat(40)).astype(np.int64)
     f64, T, A = orc.logits_sampled(qf, qs, w, np.array([0, 16], np.int32), table, pay, sc, rows, toks)
     check_logits(a[rows, toks], f64, T, A, "16-row request")
