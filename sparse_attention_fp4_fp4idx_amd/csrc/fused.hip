@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kFusedThreads) void mqa_logits_topk_kernel(
   float v[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) v[j] = stage[min(tid + NT * j, ctx - 1)];
-  topk_select<NT, J>(v, ctx, K, k, o, sh);
+  topk_select<NT, J>(v, ctx, K, k, o, sh, [&](int p) { return stage[p]; });
 }
 
 template <int NMT, int J>

@@ -6,19 +6,21 @@
 // K = min(k, ctx) positions with the largest values, ties resolved toward the
 // lower position, written in ascending position order and padded with -1.
 //
-// Rows up to 32768 positions (topk_reg_kernel), one 1024-thread work-group
-// per row, everything in registers and a few KiB of LDS:
-//  1. Coalesced load of the row; slot j of thread t is position t + 1024 j
-//     (16 or 32 slots), mapped to an order-preserving 32-bit key (-0 folded
-//     onto +0; slots past the row end hold key 0, which no finite value has).
-//  2. Threshold search for the K-th largest key T: one histogram of 2048 bins
-//     linear in value between the row's min and max, then the chosen bin's
-//     keys (typically a handful) are ranked directly; exact key-space rounds
-//     (bins of the key offset) cover bins with more than 256 keys.
-//  3. Ordered compaction: wave ballots write bit masks of the positions with
-//     key > T and key == T; thread t owns the 32 positions of mask word t, one
-//     block scan of the two popcounts gives its output offset, and ties are
-//     taken in position order until K.
+// Rows up to 32768 positions (topk_reg_kernel), one work-group per row,
+// everything in registers and a few KiB of LDS:
+//  1. Coalesced load of the row; slot j of thread t is position t + NT j
+//     (J slots), the row's minimum and maximum.
+//  2. Threshold search: one histogram of 2048 bins linear in value between the
+//     row's minimum and maximum (the slots keep their bins); one wave finds the
+//     bin holding the K-th largest value.  When that bin holds at most 256
+//     values (the common case), one pass writes bit masks of the positions in
+//     higher bins and gathers the bin's positions, and each of those
+//     candidates is kept when fewer than K - (values above) candidates come
+//     before it in (value descending, position ascending) order; its bit joins
+//     the masks.  Otherwise exact key-space rounds find the K-th largest value
+//     T and the masks hold value > T and the first ties of value == T.
+//  3. Ordered compaction: thread t owns the 32 positions of mask word t, one
+//     block scan of the popcounts gives its output offset.
 // Longer rows (topk_long_kernel) re-read the logits in each pass, with four
 // waves per row and ballot-based compaction.
 #include "launch.hpp"
@@ -257,7 +259,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     const uint32_t off = min(off0 + 4u * (uint32_t)(j * NT), off_last);
     v[j] = __builtin_nontemporal_load(reinterpret_cast<const float*>(srcb + off));
   });
-  topk_select<NT, J>(v, ctx, K, k, o, sh);
+  topk_select<NT, J>(v, ctx, K, k, o, sh, [&](int p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const float*>(srcb + 4u * (uint32_t)p));
+  });
 }
 
 template <int NT, int J>

@@ -9,6 +9,13 @@
 namespace fp4idx {
 
 constexpr int kBins = 2048;
+// First-cut bins in LDS: bin b (b >= -64; b < 0 are the lanes' spare
+// counters) at word bin_word(b) = b + floor(b / 32) past kHistBase: one pad
+// word per 32 bins, so the 32 bins a lane sums start 33 words after the
+// previous lane's and a wave's reads fall in different banks.
+constexpr int kHistBase = 66;
+constexpr int kHistWords = kHistBase + kBins + kBins / 32;
+__device__ __forceinline__ int bin_word(int b) { return b + (b >> 5); }
 
 __device__ __forceinline__ uint32_t order_key(float v) {
   uint32_t u = __float_as_uint(v);
@@ -138,38 +145,92 @@ __device__ __forceinline__ void rank_candidates(const float* cand, int m, int ne
 
 // Rows of up to NT*J positions, one work-group of NT threads per row: slot j
 // of thread t is position t + NT j.  Every pass runs over all J slots with no
-// branches (so the loads issue back to back and independent slots overlap);
-// the launch picks J for the longest row.  Slots past the row end load a copy
-// of the row's last value (clamped offset), which cannot move the row's
-// minimum or maximum, and are then set to -inf, which no (finite) logit
-// equals.  Values stay fp32: IEEE comparisons already treat -0 and +0 as one
-// value.
+// per-slot branches on the common path (so the loads issue back to back and
+// independent slots overlap); the launch picks J for the longest row.  Slots
+// past the row end load a copy of the row's last value (clamped offset), which
+// cannot move the row's minimum or maximum, and are then set to -inf, which no
+// (finite) logit equals.  Values stay fp32: IEEE comparisons already treat -0
+// and +0 as one value.
 // LDS of one row's selection (NT threads, J slots per thread).
 template <int NT, int J>
 struct TopkRegShared {
   static constexpr int NW = NT / 64;       // waves
   static constexpr int NWD = NT * J / 32;  // 32-position mask words of a row
-  uint32_t hist[kBins + 64];               // + 64 spare counters (one per lane)
+  uint32_t hist[kHistWords];               // first-cut bins, padded (bin_word), and 64 spare counters
   uint32_t gtmask[NWD], eqmask[NWD];       // one bit per position
   float cand[kCandMax];
+  int32_t cand_pos[kCandMax];
   uint32_t part[NW];
   uint32_t wmin[NW], wmax[NW];
   int32_t s_bin, s_cnt, s_ncand, s_gt;
   float s_T;
 };
 
-// The selection for one row of ctx positions (K = min(k, ctx) < ctx): slot j
-// of thread t holds position t + NT j; slots at or past ctx hold a copy of a
-// value of the row (they are set to -inf here, after the range).  Writes the
-// row's k outputs to o.
-template <int NT, int J>
-__device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k, int32_t* __restrict__ o,
-                                            TopkRegShared<NT, J>& sh) {
-  static_assert(NT >= kCandMax && NT <= 1024 && kBins % NT == 0, "threads per row");
+// Ordered compaction of a row's bit masks (word wd holds positions 32 wd ..
+// 32 wd + 31): the positions set in gtmask, then (EQ) the first need_eq set
+// in eqmask, in position order; written ascending to o[0, K), -1 after.
+// Thread t owns the 32*WPT consecutive positions of words WPT t ..: one scan
+// of both counts (packed in 16-bit halves; a row has at most 32768
+// positions), then ties are taken in position order.  Words from nwd on are
+// zero.
+template <int NT, int J, bool EQ>
+__device__ __forceinline__ void compact_masks(TopkRegShared<NT, J>& sh, int nwd, int need_eq, int K, int k,
+                                              int32_t* __restrict__ o) {
+  constexpr int NW = NT / 64;
+  constexpr int NWD = NT * J / 32;
+  constexpr int WPT = (NWD + NT - 1) / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t gw[WPT], ew[WPT];
+  uint32_t packed = 0;
+#pragma unroll
+  for (int u = 0; u < WPT; ++u) {
+    const int wd = WPT * tid + u;
+    gw[u] = wd < nwd ? sh.gtmask[wd] : 0u;
+    ew[u] = EQ && wd < nwd ? sh.eqmask[wd] : 0u;
+    packed += (uint32_t)__popc(gw[u]) | ((uint32_t)__popc(ew[u]) << 16);
+  }
+  const uint32_t before = block_excl_scan<NW>(packed, lane, wave, sh.part);
+  const int gt_before = (int)(before & 0xFFFFu);
+  int eq_seen = (int)(before >> 16);
+  int out = gt_before + min(eq_seen, need_eq);
+#pragma unroll
+  for (int u = 0; u < WPT; ++u) {
+    uint32_t sel = gw[u];
+    if constexpr (EQ) {
+      int take = min(max(need_eq - eq_seen, 0), __popc(ew[u]));
+      eq_seen += __popc(ew[u]);
+      uint32_t e = ew[u];
+      for (; take > 0; --take) {
+        sel |= e & (~e + 1u);  // lowest remaining tie
+        e &= e - 1u;
+      }
+    }
+    while (sel) {
+      const int b = __ffs(sel) - 1;
+      if (out < K) o[out] = 32 * (WPT * tid + u) + b;
+      ++out;
+      sel &= sel - 1u;
+    }
+  }
+  for (int i = K + tid; i < k; i += NT) o[i] = -1;
+}
+
+// The rare paths of topk_select.  They keep no copy of the row: every use of
+// slot j's value is a fresh reload(j) (the value of slot j, -inf past the row
+// end), and their slot loops go eight slots at a time, so they need few
+// registers and the common path holds nothing for them.  crowded: the first
+// cut's bin c_bin (bins of (v - c_vmin) * c_vscale) holds more than kCandMax
+// values; otherwise [lo, hi] is the key interval left to search.  cnt_above
+// values lie above the interval.
+template <int NT, int J, typename Reload>
+__device__ __forceinline__ void topk_select_exact(Reload reload, int ctx, int K, int k, int32_t* __restrict__ o,
+                                                  TopkRegShared<NT, J>* shp, bool crowded, int c_bin,
+                                                  float c_vmin, float c_vscale, uint32_t lo, uint32_t hi,
+                                                  int cnt_above) {
   constexpr int NW = NT / 64;               // waves
   constexpr int NWD = NT * J / 32;          // 32-position mask words of a row
-  constexpr int WPT = (NWD + NT - 1) / NT;  // mask words owned by a thread
-  uint32_t* hist = sh.hist;
+  TopkRegShared<NT, J>& sh = *shp;
+  uint32_t* bins = sh.hist + kHistBase;  // the rounds' bins: plain, [0, nb)
   uint32_t* gtmask = sh.gtmask;
   uint32_t* eqmask = sh.eqmask;
   float* cand = sh.cand;
@@ -183,147 +244,65 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
   float& s_T = sh.s_T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nj = (ctx + NT - 1) / NT;  // 1 <= nj <= J
+  // eight slots at a time: their loads are in flight together
   auto slots = [&](auto&& f) {
-#pragma unroll
+#pragma unroll 8
     for (int j = 0; j < J; ++j) f(j);
   };
-
-  for (int b = tid; b < kBins; b += NT) hist[b] = 0;
-  if (tid == 0) s_ncand = 0;
-  float mn = v[0], mx = v[0];
-  slots([&](int j) {
-    if (j > 0) {
-      mn = fminf(mn, v[j]);
-      mx = fmaxf(mx, v[j]);
-    }
-  });
-  {
-    const uint32_t kmn = wave_min_u32(order_key(mn)), kmx = wave_max_u32(order_key(mx));
-    if (lane == 0) {
-      wmin[wave] = kmn;
-      wmax[wave] = kmx;
-    }
-  }
-  slots([&](int j) {
-    if (tid + j * NT >= ctx) v[j] = -__builtin_inff();
-  });
-  __syncthreads();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;  // order keys of the row's min and max
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    lo = min(lo, wmin[w]);
-    hi = max(hi, wmax[w]);
-  }
-  int cnt_above = 0;  // values above the current search interval
   bool found = false;
   float T = key_value(lo);
-
-  // 2. threshold search: the K-th largest value T.
-  // 2a. First cut, linear in value: bin(v) = min(2047, (v - vmin) * 2048 /
-  //     (vmax - vmin)) is monotone in v, so the bin holding the K-th largest
-  //     value holds a contiguous value interval, and ties share a bin.  (Bins
-  //     linear in the bit pattern would be logarithmic in value and pile a
-  //     row onto a few bins.)  Skipped when the value range is not a finite
-  //     positive float.
-  if (lo < hi) {
-    const float vmin = key_value(lo), vmax = key_value(hi);
-    const float vrange = vmax - vmin;
-    const float vscale = (float)kBins / vrange;
-    if (vrange > 0.0f && vrange <= 3.4028234664e38f && vscale <= 3.4028234664e38f) {
-      // bin of a value: one correctly rounded fma is monotone in x, and the
-      // clamp before the conversion keeps it defined for -inf (bin 0)
-      const float voff = -vmin * vscale;
-      auto bin_of = [&](float x) {
-        return (int)__builtin_amdgcn_fmed3f(__builtin_fmaf(x, vscale, voff), 0.0f, (float)(kBins - 1));
-      };
-      // slots past the row end count into a per-lane spare counter that is
-      // never read: no branch, and no pile-up of atomics on one bin
-      slots([&](int j) { atomicAdd(&hist[v[j] >= vmin ? bin_of(v[j]) : kBins + lane], 1u); });
-      __syncthreads();
-      const int bsel = select_bin<NT>(hist, kBins, K, cnt_above, tid, lane, wave, part, s_bin, s_cnt);
-      const int m = (int)hist[bsel];
-      cnt_above = s_cnt;
-      // The bins (and the row-end tests) are recomputed below rather than
-      // kept from the histogram pass (J more registers); the opaque copies
-      // stop the compiler from keeping them.  Same operands, same bins.
-      float vscale2 = vscale, vmin2 = vmin;
-      asm volatile("" : "+v"(vscale2), "+v"(vmin2));
-      auto in_bin = [&](int j) {
-        const int bj = (int)__builtin_amdgcn_fmed3f(__builtin_fmaf(v[j], vscale2, voff), 0.0f, (float)(kBins - 1));
-        return (bj == bsel) & (v[j] >= vmin2);
-      };
-      if (m <= kCandMax) {
-        // gather the bin's values and rank them
-        slots([&](int j) {
-          const bool in = in_bin(j);
-          const uint64_t mask = __ballot(in);
-          if (mask) {
-            const int leader = __ffsll((unsigned long long)mask) - 1;
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&s_ncand, __popcll(mask));
-            base = __shfl(base, leader);
-            if (in) cand[base + __popcll(mask & ((1ull << lane) - 1ull))] = v[j];
-          }
-        });
-        __syncthreads();
-        rank_candidates(cand, m, K - cnt_above, tid, s_T, s_gt);
-        __syncthreads();
-        cnt_above += s_gt;
-        T = s_T;
-        found = true;
-      } else {
-        // a crowded bin: exact key rounds below, over its key interval
-        uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
-        slots([&](int j) {
-          const bool in = in_bin(j);
-          const uint32_t kj = order_key(v[j]);
-          cmin = min(cmin, in ? kj : 0xFFFFFFFFu);
-          cmax = max(cmax, in ? kj : 0u);
-        });
-        cmin = wave_min_u32(cmin);
-        cmax = wave_max_u32(cmax);
-        if (lane == 0) {
-          wmin[wave] = cmin;
-          wmax[wave] = cmax;
-        }
-        __syncthreads();
-        lo = 0xFFFFFFFFu;
-        hi = 0u;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          lo = min(lo, wmin[w]);
-          hi = max(hi, wmax[w]);
-        }
-      }
-      __syncthreads();
+  if (crowded) {
+    uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
+    const float spare = -1.0f - (float)lane;
+    slots([&](int j) {
+      const float x = reload(j);
+      const int bj = (int)__builtin_amdgcn_fmed3f((x - c_vmin) * c_vscale, spare, (float)(kBins - 1));
+      const bool in = bj == c_bin;
+      const uint32_t kj = order_key(x);
+      cmin = min(cmin, in ? kj : 0xFFFFFFFFu);
+      cmax = max(cmax, in ? kj : 0u);
+    });
+    cmin = wave_min_u32(cmin);
+    cmax = wave_max_u32(cmax);
+    if (lane == 0) {
+      wmin[wave] = cmin;
+      wmax[wave] = cmax;
     }
+    __syncthreads();
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lo = min(lo, wmin[w]);
+      hi = max(hi, wmax[w]);
+    }
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    __syncthreads();
   }
-  // 2b. Exact rounds over the order keys in [lo, hi]: cut into at most 2048
+  // 2f. Exact rounds over the order keys in [lo, hi]: cut into at most 2048
   //     bins (a shift of the key offset), keep the bin holding the K-th
   //     largest; when it holds <= kCandMax values they are ranked directly.
-  //     (Keys are recomputed each round; the opaque copy keeps the compiler
-  //     from hoisting J of them out of the loop.  -inf maps below every
-  //     finite key.)
+  //     (Keys are recomputed from fresh reloads each round.  -inf maps below
+  //     every finite key.)
   auto key_of = [&](int j) {
-    float x = v[j];
-    asm volatile("" : "+v"(x));
-    return order_key(x);
+    return order_key(reload(j));
   };
   for (int round = 0; round < 4 && !found && lo < hi; ++round) {
     const uint32_t range = hi - lo;
     const int width = 32 - __clz(range);
     const int shift = width > 11 ? width - 11 : 0;
     const int nb = (int)(range >> shift) + 1;
-    for (int b = tid; b < nb; b += NT) hist[b] = 0;
+    for (int b = tid; b < nb; b += NT) bins[b] = 0;
     if (tid == 0) s_ncand = 0;
     __syncthreads();
     slots([&](int j) {
       const uint32_t kj = key_of(j);
-      if (kj >= lo && kj <= hi) atomicAdd(&hist[(kj - lo) >> shift], 1u);
+      if (kj >= lo && kj <= hi) atomicAdd(&bins[(kj - lo) >> shift], 1u);
     });
     __syncthreads();
-    const int b = select_bin<NT>(hist, nb, K, cnt_above, tid, lane, wave, part, s_bin, s_cnt);
-    const int m = (int)hist[b];
+    const int b = select_bin<NT>(bins, nb, K, cnt_above, tid, lane, wave, part, s_bin, s_cnt);
+    const int m = (int)bins[b];
     cnt_above = s_cnt;
     const uint64_t nlo = (uint64_t)lo + ((uint64_t)b << shift);
     const uint64_t nhi = nlo + ((1ull << shift) - 1ull);
@@ -331,7 +310,8 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
     hi = (uint32_t)min<uint64_t>(nhi, (uint64_t)hi);
     if (lo < hi && m <= kCandMax) {
       slots([&](int j) {
-        const uint32_t kj = key_of(j);
+        const float x = reload(j);
+        const uint32_t kj = order_key(x);
         const bool in = (kj >= lo) & (kj <= hi);
         const uint64_t mask = __ballot(in);
         if (mask) {
@@ -339,7 +319,7 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
           int base = 0;
           if (lane == leader) base = atomicAdd(&s_ncand, __popcll(mask));
           base = __shfl(base, leader);
-          if (in) cand[base + __popcll(mask & ((1ull << lane) - 1ull))] = v[j];
+          if (in) cand[base + __popcll(mask & ((1ull << lane) - 1ull))] = x;
         }
       });
       __syncthreads();
@@ -358,8 +338,9 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
   //    value == T (-inf is neither), one ballot per slot: slot j of wave w
   //    covers positions NT j + 64 w .. +63, mask words NT j / 32 + 2 w, + 1.
   slots([&](int j) {
-    const uint64_t g = __ballot(v[j] > T);
-    const uint64_t e = __ballot(v[j] == T);
+    const float x = reload(j);
+    const uint64_t g = __ballot(x > T);
+    const uint64_t e = __ballot(x == T);
     if (lane == 0) {
       const int wd = NT / 32 * j + 2 * wave;
       gtmask[wd] = (uint32_t)g;
@@ -369,41 +350,242 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
     }
   });
   __syncthreads();
-  //    Thread t owns the 32*WPT consecutive positions of words WPT t ..: one
-  //    scan of both counts (packed in 16-bit halves; a row has at most 32768
-  //    positions), then ties are taken in position order.
-  const int nwd = nj * (NT / 32);  // words past the last slot holding positions are all zero
-  uint32_t gw[WPT], ew[WPT];
-  uint32_t packed = 0;
+  compact_masks<NT, J, true>(sh, nj * (NT / 32), need_eq, K, k, o);
+}
+
+// The first-cut bin holding the K-th largest value, picked by one wave (the
+// caller's wave 0): lane l owns the 32 bins of group g = 63 - l (bins 32 g ..
+// 32 g + 31, at words 33 g .. 33 g + 31), lanes in descending bin order, so a
+// wave scan of the lanes' sums counts the values above each lane's bins.  The
+// lane that holds the K-th largest writes its bin to s_bin and the count of
+// values above that bin to s_cnt.
+__device__ __forceinline__ void select_bin_wave(const uint32_t* bins, int K, int lane, int32_t& s_bin,
+                                                int32_t& s_cnt) {
+  const int g = 63 - lane;
+  const uint32_t* src = bins + 33 * g;
+  uint32_t c[32];
 #pragma unroll
-  for (int u = 0; u < WPT; ++u) {
-    const int wd = WPT * tid + u;
-    gw[u] = wd < nwd ? gtmask[wd] : 0u;
-    ew[u] = wd < nwd ? eqmask[wd] : 0u;
-    packed += (uint32_t)__popc(gw[u]) | ((uint32_t)__popc(ew[u]) << 16);
-  }
-  const uint32_t before = block_excl_scan<NW>(packed, lane, wave, part);
-  const int gt_before = (int)(before & 0xFFFFu);
-  int eq_seen = (int)(before >> 16);
-  int out = gt_before + min(eq_seen, need_eq);
+  for (int i = 0; i < 32; ++i) c[i] = src[i];
+  uint32_t local = 0;
 #pragma unroll
-  for (int u = 0; u < WPT; ++u) {
-    int take = min(max(need_eq - eq_seen, 0), __popc(ew[u]));
-    eq_seen += __popc(ew[u]);
-    uint32_t sel = gw[u];
-    uint32_t e = ew[u];
-    for (; take > 0; --take) {
-      sel |= e & (~e + 1u);  // lowest remaining tie
-      e &= e - 1u;
+  for (int i = 0; i < 32; ++i) local += c[i];
+  const int above = (int)(wave_incl_scan(local, lane) - local);
+  // from the group's top bin down: the first bin where the running count
+  // reaches K (branch-free; only the lane whose range holds K finds one)
+  int run = above, at = -1, before = 0;
+#pragma unroll
+  for (int i = 31; i >= 0; --i) {
+    const int next = run + (int)c[i];
+    const bool hit = at < 0 && run < K && next >= K;
+    at = hit ? i : at;
+    before = hit ? run : before;
+    run = next;
+  }
+  if (at >= 0) {
+    s_bin = 32 * g + at;
+    s_cnt = before;
+  }
+}
+
+// The selection for one row of ctx positions (K = min(k, ctx) < ctx): slot j
+// of thread t holds position t + NT j; slots at or past ctx hold a copy of a
+// value of the row (they are set to -inf here, after the range).  at(p) reads
+// the value of position p < ctx again.  Writes the row's k outputs to o.
+//
+// Common path (the threshold bin of the first histogram holds at most
+// kCandMax values): one pass writes bit masks of the positions in bins above
+// the threshold bin and gathers the threshold bin's positions; each
+// candidate's rank in (value descending, position ascending) order decides
+// whether it is one of the K - above selected from that bin, whose bits join
+// the masks; the masks are compacted in position order.  Otherwise exact key
+// rounds find the K-th largest value T and positions are compacted from bit
+// masks of value > T and value == T.
+template <int NT, int J, typename At>
+__device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k, int32_t* __restrict__ o,
+                                            TopkRegShared<NT, J>& sh, At&& at) {
+  static_assert(NT >= kCandMax && NT <= 1024 && kBins % NT == 0, "threads per row");
+  constexpr int NW = NT / 64;       // waves
+  constexpr int NWD = NT * J / 32;  // 32-position mask words of a row
+  // Rows of up to 32 slots keep their values beside the bins (J more
+  // registers fit), so the threshold bin's values are gathered from
+  // registers; longer rows keep only the bins and read those values again.
+  constexpr bool KEEP = J <= 32;
+  uint32_t* bins = sh.hist + kHistBase;  // first-cut bin b counts at bins[bin_word(b)]
+  uint32_t* gtmask = sh.gtmask;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto slots = [&](auto&& f) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) f(j);
+  };
+  // a slot's position, recomputed where it is used (an opaque copy of the
+  // thread index), not kept in J registers
+  auto pos_of = [&](int j) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return t + j * NT;
+  };
+
+  for (int b = tid; b < kHistWords; b += NT) sh.hist[b] = 0;
+  if (tid == 0) sh.s_ncand = 0;
+  float mn = v[0], mx = v[0];
+  slots([&](int j) {
+    if (j > 0) {
+      mn = fminf(mn, v[j]);
+      mx = fmaxf(mx, v[j]);
     }
-    while (sel) {
-      const int b = __ffs(sel) - 1;
-      if (out < K) o[out] = 32 * (WPT * tid + u) + b;
-      ++out;
-      sel &= sel - 1u;
+  });
+  {
+    const uint32_t kmn = wave_min_u32(order_key(mn)), kmx = wave_max_u32(order_key(mx));
+    if (lane == 0) {
+      sh.wmin[wave] = kmn;
+      sh.wmax[wave] = kmx;
     }
   }
-  for (int i = K + tid; i < k; i += NT) o[i] = -1;
+  slots([&](int j) {
+    if (tid + j * NT >= ctx) v[j] = -__builtin_inff();
+  });
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;  // order keys of the row's min and max
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, sh.wmin[w]);
+    hi = max(hi, sh.wmax[w]);
+  }
+  // values read from LDS are not known to be uniform: scalar copies, so the
+  // branches on them are scalar branches
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  int cnt_above = 0;     // values above the current search interval
+  bool crowded = false;  // first-cut bin c_bin holds more than kCandMax values
+  int c_bin = 0;
+  float c_vmin = 0.0f, c_vscale = 0.0f;
+
+  // 2. threshold search.
+  // 2a. First cut, linear in value: bin(v) = min(2047, (v - vmin) * (2048 /
+  //     (vmax - vmin))), each step correctly rounded, is monotone in v, so the
+  //     bin holding the K-th largest value holds a contiguous value interval,
+  //     and ties share a bin.  (Bins linear in the bit pattern would be
+  //     logarithmic in value and pile a row onto a few bins.)  v - vmin >= 0
+  //     for every value of the row, and -inf (past the row end) gives
+  //     -1 - lane: the lane's spare counter, never a bin, so no per-slot test
+  //     and no pile-up of atomics on one bin.  Skipped when the value range is
+  //     not a finite positive float.
+  if (lo < hi) {
+    const float vmin = key_value(lo), vmax = key_value(hi);
+    const float vrange = vmax - vmin;
+    const float vscale = (float)kBins / vrange;
+    if (vrange > 0.0f && vrange <= 3.4028234664e38f && vscale <= 3.4028234664e38f) {
+      const float spare = -1.0f - (float)lane;
+      int bn[KEEP ? J : 1];  // the slots' bins (KEEP), else held in v
+      slots([&](int j) {
+        const int b = (int)__builtin_amdgcn_fmed3f((v[j] - vmin) * vscale, spare, (float)(kBins - 1));
+        atomicAdd(&bins[bin_word(b)], 1u);
+        if constexpr (KEEP) bn[j] = b;
+        else v[j] = __int_as_float(b);  // the slot's bin from here on
+      });
+      auto bin_of = [&](int j) {
+        if constexpr (KEEP) return bn[j];
+        else return __float_as_int(v[j]);
+      };
+      __syncthreads();
+      if (wave == 0) select_bin_wave(bins, K, lane, sh.s_bin, sh.s_cnt);
+      __syncthreads();
+      const int bsel = __builtin_amdgcn_readfirstlane(sh.s_bin);
+      const int m = __builtin_amdgcn_readfirstlane((int)bins[bin_word(bsel)]);
+      cnt_above = __builtin_amdgcn_readfirstlane(sh.s_cnt);
+      if (m <= kCandMax) {
+        // 2b. Bit masks of the positions in bins above bsel (lane 2 j + h of
+        //     each wave collects half h of slot j's ballot, then every lane
+        //     writes its word: slot j of wave w covers positions NT j + 64 w
+        //     .. + 63, mask words NT j / 32 + 2 w, + 1), and the positions
+        //     (and values, KEEP) of bin bsel.
+        const int need = K - cnt_above;  // 1 <= need <= m
+        constexpr int NMV = (2 * J + 63) / 64;
+        uint32_t gw[NMV];
+#pragma unroll
+        for (int r = 0; r < NMV; ++r) gw[r] = 0;
+        int bselv = bsel;
+        slots([&](int j) {
+          const int b = bin_of(j);
+          const uint64_t gm = __builtin_amdgcn_ballot_w64(b > bselv);
+          if (__builtin_amdgcn_ballot_w64(b == bselv)) {  // wave-uniform, rare
+            if (b == bselv) {
+              const int idx = atomicAdd(&sh.s_ncand, 1);
+              sh.cand_pos[idx] = pos_of(j);
+              if constexpr (KEEP) sh.cand[idx] = v[j];
+            }
+          }
+          const uint32_t glo = (uint32_t)gm, ghi = (uint32_t)(gm >> 32);
+          asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(gw[(2 * j) / 64]) : "s"(glo), "n"((2 * j) % 64));
+          asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(gw[(2 * j + 1) / 64]) : "s"(ghi), "n"((2 * j + 1) % 64));
+          // one slot at a time: the next slot's compares take bselv through
+          // this opaque copy, so the compiler does not compute every slot's
+          // ballots up front
+          asm volatile("" : "+v"(bselv) : "v"(gw[(2 * j) / 64]));
+        });
+#pragma unroll
+        for (int r = 0; r < NMV; ++r) {
+          const int e = 64 * r + lane;  // 2 j + h
+          if (e < 2 * J) gtmask[NT / 32 * (e >> 1) + 2 * wave + (e & 1)] = gw[r];
+        }
+        __syncthreads();
+        // 2c. A candidate is selected when fewer than need candidates come
+        //     before it in (value descending, position ascending) order; its
+        //     bit joins gtmask.
+        if (m <= 64) {
+          // one wave: candidate c in lane c, compared through lane reads
+          if (wave == 0) {
+            const int pt = lane < m ? sh.cand_pos[lane] : 0;
+            float vt = 0.0f;
+            if constexpr (KEEP) vt = lane < m ? sh.cand[lane] : 0.0f;
+            else vt = lane < m ? at(pt) : 0.0f;
+            int before = 0;
+            for (int c = 0; c < m; ++c) {
+              const float vc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vt), c));
+              const int pc = __builtin_amdgcn_readlane(pt, c);
+              before += (vc > vt || (vc == vt && pc < pt)) ? 1 : 0;
+            }
+            if (lane < m && before < need) atomicOr(&gtmask[pt >> 5], 1u << (pt & 31));
+          }
+        } else {
+          if constexpr (!KEEP) {
+            if (tid < m) sh.cand[tid] = at(sh.cand_pos[tid]);
+            __syncthreads();
+          }
+          if (tid < m) {
+            const float vt = sh.cand[tid];
+            const int pt = sh.cand_pos[tid];
+            int before = 0;
+            for (int c0 = 0; c0 < m; c0 += 4) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int c = min(c0 + u, m - 1);
+                const float vc = sh.cand[c];
+                const int pc = sh.cand_pos[c];
+                before += (c0 + u < m && (vc > vt || (vc == vt && pc < pt))) ? 1 : 0;
+              }
+            }
+            if (before < need) atomicOr(&gtmask[pt >> 5], 1u << (pt & 31));
+          }
+        }
+        __syncthreads();
+        // 2d. The selected positions, ascending.
+        compact_masks<NT, J, false>(sh, NWD, 0, K, k, o);
+        return;
+      }
+      crowded = true;  // the bin needs exact key rounds, over its key interval
+      c_bin = bsel;
+      c_vmin = vmin;
+      c_vscale = vscale;
+    }
+  }
+  topk_select_exact<NT, J>(
+      [&](int j) {
+        const int p = pos_of(j);  // a fresh read: not merged with the first one
+        const float x = at(min(p, ctx - 1));
+        return p < ctx ? x : -__builtin_inff();
+      },
+      ctx, K, k, o, &sh, crowded, c_bin, c_vmin, c_vscale, lo, hi, cnt_above);
 }
 
 }  // namespace fp4idx
