@@ -169,37 +169,44 @@ struct TopkRegShared {
 // Ordered compaction of a row's bit masks (word wd holds positions 32 wd ..
 // 32 wd + 31): the positions set in gtmask, then (EQ) the first need_eq set
 // in eqmask, in position order; written ascending to o[0, K), -1 after.
-// Thread t owns the 32*WPT consecutive positions of words WPT t ..: one scan
-// of both counts (packed in 16-bit halves; a row has at most 32768
-// positions), then ties are taken in position order.  Words from nwd on are
-// zero.
+// Thread t owns the J positions J t .. J t + J - 1 (every thread has a share,
+// so no lane walks more than J bits): one scan of both counts (packed in
+// 16-bit halves; a row has at most 32768 positions), then ties are taken in
+// position order.
 template <int NT, int J, bool EQ>
-__device__ __forceinline__ void compact_masks(TopkRegShared<NT, J>& sh, int nwd, int need_eq, int K, int k,
+__device__ __forceinline__ void compact_masks(TopkRegShared<NT, J>& sh, int need_eq, int K, int k,
                                               int32_t* __restrict__ o) {
   constexpr int NW = NT / 64;
   constexpr int NWD = NT * J / 32;
-  constexpr int WPT = (NWD + NT - 1) / NT;
+  constexpr int NCH = (J + 31) / 32;  // the thread's bits in 32-bit chunks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t gw[WPT], ew[WPT];
+  const int p0 = J * tid;
+  auto chunk = [&](const uint32_t* m, int q) {
+    const int pos = p0 + 32 * q, nb = J - 32 * q < 32 ? J - 32 * q : 32;
+    const int wd = pos >> 5;
+    const uint64_t two = (uint64_t)m[wd] | ((uint64_t)m[min(wd + 1, NWD - 1)] << 32);
+    const uint32_t bits = (uint32_t)(two >> (pos & 31));
+    return nb < 32 ? bits & ((1u << nb) - 1u) : bits;
+  };
+  uint32_t gw[NCH], ew[NCH];
   uint32_t packed = 0;
 #pragma unroll
-  for (int u = 0; u < WPT; ++u) {
-    const int wd = WPT * tid + u;
-    gw[u] = wd < nwd ? sh.gtmask[wd] : 0u;
-    ew[u] = EQ && wd < nwd ? sh.eqmask[wd] : 0u;
-    packed += (uint32_t)__popc(gw[u]) | ((uint32_t)__popc(ew[u]) << 16);
+  for (int q = 0; q < NCH; ++q) {
+    gw[q] = chunk(sh.gtmask, q);
+    ew[q] = EQ ? chunk(sh.eqmask, q) : 0u;
+    packed += (uint32_t)__popc(gw[q]) | ((uint32_t)__popc(ew[q]) << 16);
   }
   const uint32_t before = block_excl_scan<NW>(packed, lane, wave, sh.part);
   const int gt_before = (int)(before & 0xFFFFu);
   int eq_seen = (int)(before >> 16);
   int out = gt_before + min(eq_seen, need_eq);
 #pragma unroll
-  for (int u = 0; u < WPT; ++u) {
-    uint32_t sel = gw[u];
+  for (int q = 0; q < NCH; ++q) {
+    uint32_t sel = gw[q];
     if constexpr (EQ) {
-      int take = min(max(need_eq - eq_seen, 0), __popc(ew[u]));
-      eq_seen += __popc(ew[u]);
-      uint32_t e = ew[u];
+      int take = min(max(need_eq - eq_seen, 0), __popc(ew[q]));
+      eq_seen += __popc(ew[q]);
+      uint32_t e = ew[q];
       for (; take > 0; --take) {
         sel |= e & (~e + 1u);  // lowest remaining tie
         e &= e - 1u;
@@ -207,7 +214,7 @@ __device__ __forceinline__ void compact_masks(TopkRegShared<NT, J>& sh, int nwd,
     }
     while (sel) {
       const int b = __ffs(sel) - 1;
-      if (out < K) o[out] = 32 * (WPT * tid + u) + b;
+      if (out < K) o[out] = p0 + 32 * q + b;
       ++out;
       sel &= sel - 1u;
     }
@@ -243,7 +250,6 @@ __device__ __forceinline__ void topk_select_exact(Reload reload, int ctx, int K,
   int32_t& s_gt = sh.s_gt;
   float& s_T = sh.s_T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nj = (ctx + NT - 1) / NT;  // 1 <= nj <= J
   // eight slots at a time: their loads are in flight together
   auto slots = [&](auto&& f) {
 #pragma unroll 8
@@ -350,40 +356,36 @@ __device__ __forceinline__ void topk_select_exact(Reload reload, int ctx, int K,
     }
   });
   __syncthreads();
-  compact_masks<NT, J, true>(sh, nj * (NT / 32), need_eq, K, k, o);
+  compact_masks<NT, J, true>(sh, need_eq, K, k, o);
 }
 
 // The first-cut bin holding the K-th largest value, picked by one wave (the
-// caller's wave 0): lane l owns the 32 bins of group g = 63 - l (bins 32 g ..
-// 32 g + 31, at words 33 g .. 33 g + 31), lanes in descending bin order, so a
-// wave scan of the lanes' sums counts the values above each lane's bins.  The
-// lane that holds the K-th largest writes its bin to s_bin and the count of
-// values above that bin to s_cnt.
+// caller's wave 0) in two scans: lane l first sums the 32 bins of group
+// g = 63 - l (bins 32 g .. 32 g + 31, at words 33 g .. 33 g + 31), lanes in
+// descending bin order, so a wave scan counts the values above each group;
+// then lanes 0..31 take the 32 bins of the group that holds the K-th largest,
+// again in descending order.  Lane 0 writes the bin to s_bin and the count
+// of values above it to s_cnt.  (K is at most the number of binned values,
+// so each scan has exactly one lane where the count crosses K.)
 __device__ __forceinline__ void select_bin_wave(const uint32_t* bins, int K, int lane, int32_t& s_bin,
                                                 int32_t& s_cnt) {
-  const int g = 63 - lane;
-  const uint32_t* src = bins + 33 * g;
-  uint32_t c[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) c[i] = src[i];
+  const uint32_t* src = bins + 33 * (63 - lane);
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) local += c[i];
-  const int above = (int)(wave_incl_scan(local, lane) - local);
-  // from the group's top bin down: the first bin where the running count
-  // reaches K (branch-free; only the lane whose range holds K finds one)
-  int run = above, at = -1, before = 0;
-#pragma unroll
-  for (int i = 31; i >= 0; --i) {
-    const int next = run + (int)c[i];
-    const bool hit = at < 0 && run < K && next >= K;
-    at = hit ? i : at;
-    before = hit ? run : before;
-    run = next;
-  }
-  if (at >= 0) {
-    s_bin = 32 * g + at;
-    s_cnt = before;
+  for (int i = 0; i < 32; ++i) local += src[i];
+  const uint32_t incl = wave_incl_scan(local, lane);
+  const uint64_t hit = __builtin_amdgcn_ballot_w64((int)(incl - local) < K && (int)incl >= K);
+  const int l1 = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  const int g = 63 - l1;
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - local), l1);
+  const uint32_t c = lane < 32 ? bins[33 * g + 31 - lane] : 0u;
+  const uint32_t incl2 = wave_incl_scan(c, lane) + above;
+  const uint64_t hit2 = __builtin_amdgcn_ballot_w64(lane < 32 && (int)(incl2 - c) < K && (int)incl2 >= K);
+  const int l2 = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit2));
+  const int cnt = __builtin_amdgcn_readlane((int)(incl2 - c), l2);
+  if (lane == 0) {
+    s_bin = 32 * g + 31 - l2;
+    s_cnt = cnt;
   }
 }
 
@@ -570,7 +572,7 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
         }
         __syncthreads();
         // 2d. The selected positions, ascending.
-        compact_masks<NT, J, false>(sh, NWD, 0, K, k, o);
+        compact_masks<NT, J, false>(sh, 0, K, k, o);
         return;
       }
       crowded = true;  // the bin needs exact key rounds, over its key interval
