@@ -82,10 +82,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, int lane, int wa
   const uint32_t incl = wave_incl_scan(v, lane);
   if (lane == 63) part[wave] = incl;
   __syncthreads();
-  uint32_t before = incl - v;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) before += w < wave ? part[w] : 0u;
-  return before;
+  // the waves below this one: lane w holds wave w's total, one wave scan
+  const uint32_t pw = lane < NW ? part[lane] : 0u;
+  const uint32_t below = wave_incl_scan(pw, lane) - pw;
+  return incl - v + (uint32_t)__builtin_amdgcn_readlane((int)below, wave);
 }
 
 // Picks the bin holding the K-th largest key given counts hist[0, nb) and
@@ -447,16 +447,10 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
     if (tid + j * NT >= ctx) v[j] = -__builtin_inff();
   });
   __syncthreads();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;  // order keys of the row's min and max
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    lo = min(lo, sh.wmin[w]);
-    hi = max(hi, sh.wmax[w]);
-  }
-  // values read from LDS are not known to be uniform: scalar copies, so the
-  // branches on them are scalar branches
-  lo = __builtin_amdgcn_readfirstlane(lo);
-  hi = __builtin_amdgcn_readfirstlane(hi);
+  // order keys of the row's min and max: lane w holds wave w's, one wave
+  // reduction (its result is uniform: the branches on it are scalar)
+  uint32_t lo = wave_min_u32(lane < NW ? sh.wmin[lane] : 0xFFFFFFFFu);
+  uint32_t hi = wave_max_u32(lane < NW ? sh.wmax[lane] : 0u);
   int cnt_above = 0;     // values above the current search interval
   bool crowded = false;  // first-cut bin c_bin holds more than kCandMax values
   int c_bin = 0;
