@@ -273,30 +273,29 @@ static hipError_t launch_reg(const float* logits, int64_t n_rows, int64_t logits
 
 // Rows in registers: a few rows (at most one per CU) take 1024 threads each,
 // the shortest path for one row; more rows take 512 threads each, so that
-// several rows share a CU and one row's barriers overlap the others' work (up
-// to 24,576 positions; longer rows need too many registers for two).  From
-// 12,289 to 18,432 positions a 512-thread row needs enough registers that only
-// two fit a CU; 256-thread rows then fit four in the same registers, and the
-// extra overlap is worth their longer per-thread loops.  J covers the longest
-// row with little slack (every slot is processed).
+// several rows share a CU and one row's barriers overlap the others' work.
+// J covers the longest row with little slack (every slot is processed).
+// (Measured on 1,536 and 4,096 rows of 17,408 positions and 408 rows of up to
+// 32,768: 512 x 36 and 512 x 64 beat 256 x 72 and 1024 x 18, and 1024 x 32,
+// by 5-15 %.)
 constexpr int64_t kRowsPerCuSwitch = 256;
 
 hipError_t launch_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx, int32_t k,
                        int32_t* out_idx, int64_t max_ctx, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  if (max_ctx <= kRegMaxCtx && (n_rows <= kRowsPerCuSwitch || max_ctx > 24576)) {
+  if (max_ctx <= kRegMaxCtx && n_rows <= kRowsPerCuSwitch) {
     if (max_ctx <= 8192) return launch_reg<1024, 8>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
     if (max_ctx <= 16384) return launch_reg<1024, 16>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
     if (max_ctx <= 24576) return launch_reg<1024, 24>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
     return launch_reg<1024, 32>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
   }
-  if (max_ctx <= 24576) {  // two or more rows per CU fit the registers up to here
+  if (max_ctx <= kRegMaxCtx) {
     if (max_ctx <= 8192) return launch_reg<512, 16>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
     if (max_ctx <= 12288) return launch_reg<512, 24>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
-    if (max_ctx <= 16384) return launch_reg<256, 64>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
-    if (max_ctx <= 18432) return launch_reg<256, 72>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
-    return launch_reg<512, 48>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
+    if (max_ctx <= 18432) return launch_reg<512, 36>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
+    if (max_ctx <= 24576) return launch_reg<512, 48>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
+    return launch_reg<512, 64>(logits, n_rows, logits_stride, row_ctx, k, out_idx, stream);
   }
   return launch(topk_long_kernel<false>, dim3((unsigned)n_rows), dim3(kTopkThreads), kBins * sizeof(uint32_t), stream,
                 logits, logits_stride, row_ctx, k, out_idx);

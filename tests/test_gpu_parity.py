@@ -481,10 +481,10 @@ def test_topk_full_size_bit_exact(F, orc, cfg):
 @pytest.mark.parametrize("rows,max_ctx", [(300, 8000), (300, 12000), (300, 16000), (300, 18000), (300, 24000),
                                           (300, 30000), (40, 20000), (40, 30000)])
 def test_topk_every_register_variant_bit_exact(F, orc, rows, max_ctx):
-    """Row counts on both sides of the 1024-thread / smaller-row switch and
-    row lengths in every register band (512-thread rows up to 12,288 and past
-    18,432 positions, 256-thread rows between); ragged rows (including ctx 0, ctx < k,
-    ctx = k, ctx = k + 1), planted ties and a crowded row."""
+    """Row counts on both sides of the 1024-thread / 512-thread switch and row
+    lengths in every register band (512 threads x 16, 24, 36, 48 and 64 slots;
+    1024 x 24 and 32); ragged rows (including ctx 0, ctx < k, ctx = k,
+    ctx = k + 1), planted ties and a crowded row."""
     rng = np.random.default_rng([rows, max_ctx])
     vals = (rng.standard_normal((rows, max_ctx)) * 10).astype(np.float32)
     vals[:, ::61] = np.round(vals[:, ::61])                          # ties
