@@ -444,7 +444,7 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
     }
   }
   slots([&](int j) {
-    if (tid + j * NT >= ctx) v[j] = -__builtin_inff();
+    if (tid >= ctx - j * NT) v[j] = -__builtin_inff();  // position tid + NT j past the row end
   });
   __syncthreads();
   // order keys of the row's min and max: lane w holds wave w's, one wave
@@ -517,7 +517,7 @@ __device__ __forceinline__ void topk_select(float (&v)[J], int ctx, int K, int k
           // one slot at a time: the next slot's compares take bselv through
           // this opaque copy, so the compiler does not compute every slot's
           // ballots up front
-          asm volatile("" : "+v"(bselv) : "v"(gw[(2 * j) / 64]));
+          asm volatile("" : "+s"(bselv) : "v"(gw[(2 * j) / 64]));
         });
 #pragma unroll
         for (int r = 0; r < NMV; ++r) {
