@@ -286,7 +286,7 @@ __device__ __forceinline__ void topk_select_exact(Reload reload, int ctx, int K,
     hi = __builtin_amdgcn_readfirstlane(hi);
     __syncthreads();
   }
-  // 2f. Exact rounds over the order keys in [lo, hi]: cut into at most 2048
+  // Exact rounds over the order keys in [lo, hi]: cut into at most 2048
   //     bins (a shift of the key offset), keep the bin holding the K-th
   //     largest; when it holds <= kCandMax values they are ranked directly.
   //     (Keys are recomputed from fresh reloads each round.  -inf maps below
