@@ -482,37 +482,33 @@ static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const f
 }
 
 // FP4 batches of requests with three or more rows each on average: the
-// shared-page kernel, NW waves of RW rows per work-group (at 128 heads two
-// rows per wave keep the Q operands in registers).  The work-group's row count
-// follows `rows`, the largest request's rows when the counts are near-uniform
-// and the average otherwise (a larger work-group than the typical request
-// leaves its waves idle).  A non-uniform batch also takes shorter page chunks:
-// its work-groups' lengths vary with their requests' rows and contexts, and
-// the last ones to finish set the kernel's time (measured on 48 requests of
-// 1-16 rows over 8k-32k tokens: 81 us against 111 us with the near-uniform
-// shape and chunks; on the near-uniform batches the shorter chunks change
-// nothing).
+// shared-page kernel, NW waves of RW rows per work-group.  Two rows per wave
+// at most past six rows: a third or fourth row's Q operands and weights take
+// enough registers to cut the waves per SIMD from four to two, which costs
+// more than the extra page staging saves (prefill, 4,096 rows: 365 us with
+// 4 x 2 against 386 us with 4 x 4; 6-row decode: 2 x 3 and 4 x 2 alike).  A
+// batch whose row counts are far from uniform (the average below 3/4 of the
+// largest) takes two waves of two rows and page chunks of at most 16
+// page-rows per wave: its work-groups' lengths vary with their requests' rows
+// and contexts, and the last ones to finish set the kernel's time (48
+// requests of 1-16 rows over 8k-32k tokens: 76 us, against 85 us with 4 x 3
+// and 32 page-rows and 111 us with the near-uniform shape and chunks).
 template <int NMT>
 static hipError_t launch_fp4_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                                     int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
                                     int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
                                     int64_t num_pages, float* logits, int64_t logits_stride,
-                                    int32_t max_rows_per_req, int64_t max_ctx, int64_t rows, bool uniform,
-                                    hipStream_t stream) {
-  const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 2;
+                                    int32_t max_rows_per_req, int64_t max_ctx, bool uniform, hipStream_t stream) {
+  const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 4;
 #define FP4IDX_SHARED(NW, RW)                                                                                       \
   launch_shared<NW, RW, NMT>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,       \
                              num_pages, logits, logits_stride, max_rows_per_req, max_ctx, page_rows, stream)
-  const int64_t r = rows;
-  if constexpr (NMT == 8) {
-    return r <= 4 ? FP4IDX_SHARED(2, 2) : FP4IDX_SHARED(4, 2);
-  } else {
-    if (r <= 4) return FP4IDX_SHARED(2, 2);
+  const int r = max_rows_per_req;
+  if (!uniform || r <= 4) return FP4IDX_SHARED(2, 2);
+  if constexpr (NMT != 8) {
     if (r <= 6) return FP4IDX_SHARED(2, 3);
-    if (r <= 8) return FP4IDX_SHARED(2, 4);
-    if (r <= 12) return FP4IDX_SHARED(4, 3);
-    return FP4IDX_SHARED(4, 4);
   }
+  return FP4IDX_SHARED(4, 2);
 #undef FP4IDX_SHARED
 }
 
@@ -537,8 +533,8 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
 #define FP4IDX_HEADS(H, NMT)                                                                                        \
   case H:                                                                                                           \
     return launch_fp4_shared<NMT>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,     \
-                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx,              \
-                                  uniform ? (int64_t)max_rows_per_req : avg_rows, uniform, stream);
+                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, uniform,     \
+                                  stream);
     FP4IDX_HEADS(16, 1)
     FP4IDX_HEADS(32, 2)
     FP4IDX_HEADS(64, 4)

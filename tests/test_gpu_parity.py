@@ -279,11 +279,12 @@ def test_logits_rows_per_request_variants(F, orc):
 
 @pytest.mark.parametrize("rows,heads", [((3, 3), 64), ((4, 4, 3), 64), ((5, 5), 64), ((8, 7), 64), ((10, 9), 64),
                                         ((12, 12), 64), ((13, 13), 64), ((16, 14), 32), ((4, 4), 128),
-                                        ((7, 7), 128), ((6, 5), 16)])
+                                        ((7, 7), 128), ((6, 5), 16), ((16, 1, 1), 64), ((14, 2, 5), 128)])
 def test_logits_shared_page_kernel_every_shape(F, orc, rows, heads):
-    """Batches whose requests all have about the same number (three or more)
-    of rows go to the shared-page kernel; each rows-per-work-group shape it
-    picks, every head count, ragged contexts (a row block whose rows need
+    """Batches with three or more rows per request on average go to the
+    shared-page kernel; each rows-per-work-group shape it picks (near-uniform
+    row counts by the largest request, far-from-uniform ones with short page
+    chunks), every head count, ragged contexts (a row block whose rows need
     different pages, a zero-context row)."""
     ctxs = tuple(64 * 3 + 17 * (i + 1) for i in range(len(rows)))
     wl = W.small(seed=sum(rows) * heads, rows=rows, ctxs=ctxs, heads=heads)
