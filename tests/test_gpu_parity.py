@@ -497,6 +497,24 @@ def test_topk_every_register_variant_bit_exact(F, orc, rows, max_ctx):
     assert np.array_equal(got, orc.topk(vals, ctx, 2048))
 
 
+@pytest.mark.parametrize("rows", [300, 40])
+def test_topk_threshold_bin_paths_bit_exact(F, orc, rows):
+    """Values on a 1/8 grid, so every first-cut bin holds one grid value and
+    its ties: k = 64 leaves a few dozen candidates in the threshold bin (ranked
+    by one wave), k = 256 about a hundred (ranked through LDS), k = 2048 some
+    hundreds (exact key rounds).  300 rows of up to 18,000 positions take
+    512-thread rows of 36 slots, which re-read the candidates' values; 40 rows
+    take 1024-thread rows, which keep them in registers."""
+    rng = np.random.default_rng([rows, 7])
+    S = 18000
+    vals = (np.round(rng.standard_normal((rows, S)) * 8) / 8).astype(np.float32)
+    ctx = rng.integers(S - 3000, S + 1, rows).astype(np.int32)
+    ctx[-1] = S
+    for k in (64, 256, 2048):
+        got = _gpu_topk(F, vals, ctx, k)
+        assert np.array_equal(got, orc.topk(vals, ctx, k)), k
+
+
 def test_topk_long_rows_use_global_path(F, orc):
     rng = np.random.default_rng(43)
     T, S = 3, 40000
