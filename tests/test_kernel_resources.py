@@ -49,3 +49,30 @@ def test_no_kernel_spills_or_uses_scratch():
                            f"sgpr_spill={sspill}")
     assert seen >= 40, f"only {seen} kernels found in the assembly"
     assert not bad, "\n".join(bad)
+
+
+def _vgprs(asm: str):
+    for m in re.finditer(r"^\s+- \.agpr_count:.*?(?=^\s+- \.agpr_count:|\Z)", asm, re.S | re.M):
+        block = m.group(0)
+        name = re.search(r"\.name:\s+(\S+)", block)
+        if name:
+            agpr = int(re.search(r"\.agpr_count:\s+(\d+)", block).group(1))
+            vgpr = int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1))
+            yield name.group(1), vgpr + agpr
+
+
+def test_register_budgets_the_launch_shapes_rely_on():
+    """Launch shapes chosen for occupancy: a 512-thread top-k row (eight
+    waves) shares a CU with a second row only at <= 128 registers per lane
+    (four waves per SIMD), and the shared-page logits kernel's 4 x 2 shape was
+    picked for four waves per SIMD as well."""
+    if not os.path.exists(build.HIPCC):
+        pytest.skip("hipcc not available")
+    srcs = [s for s in build.sources() if os.path.basename(s) in ("topk.hip", "logits.hip")]
+    with tempfile.TemporaryDirectory() as d:
+        regs = dict(kv for s in srcs for kv in _vgprs(_assemble(s, d)))
+    want = {n: r for n, r in regs.items()
+            if "topk_reg_kernelILi512E" in n or "mqa_logits_shared_kernelILi4ELi2ELi4E" in n}
+    assert len(want) >= 6, sorted(regs)
+    over = {n: r for n, r in want.items() if r > 128}
+    assert not over, over
