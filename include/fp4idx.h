@@ -140,7 +140,10 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
  *
  *   q_fp4, q_scale, w   as produced by fp4idx_pack_q ([n_rows, n_heads, ...])
  *   req_row_indptr      [n_reqs+1] int32: rows of request b are
- *                       [indptr[b], indptr[b+1]); indptr[0] = 0, indptr[n_reqs] = n_rows
+ *                       [indptr[b], indptr[b+1]); indptr[0] = 0, indptr[n_reqs] = n_rows,
+ *                       non-decreasing (each bound is clamped into [0, n_rows] and
+ *                       indptr[b+1] to at least indptr[b], so broken values only
+ *                       ever touch rows 0..n_rows-1; their results are then unspecified)
  *   row_ctx_len         [n_rows] int32: row t scores tokens [0, ctx[t]);
  *                       0 <= ctx[t] <= max_ctx (a larger value writes at
  *                       most min(logits_stride, bt_stride*64) entries)

@@ -78,8 +78,8 @@ def _load():
         lib.orc_encode_q_head_fp8.argtypes = [P, P, P, P]
         lib.orc_write_k_fp8.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, i64]
         lib.orc_pack_q_fp8.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P]
-        lib.orc_logits_fp8.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, i64, P, i64, P, P, P]
-        lib.orc_logits_fp8_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, i64, i64, P, P, P, P, P]
+        lib.orc_logits_fp8.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, i64, P, i64, P, P, P, P]
+        lib.orc_logits_fp8_sampled.argtypes = [P, P, P, i32, P, i32, P, i32, P, i64, i64, P, P, P, P, P, P]
         for name in ("orc_write_k", "orc_pack_q", "orc_logits", "orc_logits_sampled", "orc_topk", "orc_read_k",
                      "orc_write_k_fp8", "orc_pack_q_fp8", "orc_logits_fp8", "orc_logits_fp8_sampled"):
             getattr(lib, name).restype = ctypes.c_int
@@ -337,9 +337,11 @@ def pack_q_fp8(q, pos, cos_sin, w_in, w_scale=1.0):
     return q_fp8, q_scale, w_out
 
 
-def logits_fp8(q_fp8, q_scale, w, indptr, row_ctx, block_table, pool, logits_stride=None, want_f64=False):
+def logits_fp8(q_fp8, q_scale, w, indptr, row_ctx, block_table, pool, logits_stride=None, want_f64=False,
+               want_b16=False):
     """FP8-variant logits [T, stride] (fp32; entries >= ctx stay NaN); with
-    want_f64 also the fp64 values and the T, A tolerance scales."""
+    want_f64 also the fp64 values and the T, A tolerance scales, and with
+    want_b16 as well B16 = sum_h |w_h| (sum of the 16 largest |q_hi k_i|)."""
     q_fp8 = _c(q_fp8, np.uint8); q_scale = _c(q_scale, np.float32); w = _c(w, np.float32)
     indptr = _c(indptr, np.int32); row_ctx = _c(row_ctx, np.int32); bt = _c(block_table, np.int32)
     T, H = q_fp8.shape[0], q_fp8.shape[1]
@@ -348,24 +350,29 @@ def logits_fp8(q_fp8, q_scale, w, indptr, row_ctx, block_table, pool, logits_str
     f64 = np.full((T, stride), np.nan, np.float64) if want_f64 else None
     tol = np.full((T, stride), np.nan, np.float64) if want_f64 else None
     absr = np.full((T, stride), np.nan, np.float64) if want_f64 else None
+    b16 = np.full((T, stride), np.nan, np.float64) if (want_f64 and want_b16) else None
     rc = _load().orc_logits_fp8(_p(q_fp8), _p(q_scale), _p(w), T, H, _p(indptr), len(indptr) - 1, _p(row_ctx),
                                 _p(bt), bt.shape[1], _p(pool), pool.size // FP8_PAGE_BYTES, _p(out), stride,
                                 _p(f64) if want_f64 else None, _p(tol) if want_f64 else None,
-                                _p(absr) if want_f64 else None)
+                                _p(absr) if want_f64 else None, _p(b16) if b16 is not None else None)
     _check(rc, "logits_fp8")
-    return (out, f64, tol, absr) if want_f64 else out
+    if not want_f64:
+        return out
+    return (out, f64, tol, absr, b16) if want_b16 else (out, f64, tol, absr)
 
 
-def logits_fp8_sampled(q_fp8, q_scale, w, indptr, block_table, pool, rows, toks):
-    """fp64 FP8-variant logits at (rows[i], toks[i]) with their T and A scales."""
+def logits_fp8_sampled(q_fp8, q_scale, w, indptr, block_table, pool, rows, toks, want_b16=False):
+    """fp64 FP8-variant logits at (rows[i], toks[i]) with their T and A scales
+    (and B16, see logits_fp8, with want_b16)."""
     q_fp8 = _c(q_fp8, np.uint8); q_scale = _c(q_scale, np.float32); w = _c(w, np.float32)
     indptr = _c(indptr, np.int32); bt = _c(block_table, np.int32)
     rows = _c(rows, np.int64); toks = _c(toks, np.int64)
     H = q_fp8.shape[1]
     out = np.empty(rows.size, np.float64); tol = np.empty(rows.size, np.float64)
     absr = np.empty(rows.size, np.float64)
+    b16 = np.empty(rows.size, np.float64) if want_b16 else None
     rc = _load().orc_logits_fp8_sampled(_p(q_fp8), _p(q_scale), _p(w), H, _p(indptr), len(indptr) - 1, _p(bt),
                                         bt.shape[1], _p(pool), pool.size // FP8_PAGE_BYTES, rows.size, _p(rows),
-                                        _p(toks), _p(out), _p(tol), _p(absr))
+                                        _p(toks), _p(out), _p(tol), _p(absr), _p(b16) if want_b16 else None)
     _check(rc, "logits_fp8_sampled")
-    return out, tol, absr
+    return (out, tol, absr, b16) if want_b16 else (out, tol, absr)

@@ -83,6 +83,23 @@ def logit(qcodes, qscales, w, kcodes, kscales) -> Fraction:
     return total
 
 
+def logit_terms(qvecs, w, kv):
+    """(L, T, A) exactly for dequantised vectors: L = sum_h w_h ReLU(q_h . k),
+    T = sum_h |w_h| ReLU(q_h . k) and A = sum_h |w_h| sum_i |q_hi k_i| (the
+    scales a floating-point evaluation's error is measured against).
+    qvecs: H lists of exact values, w: H floats, kv: the token's exact values."""
+    L = T = A = Fraction(0)
+    for h, qv in enumerate(qvecs):
+        d = sum((a * b for a, b in zip(qv, kv)), Fraction(0))
+        a = sum((abs(x * y) for x, y in zip(qv, kv)), Fraction(0))
+        wh = exact(w[h])
+        if d > 0:
+            L += wh * d
+            T += abs(wh) * d
+        A += abs(wh) * a
+    return L, T, A
+
+
 # ---- FP8 E4M3 (OCP OFP8 v1.0): bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN
 
 def e4m3_magnitude(code: int) -> Fraction:

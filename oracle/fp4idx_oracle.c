@@ -608,11 +608,40 @@ static void dequant_token_fp8(const uint8_t *pool, int64_t page, int t, double *
   orc_dequant_fp8_128(pool + page * PAGE8_BYTES + t * D, sc, out);
 }
 
+/* B16 = sum_h |w_h| * (the sum of the 16 largest |q_hi k_i| of head h): the
+ * scale of what an evaluation loses when it forms each dot product from 16
+ * groups of 8 products and cuts every product below a fixed fraction of its
+ * group's largest (the 16 group maxima are 16 distinct products, so their
+ * sum is at most this).  A checker's scale, not part of the score. */
+static double top16_scale(const double *qd, const float *w, int32_t n_heads, const double *kd) {
+  double B = 0.0;
+  for (int h = 0; h < n_heads; ++h) {
+    double top[16];
+    int n = 0;
+    for (int i = 0; i < D; ++i) {
+      double a = fabs(qd[h * D + i] * kd[i]);
+      if (n < 16) {
+        int j = n++;
+        while (j > 0 && top[j - 1] < a) { top[j] = top[j - 1]; --j; }
+        top[j] = a;
+      } else if (a > top[15]) {
+        int j = 15;
+        while (j > 0 && top[j - 1] < a) { top[j] = top[j - 1]; --j; }
+        top[j] = a;
+      }
+    }
+    double sum = 0.0;
+    for (int j = 0; j < n; ++j) sum += top[j];
+    B += fabs((double)w[h]) * sum;
+  }
+  return B;
+}
+
 /* The same score on the FP8 variant's exact values (fp64, rounded once). */
 int orc_logits_fp8(const uint8_t *q_fp8, const float *q_scale, const float *w, int64_t n_rows, int32_t n_heads,
                    const int32_t *indptr, int32_t n_reqs, const int32_t *row_ctx, const int32_t *block_table,
                    int32_t bt_stride, const uint8_t *pool, int64_t num_pages, float *logits, int64_t logits_stride,
-                   double *logits_f64, double *tol_ref, double *abs_ref) {
+                   double *logits_f64, double *tol_ref, double *abs_ref, double *top16_ref /* optional */) {
   int rc = check_logits_args(n_rows, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride, num_pages,
                              logits_stride);
   if (rc) return rc;
@@ -631,6 +660,7 @@ int orc_logits_fp8(const uint8_t *q_fp8, const float *q_scale, const float *w, i
       if (logits_f64) logits_f64[t * logits_stride + s] = L;
       if (tol_ref) tol_ref[t * logits_stride + s] = T;
       if (abs_ref) abs_ref[t * logits_stride + s] = A;
+      if (top16_ref) top16_ref[t * logits_stride + s] = top16_scale(qd, w + t * n_heads, n_heads, kd);
     }
     free(qd);
   }
@@ -640,7 +670,8 @@ int orc_logits_fp8(const uint8_t *q_fp8, const float *q_scale, const float *w, i
 int orc_logits_fp8_sampled(const uint8_t *q_fp8, const float *q_scale, const float *w, int32_t n_heads,
                            const int32_t *indptr, int32_t n_reqs, const int32_t *block_table, int32_t bt_stride,
                            const uint8_t *pool, int64_t num_pages, int64_t n_samples, const int64_t *rows,
-                           const int64_t *toks, double *out, double *tol_ref, double *abs_ref) {
+                           const int64_t *toks, double *out, double *tol_ref, double *abs_ref,
+                           double *top16_ref /* optional */) {
   if (n_heads <= 0 || n_samples < 0) return -1;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
@@ -655,6 +686,7 @@ int orc_logits_fp8_sampled(const uint8_t *q_fp8, const float *q_scale, const flo
     for (int h = 0; h < n_heads; ++h) orc_dequant_fp8_128(q_fp8 + (t * n_heads + h) * D, q_scale[t * n_heads + h], qd + h * D);
     dequant_token_fp8(pool, page, (int)(s % PAGE), kd);
     out[i] = score_one(qd, w + t * n_heads, n_heads, kd, &tol_ref[i], &abs_ref[i]);
+    if (top16_ref) top16_ref[i] = top16_scale(qd, w + t * n_heads, n_heads, kd);
     free(qd);
   }
   return bad ? -2 : 0;

@@ -105,7 +105,7 @@ int check_logits(int64_t n_rows, int32_t n_heads, int32_t n_reqs, int32_t bt_str
     return FP4IDX_E_INVALID;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
   if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
-  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows || n_reqs > 65535 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
   if (num_pages == 0) return FP4IDX_E_INVALID;
   return FP4IDX_OK;
@@ -192,7 +192,7 @@ int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const f
   if (n_heads != 16 && n_heads != 32 && n_heads != 64) return FP4IDX_E_INVALID;
   if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;
   if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > FP4IDX_FUSED_MAX_CTX) return FP4IDX_E_INVALID;
-  if (max_rows_per_req > n_rows || n_reqs > 65535) return FP4IDX_E_INVALID;
+  if (max_rows_per_req > n_rows || n_reqs > 65535 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
   if (max_rows_per_req < 1) return FP4IDX_E_INVALID;  // every row's k outputs are written
   if (max_ctx > 0 && num_pages == 0) return FP4IDX_E_INVALID;
@@ -202,7 +202,7 @@ int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const f
   if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16)) return FP4IDX_E_INVALID;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
-  return launched(fp4idx::launch_mqa_logits_topk(q_fp4, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+  return launched(fp4idx::launch_mqa_logits_topk(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len,
                                                  block_table, bt_stride, payload, scale, num_pages, k, out_idx,
                                                  max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }
@@ -333,7 +333,7 @@ int fp4idx_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const floa
   if (!aligned(q_fp8, 16) || !aligned(q_scale, 4) || !aligned(w, 16) || !aligned(pool, 16)) return FP4IDX_E_INVALID;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
-  return launched(fp4idx::launch_mqa_logits_fp8(q_fp8, q_scale, w, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+  return launched(fp4idx::launch_mqa_logits_fp8(q_fp8, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len,
                                                 block_table, bt_stride, pool, num_pages, logits, logits_stride,
                                                 max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
 }

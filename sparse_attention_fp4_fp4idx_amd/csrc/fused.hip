@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kFusedThreads) void mqa_logits_topk_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr, const int32_t* __restrict__ row_ctx,
     const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale, int64_t num_pages, int32_t bt_stride,
     const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale, const float* __restrict__ w, int k,
-    int32_t* __restrict__ out_idx) {
+    int32_t* __restrict__ out_idx, int32_t n_rows) {
   using FMT = Fp4Split;
   constexpr int NT = kFusedThreads;
   constexpr int H = NMT * 16;
@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kFusedThreads) void mqa_logits_topk_kernel(
   const int req = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ip0 = indptr[req], ip1 = indptr[req + 1];
+  // the request's rows, kept inside [0, n_rows) whatever indptr holds
+  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
   const int64_t row = (int64_t)ip0 + blockIdx.x;
   if (row >= ip1) return;
   // a context length beyond the table or the LDS row is cut to what both hold
@@ -118,10 +119,10 @@ template <int NMT, int J>
 static hipError_t launch_fused_j(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, const int32_t* indptr,
                                  int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
                                  const uint8_t* payload, const uint8_t* scale, int64_t num_pages, int32_t k,
-                                 int32_t* out_idx, int32_t max_rows_per_req, hipStream_t stream) {
+                                 int32_t* out_idx, int32_t max_rows_per_req, int32_t n_rows, hipStream_t stream) {
   return launch(mqa_logits_topk_kernel<NMT, J>, dim3((unsigned)max_rows_per_req, (unsigned)n_reqs),
                 dim3(kFusedThreads), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride,
-                q_fp4, q_scale, w, k, out_idx);
+                q_fp4, q_scale, w, k, out_idx, n_rows);
 }
 
 template <int NMT>
@@ -129,40 +130,40 @@ static hipError_t launch_fused_nmt(const uint8_t* q_fp4, const uint8_t* q_scale,
                                    const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                                    const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                                    const uint8_t* scale, int64_t num_pages, int32_t k, int32_t* out_idx,
-                                   int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+                                   int32_t max_rows_per_req, int64_t max_ctx, int32_t n_rows, hipStream_t stream) {
   // J slots per thread cover the longest row (J * 1024 >= max_ctx)
   if (max_ctx <= 1024)
     return launch_fused_j<NMT, 1>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                  num_pages, k, out_idx, max_rows_per_req, stream);
+                                  num_pages, k, out_idx, max_rows_per_req, n_rows, stream);
   if (max_ctx <= 4096)
     return launch_fused_j<NMT, 4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                  num_pages, k, out_idx, max_rows_per_req, stream);
+                                  num_pages, k, out_idx, max_rows_per_req, n_rows, stream);
   if (max_ctx <= 8192)
     return launch_fused_j<NMT, 8>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                  num_pages, k, out_idx, max_rows_per_req, stream);
+                                  num_pages, k, out_idx, max_rows_per_req, n_rows, stream);
   if (max_ctx <= 16384)
     return launch_fused_j<NMT, 16>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,
-                                   scale, num_pages, k, out_idx, max_rows_per_req, stream);
+                                   scale, num_pages, k, out_idx, max_rows_per_req, n_rows, stream);
   return launch_fused_j<NMT, 32>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, stream);
+                                 num_pages, k, out_idx, max_rows_per_req, n_rows, stream);
 }
 
-hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
+hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int n_heads,
                                   const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                                   const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                                   const uint8_t* scale, int64_t num_pages, int32_t k, int32_t* out_idx,
                                   int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
-  if (max_ctx > kFusedMaxCtx || max_rows_per_req > 0x7FFFFFFF || n_reqs > 65535) return hipErrorInvalidConfiguration;
+  if (max_ctx > kFusedMaxCtx || n_rows > 0x7FFFFFFFLL || n_reqs > 65535) return hipErrorInvalidConfiguration;
   switch (n_heads) {
     case 16:
       return launch_fused_nmt<1>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, stream);
+                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
     case 32:
       return launch_fused_nmt<2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, stream);
+                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
     case 64:
       return launch_fused_nmt<4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, stream);
+                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
     default:
       return hipErrorInvalidValue;
   }

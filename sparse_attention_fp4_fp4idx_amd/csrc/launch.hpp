@@ -67,7 +67,7 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);
 
-hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int n_heads,
+hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int64_t n_rows, int n_heads,
                                  const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                                  const int32_t* block_table, int32_t bt_stride, const uint8_t* pool,
                                  int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
@@ -76,7 +76,7 @@ hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, con
 // Longest row the fused logits + top-k kernel holds (its LDS row).
 constexpr int64_t kFusedMaxCtx = 32768;
 
-hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int n_heads,
+hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int n_heads,
                                   const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                                   const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                                   const uint8_t* scale, int64_t num_pages, int32_t k, int32_t* out_idx,

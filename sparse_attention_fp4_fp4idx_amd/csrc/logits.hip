@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
     int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
-    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride) {
+    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t n_rows) {
   static_assert(RW >= 1 && RW <= 4, "rows per wave");
   static_assert(PPW % D == 0 && PPW <= 64, "pages per wave: a multiple of the prefetch depth, one id per lane");
   constexpr int H = NMT * 16;
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   const int32_t* bt = block_table + (int64_t)req * bt_stride;
   const int32_t my_pid = bt[min(page_begin + (lane % PPW), bt_stride - 1)];
   __builtin_amdgcn_sched_barrier(0);  // keep the load issued ahead of the indptr wait
-  const int ip0 = indptr[req], ip1 = indptr[req + 1];
+  // the request's rows, kept inside [0, n_rows) whatever indptr holds
+  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
   const int row0 = ip0 + grp * RW;
   const int row_end = ip1;
   const int nrows = max(0, min(RW, row_end - row0));
@@ -275,7 +276,8 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
     int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
-    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t chunk_pages) {
+    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t chunk_pages,
+    int32_t n_rows) {
   constexpr int NT = NW * 64;
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
   const int lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
 
-  const int ip0 = indptr[req], ip1 = indptr[req + 1];
+  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
   const int row0 = ip0 + (int)blockIdx.y * ROWS;
   const int nrows = max(0, min(ROWS, ip1 - row0));
   if (nrows == 0) return;  // the whole work-group
@@ -385,99 +387,86 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
   }
 }
 
+// The arguments of one logits call, as the launchers pass them down.
+struct LogitsCall {
+  const uint8_t* q;
+  const uint8_t* q_scale;
+  const float* w;
+  const int32_t* indptr;
+  int32_t n_reqs;
+  int32_t n_rows;
+  const int32_t* row_ctx;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const uint8_t* payload;
+  const uint8_t* scale;
+  int64_t num_pages;
+  float* logits;
+  int64_t logits_stride;
+  int32_t max_rows_per_req;
+  int64_t max_ctx;
+  hipStream_t stream;
+};
+
 template <int NW, int RW, int NMT>
-static hipError_t launch_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
-                                int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
-                                int32_t bt_stride, const uint8_t* payload, const uint8_t* scale, int64_t num_pages,
-                                float* logits, int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx,
-                                int page_rows, hipStream_t stream) {
+static hipError_t launch_shared(const LogitsCall& c, int page_rows) {
   constexpr int ROWS = NW * RW;
-  const int64_t pages = (max_ctx + 63) / 64;
-  const int64_t blocks = (max_rows_per_req + ROWS - 1) / ROWS;
-  if (pages == 0 || blocks == 0 || n_reqs == 0) return hipSuccess;
-  if (blocks > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
+  const int64_t pages = (c.max_ctx + 63) / 64;
+  const int64_t blocks = (c.max_rows_per_req + ROWS - 1) / ROWS;
+  if (pages == 0 || blocks == 0 || c.n_reqs == 0) return hipSuccess;
+  if (blocks > 65535 || c.n_reqs > 65535) return hipErrorInvalidConfiguration;
   // Page chunks: at least about two waves for each of the 1,024 SIMDs, and
   // no work-group longer than about page_rows page-rows per wave (a
   // request's block whose rows are long must not become the critical path:
   // the hardware balances many short work-groups across the CUs), and not
   // shorter than 8 pages (a work-group's set-up is paid per chunk).
   const int64_t want = 2048 / NW;
-  int64_t chunks = (want + n_reqs * blocks - 1) / (n_reqs * blocks);
+  int64_t chunks = (want + c.n_reqs * blocks - 1) / (c.n_reqs * blocks);
   chunks = std::max<int64_t>(chunks, (pages * RW + page_rows - 1) / page_rows);
   chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, (pages + 7) / 8));
   int64_t chunk_pages = std::min<int64_t>((pages + chunks - 1) / chunks, kSharedMaxChunk);
   chunks = (pages + chunk_pages - 1) / chunk_pages;
   if (chunks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  return launch(mqa_logits_shared_kernel<NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)n_reqs),
-                dim3(NW * 64), 0, stream, block_table, indptr, row_ctx, payload, scale, num_pages, bt_stride, q,
-                q_scale, w, logits, logits_stride, (int32_t)chunk_pages);
+  return launch(mqa_logits_shared_kernel<NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)c.n_reqs),
+                dim3(NW * 64), 0, c.stream, c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages,
+                c.bt_stride, c.q, c.q_scale, c.w, c.logits, c.logits_stride, (int32_t)chunk_pages, c.n_rows);
 }
 
 template <typename FMT, int RW, int NMT, int PPW, int D>
-static hipError_t launch_rw(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
-                            int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
-                            const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
-                            int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
-  const int64_t pages = (max_ctx + 63) / 64;
+static hipError_t launch_rw(const LogitsCall& c) {
+  const int64_t pages = (c.max_ctx + 63) / 64;
   const int64_t n_chunks = (pages + 4 * PPW - 1) / (4 * PPW);
-  const int64_t n_groups = (max_rows_per_req + RW - 1) / RW;
-  if (n_chunks == 0 || n_groups == 0 || n_reqs == 0) return hipSuccess;
-  if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || n_reqs > 65535) return hipErrorInvalidConfiguration;
+  const int64_t n_groups = (c.max_rows_per_req + RW - 1) / RW;
+  if (n_chunks == 0 || n_groups == 0 || c.n_reqs == 0) return hipSuccess;
+  if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || c.n_reqs > 65535) return hipErrorInvalidConfiguration;
   return launch(mqa_logits_kernel<FMT, RW, NMT, PPW, D>,
-                dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)n_reqs), dim3(256), 0, stream, block_table,
-                indptr, row_ctx, payload, scale, num_pages, bt_stride, q, q_scale, w, logits, logits_stride);
+                dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)c.n_reqs), dim3(256), 0, c.stream,
+                c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride, c.q, c.q_scale, c.w,
+                c.logits, c.logits_stride, c.n_rows);
 }
 
 template <typename FMT, int NMT>
-static hipError_t launch_nmt(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
-                             int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table, int32_t bt_stride,
-                             const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
-                             int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+static hipError_t launch_nmt(const LogitsCall& c) {
   constexpr int cap = NMT == 8 ? FMT::kRowsCapWide : FMT::kRowsCap;
-  if (max_rows_per_req <= 1)
-    return launch_rw<FMT, 1, NMT, FMT::kPpw1, FMT::kD1>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
-                                                        bt_stride, payload, scale, num_pages, logits, logits_stride,
-                                                        max_rows_per_req, max_ctx, stream);
+  const int r = c.max_rows_per_req;
+  if (r <= 1) return launch_rw<FMT, 1, NMT, FMT::kPpw1, FMT::kD1>(c);
   if constexpr (cap <= 2) {
-    return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
-                                                        bt_stride, payload, scale, num_pages, logits, logits_stride,
-                                                        max_rows_per_req, max_ctx, stream);
+    return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(c);
   } else {
-    if (max_rows_per_req == 2)
-      return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
-                                                          bt_stride, payload, scale, num_pages, logits, logits_stride,
-                                                          max_rows_per_req, max_ctx, stream);
-    if (max_rows_per_req == 3 || max_rows_per_req == 6)
-      return launch_rw<FMT, 3, NMT, FMT::kPpwMany, FMT::kDMany>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
-                                                                bt_stride, payload, scale, num_pages, logits,
-                                                                logits_stride, max_rows_per_req, max_ctx, stream);
-    return launch_rw<FMT, 4, NMT, FMT::kPpwMany, FMT::kDMany>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table,
-                                                              bt_stride, payload, scale, num_pages, logits,
-                                                              logits_stride, max_rows_per_req, max_ctx, stream);
+    if (r == 2) return launch_rw<FMT, 2, NMT, FMT::kPpw2, FMT::kD2>(c);
+    if (r == 3 || r == 6) return launch_rw<FMT, 3, NMT, FMT::kPpwMany, FMT::kDMany>(c);
+    return launch_rw<FMT, 4, NMT, FMT::kPpwMany, FMT::kDMany>(c);
   }
 }
 
 template <typename FMT>
-static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const float* w, int n_heads,
-                               const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
-                               const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
-                               const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
-                               int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+static hipError_t launch_heads(const LogitsCall& c, int n_heads) {
   switch (n_heads) {
-    case 16:
-      return launch_nmt<FMT, 1>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 32:
-      return launch_nmt<FMT, 2>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 64:
-      return launch_nmt<FMT, 4>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    case 128:
-      return launch_nmt<FMT, 8>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
-    default:
-      return hipErrorInvalidValue;
+    case 16: return launch_nmt<FMT, 1>(c);
+    case 32: return launch_nmt<FMT, 2>(c);
+    case 64: return launch_nmt<FMT, 4>(c);
+    case 128: return launch_nmt<FMT, 8>(c);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -494,22 +483,14 @@ static hipError_t launch_heads(const uint8_t* q, const uint8_t* q_scale, const f
 // requests of 1-16 rows over 8k-32k tokens: 76 us, against 85 us with 4 x 3
 // and 32 page-rows and 111 us with the near-uniform shape and chunks).
 template <int NMT>
-static hipError_t launch_fp4_shared(const uint8_t* q, const uint8_t* q_scale, const float* w, const int32_t* indptr,
-                                    int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
-                                    int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
-                                    int64_t num_pages, float* logits, int64_t logits_stride,
-                                    int32_t max_rows_per_req, int64_t max_ctx, bool uniform, hipStream_t stream) {
+static hipError_t launch_fp4_shared(const LogitsCall& c, bool uniform) {
   const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 4;
-#define FP4IDX_SHARED(NW, RW)                                                                                       \
-  launch_shared<NW, RW, NMT>(q, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,       \
-                             num_pages, logits, logits_stride, max_rows_per_req, max_ctx, page_rows, stream)
-  const int r = max_rows_per_req;
-  if (!uniform || r <= 4) return FP4IDX_SHARED(2, 2);
+  const int r = c.max_rows_per_req;
+  if (!uniform || r <= 4) return launch_shared<2, 2, NMT>(c, page_rows);
   if constexpr (NMT != 8) {
-    if (r <= 6) return FP4IDX_SHARED(2, 3);
+    if (r <= 6) return launch_shared<2, 3, NMT>(c, page_rows);
   }
-  return FP4IDX_SHARED(4, 2);
-#undef FP4IDX_SHARED
+  return launch_shared<4, 2, NMT>(c, page_rows);
 }
 
 hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
@@ -517,6 +498,10 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
                              const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
                              const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
                              int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+  if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const LogitsCall c{q_fp4,       q_scale,   w,       indptr,    n_reqs,    (int32_t)n_rows, row_ctx,
+                     block_table, bt_stride, payload, scale,     num_pages, logits,          logits_stride,
+                     max_rows_per_req, max_ctx, stream};
   // The shared-page kernel splits a request's rows among a work-group's
   // waves and stages each page once for all of them; the per-wave kernel
   // splits pages instead and reads each page once per wave.  Shared pages
@@ -526,33 +511,26 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
   // largest.  Both kernels give the same bits.
   const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
   const int64_t avg_rows = n_reqs > 0 ? (n_rows + n_reqs - 1) / n_reqs : 0;
-  if (max_rows_per_req <= 2 || avg_rows < 3)
-    return launch_heads<Fp4Split>(q_fp4, q_scale, w, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride,
-                                  payload, scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, stream);
+  if (max_rows_per_req <= 2 || avg_rows < 3) return launch_heads<Fp4Split>(c, n_heads);
   switch (n_heads) {
-#define FP4IDX_HEADS(H, NMT)                                                                                        \
-  case H:                                                                                                           \
-    return launch_fp4_shared<NMT>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload,     \
-                                  scale, num_pages, logits, logits_stride, max_rows_per_req, max_ctx, uniform,     \
-                                  stream);
-    FP4IDX_HEADS(16, 1)
-    FP4IDX_HEADS(32, 2)
-    FP4IDX_HEADS(64, 4)
-    FP4IDX_HEADS(128, 8)
-#undef FP4IDX_HEADS
-    default:
-      return hipErrorInvalidValue;
+    case 16: return launch_fp4_shared<1>(c, uniform);
+    case 32: return launch_fp4_shared<2>(c, uniform);
+    case 64: return launch_fp4_shared<4>(c, uniform);
+    case 128: return launch_fp4_shared<8>(c, uniform);
+    default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int n_heads,
-                                 const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int64_t n_rows,
+                                 int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                                  const int32_t* block_table, int32_t bt_stride, const uint8_t* pool,
                                  int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
                                  int64_t max_ctx, hipStream_t stream) {
-  return launch_heads<Fp8Fused>(q_fp8, reinterpret_cast<const uint8_t*>(q_scale), w, n_heads, indptr, n_reqs,
-                                row_ctx, block_table, bt_stride, pool, pool, num_pages, logits, logits_stride,
-                                max_rows_per_req, max_ctx, stream);
+  if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const LogitsCall c{q_fp8,       reinterpret_cast<const uint8_t*>(q_scale), w, indptr, n_reqs, (int32_t)n_rows,
+                     row_ctx,     block_table, bt_stride, pool, pool, num_pages, logits, logits_stride,
+                     max_rows_per_req, max_ctx, stream};
+  return launch_heads<Fp8Fused>(c, n_heads);
 }
 
 }  // namespace fp4idx

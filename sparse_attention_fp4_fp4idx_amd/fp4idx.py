@@ -139,6 +139,17 @@ _U8 = (torch.uint8,)
 _F32 = (torch.float32,)
 
 
+def _need(ok: bool, what: str, msg: str) -> None:
+    if not ok:
+        raise Fp4idxError(f"{what}: {msg}")
+
+
+def _shape(t: torch.Tensor, shape, what: str, name: str) -> None:
+    """t must have exactly this shape (a buffer the kernels index by these sizes)."""
+    _need(tuple(t.shape) == tuple(int(x) for x in shape), what,
+          f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+
+
 def _pitch(t: torch.Tensor) -> int:
     """Elements between consecutive rows (dim 0).  With a single row any
     stride is valid for dim 0 (numpy and torch may report 0 for an inserted
@@ -162,8 +173,10 @@ def _write_k_args(k, pos, slot, norm_w, eps, cos_sin, payload, scale):
             and cos_sin.is_contiguous() and norm_w.is_contiguous()):
         raise Fp4idxError("write_k: pos, slot, norm_w, cos_sin and the pools must be contiguous")
     n = int(k.shape[0])
+    _need(k.dim() == 2 and (n == 0 or k.shape[1] >= HEAD_DIM), "write_k", "k must be [N, >=128]")
     if pos.numel() != n or slot.numel() != n:
         raise Fp4idxError("write_k: pos/slot length must equal the number of K rows")
+    _need(norm_w.numel() == HEAD_DIM, "write_k", "norm_w must hold 128 values")
     num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
     if payload.numel() != num_pages * PAYLOAD_PAGE_BYTES or scale.numel() != num_pages * SCALE_PAGE_BYTES:
         raise Fp4idxError("write_k: pool sizes must be num_pages*4096 and num_pages*256 bytes")
@@ -180,8 +193,10 @@ def _write_k_fp8_args(k, pos, slot, norm_w, eps, cos_sin, pool):
             and norm_w.is_contiguous()):
         raise Fp4idxError("write_k_fp8: pos, slot, norm_w, cos_sin and the pool must be contiguous")
     n = int(k.shape[0])
+    _need(k.dim() == 2 and (n == 0 or k.shape[1] >= HEAD_DIM), "write_k_fp8", "k must be [N, >=128]")
     if pos.numel() != n or slot.numel() != n:
         raise Fp4idxError("write_k_fp8: pos/slot length must equal the number of K rows")
+    _need(norm_w.numel() == HEAD_DIM, "write_k_fp8", "norm_w must hold 128 values")
     num_pages = pool.numel() // FP8_PAGE_BYTES
     if pool.numel() != num_pages * FP8_PAGE_BYTES:
         raise Fp4idxError("write_k_fp8: the pool must be num_pages*8448 bytes")
@@ -210,12 +225,18 @@ def _pack_q_args(q, pos, cos_sin, w_in, w_scale, q_out, q_scale, w_out, with_tab
     if q.dim() != 3 or q.shape[2] != HEAD_DIM or (T and (q.stride(2) != 1 or q.stride(1) != HEAD_DIM)):
         raise Fp4idxError(f"{what}: q must be [T, H, 128] with heads packed inside a row")
     dev = q.device
-    if fp8:
-        q_out = q_out if q_out is not None else torch.empty((T, H, HEAD_DIM), dtype=torch.uint8, device=dev)
-        q_scale = q_scale if q_scale is not None else torch.empty((T, H), dtype=torch.float32, device=dev)
-    else:
-        q_out = q_out if q_out is not None else torch.empty((T, H, 64), dtype=torch.uint8, device=dev)
-        q_scale = q_scale if q_scale is not None else torch.empty((T, H, 4), dtype=torch.uint8, device=dev)
+    code_shape = (T, H, HEAD_DIM) if fp8 else (T, H, 64)
+    scale_shape = (T, H) if fp8 else (T, H, 4)
+    _need(pos.numel() == T, what, f"pos must hold one position per row ({T})")
+    _shape(w_in, (T, H), what, "w_in")
+    if with_table:
+        _need(cos_sin.dim() == 2 and cos_sin.shape[1] == ROPE_DIM, what, "cos_sin must be [max_pos, 64]")
+    for t, shp, name in ((q_out, code_shape, "q codes"), (q_scale, scale_shape, "q_scale"), (w_out, (T, H), "w_out")):
+        if t is not None:
+            _shape(t, shp, what, name)
+    q_out = q_out if q_out is not None else torch.empty(code_shape, dtype=torch.uint8, device=dev)
+    q_scale = q_scale if q_scale is not None else torch.empty(
+        scale_shape, dtype=torch.float32 if fp8 else torch.uint8, device=dev)
     w_out = w_out if w_out is not None else torch.empty((T, H), dtype=torch.float32, device=dev)
     for t, name in ((pos, "pos"), (w_in, "w_in"), (q_out, "q codes"), (q_scale, "q_scale"), (w_out, "w_out"),
                     (cos_sin, "cos_sin")):
@@ -271,8 +292,38 @@ def prepare_write_k_pack_q(k, pos_k, slot, norm_w, eps, cos_sin, payload, scale,
     return Prepared("fp4idx_write_k_pack_q", args, keep=keep), outs
 
 
+def _check_logits_shapes(what, q, q_scale, w, indptr, row_ctx, block_table, max_ctx, out, code_bytes, scale_tail):
+    """Sizes the logits kernels index by: Q codes [T, H, code_bytes], Q scales
+    [T, H, *scale_tail], w [T, H], indptr [n_reqs + 1], row_ctx [T], a block
+    table of at least n_reqs rows and ceil(max_ctx / 64) columns, and (when
+    given) an output of at least T rows and max_ctx columns."""
+    _need(q.dim() == 3 and q.shape[2] == code_bytes, what, f"Q codes must be [T, H, {code_bytes}]")
+    T, H = int(q.shape[0]), int(q.shape[1])
+    _shape(q_scale, (T, H) + tuple(scale_tail), what, "q_scale")
+    _shape(w, (T, H), what, "w")
+    _need(indptr.dim() == 1 and indptr.numel() >= 1, what, "req_row_indptr must be [n_reqs + 1]")
+    n_reqs = int(indptr.numel()) - 1
+    _need(row_ctx.numel() == T, what, f"row_ctx must hold one context length per row ({T})")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= n_reqs, what,
+          f"block_table must be [n_reqs, stride] with at least {n_reqs} rows")
+    _need(int(max_ctx) >= 0 and block_table.shape[1] * PAGE_TOKENS >= int(max_ctx), what,
+          f"block_table has {block_table.shape[1]} columns, max_ctx {max_ctx} needs {(int(max_ctx) + 63) // 64}")
+    if out is not None:
+        _need(out.dim() == 2 and out.shape[0] >= T and out.shape[1] >= int(max_ctx), what,
+              f"the output must be [>= {T}, >= {max_ctx}], got {tuple(out.shape)}")
+
+
+def _split_pool_pages(what, payload, scale) -> int:
+    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    _need(payload.numel() == num_pages * PAYLOAD_PAGE_BYTES and scale.numel() == num_pages * SCALE_PAGE_BYTES,
+          what, "pool sizes must be num_pages*4096 and num_pages*256 bytes")
+    return num_pages
+
+
 def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, max_rows_per_req,
                      max_ctx, logits, stream):
+    _check_logits_shapes("mqa_logits", q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, max_ctx, logits,
+                         64, (4,))
     T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
     n_reqs = int(req_row_indptr.numel()) - 1
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -285,7 +336,7 @@ def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, pa
                     (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale")):
         if not t.is_contiguous():
             raise Fp4idxError(f"mqa_logits: {name} must be contiguous")
-    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    num_pages = _split_pool_pages("mqa_logits", payload, scale)
     args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
             _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
@@ -315,17 +366,21 @@ def prepare_mqa_logits(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, 
 
 def _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, k,
                           max_rows_per_req, max_ctx, out_idx, stream):
+    _check_logits_shapes("mqa_logits_topk", q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, max_ctx, None,
+                         64, (4,))
     T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
     n_reqs = int(req_row_indptr.numel()) - 1
     if block_table.dim() != 2 or block_table.stride(1) != 1:
         raise Fp4idxError("mqa_logits_topk: block_table must be [n_reqs, stride] with unit inner stride")
+    if out_idx is not None:
+        _shape(out_idx, (T, int(k)), "mqa_logits_topk", "out_idx")
     if out_idx is None:
         out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=q_fp4.device)
     for t, name in ((q_fp4, "q_fp4"), (q_scale, "q_scale"), (w, "w"), (req_row_indptr, "indptr"),
                     (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale"), (out_idx, "out_idx")):
         if not t.is_contiguous():
             raise Fp4idxError(f"mqa_logits_topk: {name} must be contiguous")
-    num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
+    num_pages = _split_pool_pages("mqa_logits_topk", payload, scale)
     args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
             _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
@@ -355,9 +410,14 @@ def prepare_mqa_logits_topk(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_ta
 
 
 def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
+    _need(logits.dim() == 2, "topk", "logits must be [T, stride]")
     T = int(logits.shape[0])
     if logits.stride(-1) != 1:
         raise Fp4idxError("topk: logits must have unit inner stride")
+    _need(row_ctx.numel() == T, "topk", f"row_ctx must hold one context length per row ({T})")
+    _need(0 <= int(max_ctx) <= logits.shape[1], "topk", f"max_ctx {max_ctx} exceeds the logits rows ({logits.shape[1]})")
+    if out_idx is not None:
+        _shape(out_idx, (T, int(k)), "topk", "out_idx")
     if out_idx is None:
         out_idx = torch.empty((T, int(k)), dtype=torch.int32, device=logits.device)
     if not out_idx.is_contiguous() or not row_ctx.is_contiguous():
@@ -390,6 +450,9 @@ def fp4idx_read_k(payload: torch.Tensor, scale: torch.Tensor, slot: torch.Tensor
     num_pages = payload.numel() // PAYLOAD_PAGE_BYTES
     if payload.numel() != num_pages * PAYLOAD_PAGE_BYTES or scale.numel() != num_pages * SCALE_PAGE_BYTES:
         raise Fp4idxError("read_k: pool sizes must be num_pages*4096 and num_pages*256 bytes")
+    if out is not None:
+        _need(out.dim() == 2 and out.shape[0] == n and out.shape[1] >= HEAD_DIM, "read_k",
+              f"out must be [{n}, >=128], got {tuple(out.shape)}")
     if out is None:
         out = torch.empty((n, HEAD_DIM), dtype=torch.float32, device=payload.device)
     _run("fp4idx_read_k", [_ptr(payload, _U8, "payload"), _ptr(scale, _U8, "scale"), num_pages,
@@ -501,6 +564,8 @@ def prepare_write_k_pack_q_fp8(k, pos_k, slot, norm_w, eps, cos_sin, pool, q, po
 
 def _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, pool, max_rows_per_req, max_ctx,
                          logits, stream):
+    _check_logits_shapes("mqa_logits_fp8", q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table, max_ctx, logits,
+                         HEAD_DIM, ())
     T, H = int(q_fp8.shape[0]), int(q_fp8.shape[1])
     n_reqs = int(req_row_indptr.numel()) - 1
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -514,6 +579,7 @@ def _mqa_logits_fp8_args(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_table
         if not t.is_contiguous():
             raise Fp4idxError(f"mqa_logits_fp8: {name} must be contiguous")
     num_pages = pool.numel() // FP8_PAGE_BYTES
+    _need(pool.numel() == num_pages * FP8_PAGE_BYTES, "mqa_logits_fp8", "the pool must be num_pages*8448 bytes")
     args = [_ptr(q_fp8, _U8, "q_fp8"), _ptr(q_scale, _F32, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
             _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(pool, _U8, "pool"), num_pages,

@@ -182,3 +182,95 @@ def test_binding_imports_no_oracle():
     assert "oracle" not in src.replace("no fallback", "")
     for f in os.listdir(os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc", f)).read().lower()
+
+
+def _logits_inputs(T=3, H=64, B=2, max_ctx=200, code=64, fp8=False):
+    import torch
+    q = torch.zeros((T, H, code), dtype=torch.uint8)
+    qs = torch.zeros((T, H), dtype=torch.float32) if fp8 else torch.zeros((T, H, 4), dtype=torch.uint8)
+    return dict(q=q, qs=qs, w=torch.zeros((T, H)), ind=torch.zeros(B + 1, dtype=torch.int32),
+                ctx=torch.zeros(T, dtype=torch.int32), bt=torch.zeros((B, (max_ctx + 63) // 64), dtype=torch.int32),
+                pay=torch.zeros(5 * 4096, dtype=torch.uint8), sc=torch.zeros(5 * 256, dtype=torch.uint8),
+                pool=torch.zeros(5 * 8448, dtype=torch.uint8), out=torch.zeros((T, max_ctx)),
+                idx=torch.zeros((T, 16), dtype=torch.int32))
+
+
+def _raises(F, fn, *words):
+    with pytest.raises(F.Fp4idxError) as e:
+        fn()
+    for w in words:
+        assert w in str(e.value), (w, str(e.value))
+
+
+def test_binding_checks_buffer_sizes_before_any_call(F):
+    """Every buffer the kernels index by T, H, k, n_reqs or num_pages is
+    checked against those sizes in the binding: a mismatch raises
+    Fp4idxError naming the buffer (host tensors: with every size right the
+    binding gets as far as asking for device memory)."""
+    import torch
+    d = _logits_inputs()
+
+    def logits(**kw):
+        a = dict(d, **kw)
+        return lambda: F.mqa_logits(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pay"], a["sc"], 2, 200,
+                                    logits=a["out"])
+    _raises(F, logits(), "device tensor")
+    _raises(F, logits(out=torch.zeros((2, 200))), "output")                 # fewer rows than T
+    _raises(F, logits(out=torch.zeros((3, 150))), "output")                 # rows shorter than max_ctx
+    _raises(F, logits(ctx=torch.zeros(2, dtype=torch.int32)), "row_ctx")
+    _raises(F, logits(bt=torch.zeros((1, 4), dtype=torch.int32)), "block_table")
+    _raises(F, logits(bt=torch.zeros((2, 3), dtype=torch.int32)), "block_table")  # 3 pages < 200 tokens
+    _raises(F, logits(w=torch.zeros((3, 32))), "w")
+    _raises(F, logits(qs=torch.zeros((3, 64, 3), dtype=torch.uint8)), "q_scale")
+    _raises(F, logits(q=torch.zeros((3, 64, 32), dtype=torch.uint8)), "Q codes")
+    _raises(F, logits(sc=torch.zeros(4 * 256, dtype=torch.uint8)), "pool sizes")
+
+    def fused(**kw):
+        a = dict(d, **kw)
+        return lambda: F.mqa_logits_topk(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pay"], a["sc"], 16,
+                                         2, 200, out_idx=a["idx"])
+    _raises(F, fused(), "device tensor")
+    _raises(F, fused(idx=torch.zeros((3, 8), dtype=torch.int32)), "out_idx")
+    _raises(F, fused(ctx=torch.zeros(4, dtype=torch.int32)), "row_ctx")
+
+    def topk(**kw):
+        a = dict(d, **kw)
+        return lambda: F.topk(a["out"], a["ctx"], 16, a.get("mc", 200), out_idx=a["idx"])
+    _raises(F, topk(), "device tensor")
+    _raises(F, topk(idx=torch.zeros((2, 16), dtype=torch.int32)), "out_idx")
+    _raises(F, topk(ctx=torch.zeros(5, dtype=torch.int32)), "row_ctx")
+    _raises(F, topk(mc=201), "max_ctx")
+
+    d8 = _logits_inputs(code=128, fp8=True)
+
+    def logits8(**kw):
+        a = dict(d8, **kw)
+        return lambda: F.mqa_logits_fp8(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pool"], 2, 200,
+                                        logits=a["out"])
+    _raises(F, logits8(), "device tensor")
+    _raises(F, logits8(qs=torch.zeros((3, 64, 4), dtype=torch.uint8)), "q_scale")
+    _raises(F, logits8(pool=torch.zeros(5 * 8448 + 1, dtype=torch.uint8)), "8448")
+    _raises(F, logits8(out=torch.zeros((3, 199))), "output")
+
+    # the encoders
+    q = torch.zeros((3, 64, 128), dtype=torch.bfloat16)
+    tab = torch.zeros((10, 64), dtype=torch.bfloat16)
+    pos = torch.zeros(3, dtype=torch.int32)
+    w = torch.zeros((3, 64))
+    _raises(F, lambda: F.pack_q(q, pos, tab, w), "device tensor")
+    _raises(F, lambda: F.pack_q(q, pos[:2], tab, w), "pos")
+    _raises(F, lambda: F.pack_q(q, pos, tab, w[:, :32]), "w_in")
+    _raises(F, lambda: F.pack_q(q, pos, tab, w, 1.0, torch.zeros((3, 64, 32), dtype=torch.uint8)), "q codes")
+    _raises(F, lambda: F.pack_q(q, pos, tab, w, 1.0, None, torch.zeros((3, 64), dtype=torch.uint8)), "q_scale")
+    _raises(F, lambda: F.pack_q(q, pos, tab, w, 1.0, None, None, torch.zeros((2, 64))), "w_out")
+    _raises(F, lambda: F.pack_q(q, pos, torch.zeros((10, 32), dtype=torch.bfloat16), w), "cos_sin")
+    _raises(F, lambda: F.pack_q_fp8(q, pos, tab, w, 1.0, None, torch.zeros((3, 64, 4), dtype=torch.float32)),
+            "q_scale")
+    k = torch.zeros((4, 128), dtype=torch.bfloat16)
+    kp, ks = torch.zeros(4, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)
+    nw = torch.zeros(128, dtype=torch.bfloat16)
+    _raises(F, lambda: F.write_k(k, kp, ks, nw, 1e-6, tab, d["pay"], d["sc"]), "device tensor")
+    _raises(F, lambda: F.write_k(k, kp, ks, nw[:64], 1e-6, tab, d["pay"], d["sc"]), "norm_w")
+    _raises(F, lambda: F.write_k(k[:, :100], kp, ks, nw, 1e-6, tab, d["pay"], d["sc"]), "k must be")
+    _raises(F, lambda: F.write_k(k, kp[:3], ks, nw, 1e-6, tab, d["pay"], d["sc"]), "pos/slot")
+    _raises(F, lambda: F.read_k(d["pay"], d["sc"], ks, out=torch.zeros((3, 128))), "out must be")

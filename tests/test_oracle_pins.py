@@ -425,6 +425,47 @@ def test_logits_integer_lut_formulation_agrees(orc):
             assert f64[t, s] == float(L)
 
 
+def _sample_pairs(rng, row_ctx, n):
+    """Random (row, token) pairs over rows with context, plus every such row's
+    first and last token and the tokens on both sides of each page boundary."""
+    live = np.nonzero(row_ctx > 0)[0]
+    rows = rng.choice(live, n)
+    toks = (rng.random(n) * row_ctx[rows]).astype(np.int64)
+    er, et = [], []
+    for t in live:
+        c = int(row_ctx[t])
+        for s in {0, c - 1, *[p for b in range(64, c, 64) for p in (b - 1, b)]}:
+            er.append(t); et.append(s)
+    return np.concatenate([rows, er]).astype(np.int64), np.concatenate([toks, et]).astype(np.int64)
+
+
+def test_sampled_logits_checker_equals_full_logits_and_brute_force(orc):
+    """orc_logits_sampled (the checker of the full-size GPU logits tests, which
+    finds each sample's request from the row and its page from the block
+    table) against orc_logits, which walks every row of every request, at
+    random (row, token) pairs of a multi-request paged problem with permuted
+    page ids and unequal row counts; and, on a subset, against the exact
+    rational L, T and A of the brute force read through the page shapes."""
+    rng = np.random.default_rng(23)
+    qf, qs, w, indptr, row_ctx, bt, pay, sc = _tiny_logit_problem(rng, H=4, ctx=(70, 200, 5, 130),
+                                                                   rows=(2, 1, 3, 2))
+    stride = 200
+    _, f64, tol, absr = orc.logits(qf, qs, w, indptr, row_ctx, bt, pay, sc, logits_stride=stride, want_f64=True)
+    rows, toks = _sample_pairs(rng, row_ctx, 300)
+    s64, sT, sA = orc.logits_sampled(qf, qs, w, indptr, bt, pay, sc, rows, toks)
+    assert np.array_equal(s64, f64[rows, toks])
+    assert np.array_equal(sT, tol[rows, toks]) and np.array_equal(sA, absr[rows, toks])
+    req = np.searchsorted(indptr, rows, side="right") - 1
+    for i in range(0, rows.size, 9):
+        t, s, b = int(rows[i]), int(toks[i]), int(req[i])
+        kc, ks = brute.pool_token(pay, sc, int(bt[b, s // 64]) * 64 + s % 64)
+        kv = brute.decode_vector(kc, ks)
+        qv = [brute.decode_vector(qf[t, h], qs[t, h]) for h in range(qf.shape[1])]
+        L, T, A = brute.logit_terms(qv, w[t], kv)
+        for got, want in ((s64[i], L), (sT[i], T), (sA[i], A)):
+            assert abs(got - float(want)) <= 1e-12 * abs(float(want)), (t, s)
+
+
 # ---------------------------------------------------------------- top-k
 
 def _ref_topk(vals, ctx, k):
@@ -622,3 +663,53 @@ def test_fp8_logits_against_exact_rational_brute_force(orc):
                          for h in range(H))
                 assert abs(f64[t, s] - float(ex)) <= 1e-12 * abs(float(ex)) + 1e-300
                 assert out[t, s] == np.float32(float(ex))
+
+
+def test_fp8_sampled_logits_checker_equals_full_logits_and_brute_force(orc):
+    """orc_logits_fp8_sampled (the checker of the full-size FP8 logits tests)
+    against orc_logits_fp8 at random (row, token) pairs of a multi-request
+    paged problem with permuted page ids, and on a subset against the exact
+    rational L, T and A through the fused page shape."""
+    rng = np.random.default_rng(87)
+    H = 3
+    rows_per = (2, 1, 3)
+    ctxs = (130, 64, 200)
+    indptr = np.concatenate([[0], np.cumsum(rows_per)]).astype(np.int32)
+    row_ctx = np.concatenate([[c] * r for c, r in zip(ctxs, rows_per)]).astype(np.int32)
+    row_ctx[4] = 150   # rows of one request with different contexts
+    pages = [(c + 63) // 64 for c in ctxs]
+    num_pages = sum(pages) + 2
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((3, max(pages)), -1, np.int32)
+    cur = 0
+    for b in range(3):
+        bt[b, :pages[b]] = perm[cur:cur + pages[b]]; cur += pages[b]
+    pool = np.zeros(num_pages * 8448, np.uint8)
+    pv = pool.reshape(num_pages, 8448)
+    codes = rng.integers(0, 256, (num_pages, 8192)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11
+    pv[:, :8192] = codes
+    pv[:, 8192:].view(np.float32)[:] = (2.0 ** rng.integers(-12, 4, (num_pages, 64))).astype(np.float32)
+    T = int(indptr[-1])
+    qf = rng.integers(0, 256, (T, H, 128)).astype(np.uint8); qf[(qf & 0x7F) == 0x7F] = 0x22
+    qs = (2.0 ** rng.integers(-6, 3, (T, H))).astype(np.float32)
+    w = rng.uniform(-1, 1, (T, H)).astype(np.float32)
+    _, f64, tol, absr, b16 = orc.logits_fp8(qf, qs, w, indptr, row_ctx, bt, pool, logits_stride=200,
+                                             want_f64=True, want_b16=True)
+    rows, toks = _sample_pairs(rng, row_ctx, 200)
+    s64, sT, sA, sB = orc.logits_fp8_sampled(qf, qs, w, indptr, bt, pool, rows, toks, want_b16=True)
+    assert np.array_equal(s64, f64[rows, toks])
+    assert np.array_equal(sT, tol[rows, toks]) and np.array_equal(sA, absr[rows, toks])
+    assert np.array_equal(sB, b16[rows, toks])
+    req = np.searchsorted(indptr, rows, side="right") - 1
+    for i in range(0, rows.size, 11):
+        t, s, b = int(rows[i]), int(toks[i]), int(req[i])
+        kc, ks = brute.fp8_pool_token(pool, int(bt[b, s // 64]) * 64 + s % 64)
+        kv = brute.fp8_decode(kc, ks)
+        qv = [brute.fp8_decode(qf[t, h], qs[t, h]) for h in range(H)]
+        L, Tt, A = brute.logit_terms(qv, w[t], kv)
+        # B16: per head the 16 largest |q_i k_i|, exactly
+        B = sum(abs(Fraction(float(w[t, h]))) * sum(sorted((abs(a * c) for a, c in zip(qv[h], kv)),
+                                                           reverse=True)[:16]) for h in range(H))
+        for got, want in ((s64[i], L), (sT[i], Tt), (sA[i], A), (sB[i], B)):
+            assert abs(got - float(want)) <= 1e-12 * abs(float(want)), (t, s)
