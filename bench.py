@@ -57,7 +57,7 @@ MFMA_FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 CACHE_BYTES = 256 << 20
 HEADLINE = 3
-NAMES = ("write_k", "pack_q", "mqa_logits", "topk")
+NAMES = ("write_k", "pack_q", "plan", "mqa_logits", "topk")
 
 
 def log(*a):
@@ -301,6 +301,7 @@ def main():
             for c in range(copies):
                 s = {n: (v if c == 0 else v.clone()) for n, v in base.items()}
                 s["logits"] = torch.empty((T, wl.max_ctx), dtype=torch.float32, device=dev)
+                s["ws"] = F.new_workspace(T, wl.n_reqs, wl.max_ctx, dev)
                 s["q_code"] = torch.empty((T, H, qcode_b), dtype=torch.uint8, device=dev)
                 s["q_scale"] = (torch.empty((T, H), dtype=torch.float32, device=dev) if fp8
                                 else torch.empty((T, H, 4), dtype=torch.uint8, device=dev))
@@ -313,9 +314,12 @@ def main():
 
             def step(s, strm, ev=None):
                 """One pass of the path on stream strm.  The timed steps encode
-                the step's K tokens and query rows in one launch; the kernel
-                pass (ev given) launches the two encoders separately so that
-                each kernel gets its own duration."""
+                the step's K tokens and query rows in one launch and the FP4
+                logits as one call (its schedule, then the scheduled kernel);
+                the kernel pass (ev given) launches the two encoders, and the
+                schedule and the logits kernel, separately so that each kernel
+                gets its own duration, and times the host-bounded logits call
+                after the step for comparison."""
                 def arm(i):   # events stamped with kernel i's own start / end (hipExtLaunchKernel)
                     if ev is not None:
                         F.time_next_call(ev[i][0], ev[i][1])
@@ -330,16 +334,31 @@ def main():
                     arm(1)
                     (F.pack_q_fp8 if fp8 else F.pack_q)(s["q"], pos_q, tab, s["w"], wl.w_scale, s["q_code"],
                                                         s["q_scale"], s["w_out"], stream=strm)
-                arm(2)
                 if fused:
+                    arm(3)
                     F.mqa_logits_topk(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt, *pool_args(s), k,
                                       wl.max_rows_per_req, wl.max_ctx, out_idx=s["top"], stream=strm)
                     return
-                (F.mqa_logits_fp8 if fp8 else F.mqa_logits)(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt,
-                                                            *pool_args(s), wl.max_rows_per_req, wl.max_ctx,
-                                                            logits=s["logits"], stream=strm)
-                arm(3)
+                if fp8:
+                    arm(3)
+                    F.mqa_logits_fp8(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt, *pool_args(s),
+                                     wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=strm)
+                elif ev is None:
+                    F.mqa_logits(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt, *pool_args(s),
+                                 logits=s["logits"], workspace=s["ws"], stream=strm)
+                else:
+                    plan = F.LogitsPlan(H, indptr, ctx, wl.max_ctx, workspace=s["ws"], stream=strm)
+                    arm(2)
+                    plan.build()
+                    arm(3)
+                    plan.run(s["q_code"], s["q_scale"], s["w_out"], bt, *pool_args(s), logits=s["logits"],
+                             stream=strm)
+                arm(4)
                 F.topk(s["logits"], ctx, k, wl.max_ctx, out_idx=s["top"], stream=strm)
+                if ev is not None and not fp8:
+                    arm(5)
+                    F.mqa_logits_bounded(s["q_code"], s["q_scale"], s["w_out"], indptr, ctx, bt, *pool_args(s),
+                                         wl.max_rows_per_req, wl.max_ctx, logits=s["logits"], stream=strm)
 
             for i in range(args.warmup):
                 step(sets[i % copies], stream)
@@ -365,9 +384,14 @@ def main():
                                                           out_idx=s_["top"], stream=stream)
                         pt = lambda: None  # noqa: E731
                     else:
-                        pl, _ = (F.prepare_mqa_logits_fp8 if fp8 else F.prepare_mqa_logits)(
-                            s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt, *pool_args(s_),
-                            wl.max_rows_per_req, wl.max_ctx, logits=s_["logits"], stream=stream)
+                        if fp8:
+                            pl, _ = F.prepare_mqa_logits_fp8(s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx,
+                                                             bt, *pool_args(s_), wl.max_rows_per_req, wl.max_ctx,
+                                                             logits=s_["logits"], stream=stream)
+                        else:
+                            pl, _ = F.prepare_mqa_logits(s_["q_code"], s_["q_scale"], s_["w_out"], indptr, ctx, bt,
+                                                         *pool_args(s_), logits=s_["logits"], workspace=s_["ws"],
+                                                         stream=stream)
                         pt, _ = F.prepare_topk(s_["logits"], ctx, k, wl.max_ctx, out_idx=s_["top"], stream=stream)
 
                     def run(pw=pw, pl=pl, pt=pt):
@@ -389,16 +413,18 @@ def main():
 
             # kernel durations: the same K steps launched eagerly, each kernel carrying
             # HIP events its own dispatch stamps (no marker packets in between)
-            evs = [event_pairs(len(NAMES)) for _ in range(args.steps)]
+            evs = [event_pairs(len(NAMES) + 1) for _ in range(args.steps)]
             torch.cuda.synchronize()
             for i in range(args.steps):
                 step(sets[i % copies], stream, evs[i])
             torch.cuda.synchronize()
-            used = NAMES[:3] if fused else NAMES
-            times = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)]
-                     for j, n in enumerate(used)}
             if fused:
-                times = {"write_k": times["write_k"], "pack_q": times["pack_q"], "mqa_logits_topk": times["mqa_logits"]}
+                used = {"write_k": 0, "pack_q": 1, "mqa_logits_topk": 3}
+            elif fp8:
+                used = {"write_k": 0, "pack_q": 1, "mqa_logits": 3, "topk": 4}
+            else:
+                used = {"write_k": 0, "pack_q": 1, "plan": 2, "mqa_logits": 3, "topk": 4, "mqa_logits_bounded": 5}
+            times = {n: [evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)] for n, j in used.items()}
             per_kernel = {n: float(np.mean(v)) for n, v in times.items()}
             stats = {n: (float(np.median(v)), float(np.min(v))) for n, v in times.items()}
             del sets, runners
@@ -407,7 +433,8 @@ def main():
         ms, pk, copies, stats = run_cache(False, dict(payload=payload, scale=scale))
         alg = algorithmic(wl)
         kus = {n: v * 1e3 for n, v in pk.items()}
-        dom = max(kus, key=kus.get)
+        bounded_us = kus.pop("mqa_logits_bounded")   # not part of the step
+        dom = max((n for n in kus if n in alg), key=kus.get)   # the schedule's own kernel has no roofline
         key = f"config{idx}:{dom}"
         rec = {"workload": wl.name, "ms_per_step": round(ms, 4), "scores_per_step": wl.scores,
                "scores_per_s": round(wl.scores / (ms * 1e-3), 1), "rows": T, "requests": wl.n_reqs,
@@ -418,7 +445,8 @@ def main():
                "k_write": {"tokens": int(wl.k_new.shape[0]),
                            "tokens_per_s": round(wl.k_new.shape[0] / (kus["write_k"] * 1e-6), 1),
                            "roofline": roofline_of("write_k", alg, kus["write_k"], measured)},
-               "unique_k_tokens": alg["unique_k_tokens"], "input_copies": copies}
+               "unique_k_tokens": alg["unique_k_tokens"], "input_copies": copies,
+               "logits_host_bounded_us": round(bounded_us, 2)}
         if dom != "mqa_logits":
             rec["logits_roofline"] = roofline_of("mqa_logits", alg, kus["mqa_logits"], measured,
                                                  measured_traffic(f"config{idx}:mqa_logits"))
@@ -539,7 +567,8 @@ def main():
                          f"{reps} runs, {reps * cpu_s:.1f} s of host wall time): the step's K write pro rata, "
                          f"pack_q, logits and top-k of those rows on the oracle; value = sampled scores / "
                          f"mean time per run",
-               "seconds_per_run": {n: round(float(v), 4) for n, v in zip(NAMES, secs)}}
+               "seconds_per_run": {n: round(float(v), 4)
+                                   for n, v in zip(("write_k", "pack_q", "mqa_logits", "topk"), secs)}}
         log(f"[bench] cpu baseline: {cpu['value'] / 1e6:.2f} M scores/s on {cpu['cores']} threads "
             f"({time.time() - t0:.1f}s)")
         del pay_np, sc_np, lg

@@ -133,20 +133,23 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
 
 /*
  * Paged-MQA FP4 logits.  [P2] Attention runtime (FP4 paged-MQA logits over
- * the split payload/scale cache, padded rows at zero context); the score is
- * the lightning-indexer score
+ * the split payload/scale cache, padded rows at zero context; schedules built
+ * once and reused by every compressed-attention layer of a step, decode
+ * schedules built during graph capture); [P1] Summary (the schedule built
+ * on the device in two dispatches whose registers do not grow with the row
+ * count).  The score is the lightning-indexer score
  *     logits[t][s] = sum_h w[t][h] * ReLU( qhat[t][h] . khat[s] )
  * with qhat, khat the dequantised FP4 vectors (e2m1 * 2^(byte-127)).
  *
- *   q_fp4, q_scale, w   as produced by fp4idx_pack_q ([n_rows, n_heads, ...])
+ *   q_fp4, q_scale, w   as produced by fp4idx_pack_q ([n_rows, n_heads, ...]);
+ *                       n_heads 16, 32, 64 or 128
  *   req_row_indptr      [n_reqs+1] int32: rows of request b are
  *                       [indptr[b], indptr[b+1]); indptr[0] = 0, indptr[n_reqs] = n_rows,
  *                       non-decreasing (each bound is clamped into [0, n_rows] and
  *                       indptr[b+1] to at least indptr[b], so broken values only
  *                       ever touch rows 0..n_rows-1; their results are then unspecified)
- *   row_ctx_len         [n_rows] int32: row t scores tokens [0, ctx[t]);
- *                       0 <= ctx[t] <= max_ctx (a larger value writes at
- *                       most min(logits_stride, bt_stride*64) entries)
+ *   row_ctx_len         [n_rows] int32: row t scores tokens [0, ctx[t]); a value
+ *                       above min(logits_stride, bt_stride*64) is cut to it
  *   block_table         [n_reqs, bt_stride] int32: token s of request b is in
  *                       page block_table[b*bt_stride + s/64], slot s%64.  Entries
  *                       for s/64 < ceil(max ctx of b's rows / 64) must be valid
@@ -155,22 +158,99 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
  *                       later entries are never read.
  *   logits              [n_rows, logits_stride] fp32 (out); only [0, ctx[t]) of
  *                       each row is written, the rest is left untouched.
- *   n_reqs              at most 65535
- *   max_rows_per_req    host bound >= max_b (indptr[b+1]-indptr[b])
- *   max_ctx             host bound >= max_t ctx[t]; max_ctx <= bt_stride*64 and
- *                       max_ctx <= logits_stride
+ *   workspace           device memory of workspace_bytes bytes, 16-byte aligned,
+ *                       owned by the caller; fp4idx_mqa_logits_workspace_bytes()
+ *                       gives the size.  It holds the work schedule; its
+ *                       contents between calls belong to the library.  Calls
+ *                       that overlap in time must not share a workspace.
  * Arithmetic: per 16 heads x 16 tokens, one block-scaled FP4 MFMA
  * (16x16x128) with fp32 accumulation; ReLU and the head weight in fp32; the
  * head sum in a fixed order.  The result for (t, s) does not depend on the
- * batch composition, the physical pages or the launch shape.
- * No workspace is needed: the launch grid covers (request, row group, token
- * chunk) from the host bounds and idle work-groups exit at once.
+ * batch composition, the physical pages, the schedule or the launch shape,
+ * and equals fp4idx_mqa_logits_bounded's bit for bit.
+ *
+ * Two launches on `stream`: the plan (fp4idx_mqa_logits_plan with max_ctx =
+ * min(logits_stride, bt_stride*64)) and the run (fp4idx_mqa_logits_run).
+ * Returns FP4IDX_E_WORKSPACE when workspace is NULL, unaligned or smaller
+ * than the lists of the batch's row blocks need; a workspace smaller than
+ * fp4idx_mqa_logits_workspace_bytes() for the batch's longest context makes
+ * longer (fewer) work items and stays correct.  With armed timing events
+ * (fp4idx_time_next_call) the start is the plan's and the stop the run's.
  */
 int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
                       const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
                       const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
-                      int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
-                      int64_t max_ctx, void* stream);
+                      int64_t num_pages, float* logits, int64_t logits_stride, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of fp4idx_mqa_logits and fp4idx_mqa_logits_plan for a
+ * batch of n_rows rows in n_reqs requests whose rows have at most max_ctx
+ * tokens of context (any head count).  0 for an empty batch.
+ */
+size_t fp4idx_mqa_logits_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t max_ctx);
+
+/*
+ * The work schedule of a batch, built on the device into workspace (one
+ * launch of one work-group; its registers and LDS do not depend on the
+ * batch).  The kernel follows from n_rows / n_reqs and n_heads: under about
+ * three rows per request the per-wave kernel (1 or 2 rows per wave, each
+ * wave streaming its own pages), else the shared-page kernel (4, 6 or 8
+ * rows per work-group, each page staged once in LDS for all of them).  Each
+ * request's rows are split evenly into row blocks of at most that many
+ * rows, and each block's pages into chunks: for the per-wave kernel of the
+ * work-group's pages; for the shared-page kernel of about equal work (the
+ * busier a block's waves, the shorter its chunks), large ones first and
+ * the last share of every block in chunks a quarter as long, so that the
+ * item list, taken in order, ends with short items.  The items are
+ * (request, row block, page chunk).  Context lengths are read here (cut to
+ * max_ctx) and by the run.
+ *
+ * The schedule depends only on n_rows, n_heads, req_row_indptr, n_reqs and
+ * row_ctx_len, so one plan serves any number of fp4idx_mqa_logits_run calls
+ * for that batch (every compressed-attention layer of a step: other Q,
+ * weights, pools and block tables), including replays of a captured graph.
+ * Rebuild it when the batch changes.  Arguments as fp4idx_mqa_logits;
+ * max_ctx >= 0 bounds the contexts the schedule covers.
+ */
+int fp4idx_mqa_logits_plan(int64_t n_rows, int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                           const int32_t* row_ctx_len, int64_t max_ctx, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * The logits of a batch from a schedule fp4idx_mqa_logits_plan built in
+ * workspace for the same n_rows, n_heads, req_row_indptr, n_reqs and
+ * row_ctx_len (one launch: work-group i scores item i of the schedule; the
+ * grid is an upper bound on the item count from the host's sizes, and
+ * work-groups past the schedule's items leave at once).  Arguments as
+ * fp4idx_mqa_logits.  The run only reads the workspace, so runs that share
+ * one plan may overlap.  A workspace holding another batch's schedule, or
+ * none, never makes the kernel touch memory outside the buffers described
+ * here (each item is checked against the call's requests and rows); the
+ * logits are then unspecified.
+ */
+int fp4idx_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                          int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                          const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                          int64_t num_pages, float* logits, int64_t logits_stride, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * The same logits without a workspace: the launch grid covers (request, row
+ * group, token chunk) from two host bounds and idle work-groups exit at
+ * once.  Arguments as fp4idx_mqa_logits, plus
+ *   max_rows_per_req    host bound >= max_b (indptr[b+1]-indptr[b])
+ *   max_ctx             host bound >= max_t ctx[t]; max_ctx <= bt_stride*64 and
+ *                       max_ctx <= logits_stride (a larger ctx[t] is cut to
+ *                       min(logits_stride, bt_stride*64))
+ *   n_reqs              at most 65535
+ * Results equal fp4idx_mqa_logits's bit for bit.
+ */
+int fp4idx_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                              int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                              const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                              int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, void* stream);
 
 /*
  * Top-k over each logits row.  [P3] Changes (sorted top-k selection) and

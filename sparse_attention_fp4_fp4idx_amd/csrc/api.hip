@@ -3,6 +3,7 @@
 // Validation looks at host scalars and pointer values only (never at device
 // memory), so every entry point can be captured in a HIP graph.  On any
 // negative status nothing has been launched.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -111,6 +112,56 @@ int check_logits(int64_t n_rows, int32_t n_heads, int32_t n_reqs, int32_t bt_str
   return FP4IDX_OK;
 }
 
+// Host checks of a plan's arguments.
+int check_plan(int64_t n_rows, int32_t n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+               int64_t max_ctx, const void* workspace, size_t workspace_bytes) {
+  if (n_rows < 0 || n_reqs < 0 || max_ctx < 0 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
+  if (!indptr || !row_ctx) return FP4IDX_E_INVALID;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes > (size_t)INT64_MAX) return FP4IDX_E_WORKSPACE;
+  const fp4idx::PlanShape sh = fp4idx::plan_shape(n_rows, n_reqs, n_heads);
+  const fp4idx::PlanSizes sz = fp4idx::plan_sizes(n_rows, n_reqs, sh.rows);
+  const int64_t cap = fp4idx::plan_capacity(sz, (int64_t)workspace_bytes);
+  if (cap < sz.blocks || cap > 0x7FFFFFFF) return FP4IDX_E_WORKSPACE;
+  return FP4IDX_OK;
+}
+
+// Host checks of a scheduled logits call (its plan's checks, then the rest).
+int check_planned(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
+                  const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
+                  int32_t bt_stride, const uint8_t* payload, const uint8_t* scale, int64_t num_pages,
+                  const float* logits, int64_t logits_stride, const void* workspace, size_t workspace_bytes) {
+  if (bt_stride < 0 || num_pages < 0 || logits_stride < 0) return FP4IDX_E_INVALID;
+  const int rc = check_plan(n_rows, n_heads, indptr, n_reqs, row_ctx, 0, workspace, workspace_bytes);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
+  if (num_pages == 0 || !q_fp4 || !q_scale || !w || !block_table || !payload || !scale || !logits)
+    return FP4IDX_E_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16) || !aligned(scale, 4)) return FP4IDX_E_INVALID;
+  return FP4IDX_OK;
+}
+
+// Plan and run in sequence on one stream.  Armed timing events stamp the
+// plan's start and the run's end.
+hipError_t planned_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                          int32_t n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                          const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                          int64_t num_pages, float* logits, int64_t logits_stride, void* workspace,
+                          int64_t workspace_bytes, hipStream_t stream) {
+  const fp4idx::TimingEvents armed = fp4idx::t_timing;
+  // contexts are cut to the logits row and the block table in any case
+  const int64_t ctx_bound = std::min<int64_t>(logits_stride, (int64_t)bt_stride * FP4IDX_PAGE_TOKENS);
+  fp4idx::t_timing = {armed.start, nullptr};
+  hipError_t e = fp4idx::launch_mqa_logits_plan(n_rows, n_heads, indptr, n_reqs, row_ctx, ctx_bound, workspace,
+                                                workspace_bytes, stream);
+  fp4idx::t_timing = {nullptr, armed.stop};
+  if (e == hipSuccess)
+    e = fp4idx::launch_mqa_logits_run(q_fp4, q_scale, w, n_rows, n_heads, indptr, n_reqs, row_ctx, block_table,
+                                      bt_stride, payload, scale, num_pages, logits, logits_stride, workspace,
+                                      workspace_bytes, stream);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,11 +214,11 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
                                                 static_cast<hipStream_t>(stream)));
 }
 
-int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
-                      const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
-                      const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
-                      int64_t num_pages, float* logits, int64_t logits_stride, int32_t max_rows_per_req,
-                      int64_t max_ctx, void* stream) {
+int fp4idx_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                              int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                              const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                              int64_t logits_stride, int32_t max_rows_per_req, int64_t max_ctx, void* stream) {
   const TimingScope timing_scope;
   int rc = check_logits(n_rows, n_heads, n_reqs, bt_stride, num_pages, logits_stride, max_rows_per_req, max_ctx);
   if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return rc;
@@ -176,9 +227,61 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
   if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16) || !aligned(scale, 4)) return FP4IDX_E_INVALID;
   const int dev = check_device();
   if (dev != FP4IDX_OK) return dev;
-  return launched(fp4idx::launch_mqa_logits(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len,
-                                            block_table, bt_stride, payload, scale, num_pages, logits, logits_stride,
-                                            max_rows_per_req, max_ctx, static_cast<hipStream_t>(stream)));
+  return launched(fp4idx::launch_mqa_logits_bounded(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs,
+                                                    row_ctx_len, block_table, bt_stride, payload, scale, num_pages,
+                                                    logits, logits_stride, max_rows_per_req, max_ctx,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t fp4idx_mqa_logits_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t max_ctx) {
+  if (n_rows <= 0 || n_reqs <= 0 || max_ctx < 0 || n_rows > 0x7FFFFFFF) return 0;
+  return (size_t)fp4idx::plan_workspace_bytes(n_rows, n_reqs, max_ctx);
+}
+
+int fp4idx_mqa_logits_plan(int64_t n_rows, int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                           const int32_t* row_ctx_len, int64_t max_ctx, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_plan(n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, max_ctx, workspace, workspace_bytes);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_mqa_logits_plan(n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, max_ctx,
+                                                 workspace, (int64_t)workspace_bytes,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                          int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                          const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                          int64_t num_pages, float* logits, int64_t logits_stride, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_planned(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, block_table,
+                         bt_stride, payload, scale, num_pages, logits, logits_stride, workspace, workspace_bytes);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(fp4idx::launch_mqa_logits_run(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs,
+                                                row_ctx_len, block_table, bt_stride, payload, scale, num_pages,
+                                                logits, logits_stride, workspace, (int64_t)workspace_bytes,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
+                      const int32_t* req_row_indptr, int32_t n_reqs, const int32_t* row_ctx_len,
+                      const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                      int64_t num_pages, float* logits, int64_t logits_stride, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const TimingScope timing_scope;
+  int rc = check_planned(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, block_table,
+                         bt_stride, payload, scale, num_pages, logits, logits_stride, workspace, workspace_bytes);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  return launched(planned_logits(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, block_table,
+                                 bt_stride, payload, scale, num_pages, logits, logits_stride, workspace,
+                                 (int64_t)workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,

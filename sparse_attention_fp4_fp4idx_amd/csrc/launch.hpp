@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "schedule.hpp"
+
 namespace fp4idx {
 
 // Events armed by fp4idx_time_next_call() for the calling thread's next entry
@@ -61,11 +63,27 @@ hipError_t launch_write_k_pack_q_fp8(const uint16_t* k, int64_t n_tokens, int64_
                                      const int32_t* pos_q, const float* w_in, float w_scale, uint8_t* q_fp8,
                                      float* q_scale, float* w_out, hipStream_t stream);
 
-hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
-                             int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
-                             const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
-                             const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
-                             int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);
+hipError_t launch_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                                     int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                     const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                                     const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                                     int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream);
+
+// The scheduled logits: the plan kernel (the batch's items into the
+// workspace) and the persistent kernel that walks them.
+hipError_t launch_plan(const int32_t* indptr, int32_t n_reqs, int64_t n_rows, const int32_t* row_ctx,
+                       int64_t max_ctx, int32_t* ws, int64_t cap_items, const PlanSizes& sz, const PlanShape& sh,
+                       int fixed, int target, int resident, hipStream_t stream);
+PlanShape plan_shape(int64_t n_rows, int32_t n_reqs, int n_heads);
+int64_t plan_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t max_ctx);
+hipError_t launch_mqa_logits_plan(int64_t n_rows, int n_heads, const int32_t* indptr, int32_t n_reqs,
+                                  const int32_t* row_ctx, int64_t max_ctx, void* workspace, int64_t workspace_bytes,
+                                  hipStream_t stream);
+hipError_t launch_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                                 int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                 const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                                 const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                                 void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int64_t n_rows, int n_heads,
                                  const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,

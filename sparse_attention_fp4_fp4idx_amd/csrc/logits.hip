@@ -46,6 +46,7 @@
 
 #include "launch.hpp"
 #include "logits_core.hpp"
+#include "schedule.hpp"
 
 namespace fp4idx {
 
@@ -58,13 +59,29 @@ namespace fp4idx {
 template <typename FMT, int RW, int NMT>
 constexpr int kMinWavesPerSimd = NMT > 4 ? 1 : RW == 1 ? FMT::kWaves1 : RW == 2 ? FMT::kWaves2 : 1;
 
-template <typename FMT, int RW, int NMT, int PPW, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void mqa_logits_kernel(
-    // the first arguments are preloaded into SGPRs: those the prologue needs
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
-    const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
-    int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
-    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t n_rows) {
+// The arguments every per-wave item needs.
+struct WaveArgs {
+  const int32_t* block_table;
+  const int32_t* indptr;
+  const int32_t* row_ctx;
+  const uint8_t* payload;
+  const uint8_t* scale;
+  int64_t num_pages;
+  int32_t bt_stride;
+  const uint8_t* q_fp4;
+  const uint8_t* q_scale;
+  const float* w;
+  float* logits;
+  int64_t logits_stride;
+  int32_t n_rows;
+};
+
+// One wave's share of a per-wave item: request req, pages [page_begin,
+// page_end) of its block table (page_end - page_begin <= PPW), and the rows
+// rows(row0, nrows) names once the wave's page ids are on their way (0 <=
+// nrows <= RW, rows inside [0, n_rows); nrows 0 leaves).  Wave-uniform.
+template <typename FMT, int RW, int NMT, int PPW, int D, typename Rows>
+__device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_begin, int page_end, Rows rows) {
   static_assert(RW >= 1 && RW <= 4, "rows per wave");
   static_assert(PPW % D == 0 && PPW <= 64, "pages per wave: a multiple of the prefetch depth, one id per lane");
   constexpr int H = NMT * 16;
@@ -72,42 +89,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // one row per wave means one row group per request, so every page is read
   // once (non-temporal); with more rows, other row groups re-read the pages
   constexpr bool kPageNT = RW == 1;
-
-  // grid: x = page chunk, y = row group, z = request.  Work-groups go to the
-  // eight XCDs round robin by linear id, so with the chunk count a multiple
-  // of 8 a fixed chunk index would always land on the same XCD; early chunks
-  // exist for every request, late ones only for long requests, which would
-  // load the first XCDs most.  Rotating each request's chunks by its index
-  // spreads every request over all XCDs (a bijection per request).
-  const int n_chunks = gridDim.x;
-  const int grp = blockIdx.y;
-  const int req = blockIdx.z;
-  int rot = req & 7;
-  if (rot >= n_chunks) rot %= n_chunks;
-  int chunk = (int)blockIdx.x + rot;
-  if (chunk >= n_chunks) chunk -= n_chunks;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int lane = threadIdx.x & 63;
-  const int page_begin = (chunk * 4 + wave) * PPW;
-  if (page_begin >= bt_stride) return;
   const int li = lane & 15;  // token within tile (B, D) / head within M-tile (A)
   const int lg = lane >> 4;  // K block (A, B) / head quad (D)
   const uint32_t lane_pay = FMT::lane_pay(li, lg);
   const uint32_t lane_sc = FMT::lane_sc(li, lg);
+  const int bt_stride = a.bt_stride;
+  const int64_t num_pages = a.num_pages;
 
   // Memory round trip 1: the wave's page ids (one vector load, lane i reads
-  // entry i, clamped into the table) and the request's row range.  No branch
-  // depends on them before the next loads are issued: an empty row group
-  // (row0 >= row_end) loads page 0 and in-range rows, and leaves afterwards.
-  const int32_t* bt = block_table + (int64_t)req * bt_stride;
+  // entry i, clamped into the table) and the row range.  No branch depends
+  // on them before the next loads are issued: an empty row group loads page
+  // 0 and in-range rows, and leaves afterwards.
+  const int32_t* bt = a.block_table + (int64_t)req * bt_stride;
   const int32_t my_pid = bt[min(page_begin + (lane % PPW), bt_stride - 1)];
-  __builtin_amdgcn_sched_barrier(0);  // keep the load issued ahead of the indptr wait
-  // the request's rows, kept inside [0, n_rows) whatever indptr holds
-  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
-  const int row0 = ip0 + grp * RW;
-  const int row_end = ip1;
-  const int nrows = max(0, min(RW, row_end - row0));
-  const int row_hi = max(0, row_end - 1);  // a valid row index to clamp to
+  __builtin_amdgcn_sched_barrier(0);  // keep the load issued ahead of the row range
+  int row0 = 0, nrows = 0;
+  rows(row0, nrows);
+  const int row_hi = max(0, min(row0 + nrows, a.n_rows) - 1);  // a valid row index to clamp to
 
   // Round trip 2, all in flight together: the context lengths (lane r reads
   // row r; requested first so they are not queued behind the page traffic),
@@ -116,7 +115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   // (lane-dependent address: a vector load, so it is issued ahead of the
   // page loads and, loads retiring in order, waiting for it does not wait
   // for the pages)
-  const int32_t my_ctx = row_ctx[min(row0 + (lane & 3), row_hi)];
+  const int32_t my_ctx = a.row_ctx[min(row0 + (lane & 3), row_hi)];
   __builtin_amdgcn_sched_barrier(0);  // issued before the exit test below
   int32_t pid[D];  // the first D page ids; later ones are read from my_pid when they are loaded
 #pragma unroll
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
-    FMT::template load_page<kPageNT>(buf[i], payload, scale, pg, lane_pay, lane_sc);
+    FMT::template load_page<kPageNT>(buf[i], a.payload, a.scale, pg, lane_pay, lane_sc);
   }
 
   typename FMT::QOp aq[RW][NMT];
@@ -151,9 +150,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int64_t hrow = (int64_t)row * H + mt * 16 + li;
-      aq[r][mt] = FMT::load_q(q_fp4, hrow, lg);
-      asc[r][mt >> 2] |= FMT::q_scale_byte(q_scale, hrow, lg) << (8 * (mt & 3));
-      const float4 w4 = *reinterpret_cast<const float4*>(w + (int64_t)row * H + mt * 16 + lg * 4);
+      aq[r][mt] = FMT::load_q(a.q_fp4, hrow, lg);
+      asc[r][mt >> 2] |= FMT::q_scale_byte(a.q_scale, hrow, lg) << (8 * (mt & 3));
+      const float4 w4 = *reinterpret_cast<const float4*>(a.w + (int64_t)row * H + mt * 16 + lg * 4);
       const bool live = r < nrows;
       wv[r][mt][0] = live ? w4.x : 0.f;
       wv[r][mt][1] = live ? w4.y : 0.f;
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
 
   // a context length beyond the row or the table (a broken contract) is cut
   // to what both hold, so no store leaves the row
-  const int ctx_cap = (int)min(min((int64_t)bt_stride * 64, logits_stride), (int64_t)0x7FFFFFFF);
+  const int ctx_cap = (int)min(min((int64_t)bt_stride * 64, a.logits_stride), (int64_t)0x7FFFFFFF);
   int ctx_r[4] = {0, 0, 0, 0};
   int gmax = 0;
 #pragma unroll
@@ -172,7 +171,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
     ctx_r[r] = r < nrows ? min(__builtin_amdgcn_readlane(my_ctx, r), ctx_cap) : 0;
     gmax = max(gmax, ctx_r[r]);
   }
-  const int pages_needed = (gmax + 63) >> 6;
+  const int pages_needed = min((gmax + 63) >> 6, page_end);
   if (nrows == 0 || page_begin >= pages_needed) return;
   const int n_pages = min(PPW, pages_needed - page_begin);
 
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
   int lim[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    rowp[r] = logits + (int64_t)(row0 + (r < nrows ? r : 0)) * logits_stride + (int64_t)page_begin * 64;
+    rowp[r] = a.logits + (int64_t)(row0 + (r < nrows ? r : 0)) * a.logits_stride + (int64_t)page_begin * 64;
     lim[r] = r < nrows ? ctx_r[r] - page_begin * 64 : 0;
   }
   // groups of D pages (a runtime loop; within a group the buffer index is a
@@ -204,15 +203,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPe
       if (pn < n_pages) {
         const int32_t id = __builtin_amdgcn_readlane(my_pid, pn);
         if (id >= 0 && id < num_pages)
-          FMT::template load_page<kPageNT>(buf[i], payload, scale, id, lane_pay, lane_sc);
+          FMT::template load_page<kPageNT>(buf[i], a.payload, a.scale, id, lane_pay, lane_sc);
       }
     });
   }
 }
 
+// Host-bounded grid: x = page chunk, y = row group, z = request.  Work-
+// groups go to the eight XCDs round robin by linear id, so with the chunk
+// count a multiple of 8 a fixed chunk index would always land on the same
+// XCD; early chunks exist for every request, late ones only for long
+// requests, which would load the first XCDs most.  Rotating each request's
+// chunks by its index spreads every request over all XCDs (a bijection per
+// request).  Wave w takes PPW consecutive pages of the chunk.
+template <typename FMT, int RW, int NMT, int PPW, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void
+mqa_logits_kernel(WaveArgs a) {
+  const int n_chunks = gridDim.x;
+  const int grp = blockIdx.y;
+  const int req = blockIdx.z;
+  int rot = req & 7;
+  if (rot >= n_chunks) rot %= n_chunks;
+  int chunk = (int)blockIdx.x + rot;
+  if (chunk >= n_chunks) chunk -= n_chunks;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int page_begin = (chunk * 4 + wave) * PPW;
+  if (page_begin >= a.bt_stride) return;
+  wave_item<FMT, RW, NMT, PPW, D>(a, req, page_begin, page_begin + PPW, [&](int& row0, int& nrows) {
+    // the request's rows, kept inside [0, n_rows) whatever indptr holds
+    const int ip0 = min(max(a.indptr[req], 0), a.n_rows), ip1 = min(max(a.indptr[req + 1], ip0), a.n_rows);
+    row0 = ip0 + grp * RW;
+    nrows = max(0, min(RW, ip1 - row0));
+  });
+}
+
+// Scheduled: work-group i takes item i of the plan (request, RW rows,
+// 4 * PPW pages; wave w its w-th PPW pages), or leaves when the plan has
+// fewer items.  The item is checked against the call's requests and rows.
+template <typename FMT, int RW, int NMT, int PPW, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void
+mqa_logits_wave_planned_kernel(WaveArgs a, const int32_t* __restrict__ hdr, const int4* __restrict__ items,
+                               int32_t n_reqs, int32_t cap_items) {
+  const int n_items = (hdr[kHdrRows] == RW && hdr[kHdrWaves] == 0) ? min(max(hdr[kHdrItems], 0), cap_items) : 0;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int4 iv = items[item];  // the same for the whole work-group: scalar registers
+  const int4 it = make_int4(__builtin_amdgcn_readfirstlane(iv.x), __builtin_amdgcn_readfirstlane(iv.y),
+                            __builtin_amdgcn_readfirstlane(iv.z), __builtin_amdgcn_readfirstlane(iv.w));
+  const int req = it.x, pb = it.z, nr = it.w & 0xFF, npg = it.w >> 8;
+  if (req < 0 || req >= n_reqs || nr <= 0 || nr > RW || pb < 0 || npg <= 0 || npg > 4 * PPW) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int page_begin = pb + wave * PPW;
+  const int page_end = min(page_begin + PPW, pb + npg);
+  if (page_begin >= page_end || page_begin >= a.bt_stride) return;
+  wave_item<FMT, RW, NMT, PPW, D>(a, req, page_begin, page_end, [&](int& row0, int& nrows) {
+    const int ip0 = min(max(a.indptr[req], 0), a.n_rows), ip1 = min(max(a.indptr[req + 1], ip0), a.n_rows);
+    row0 = it.y;
+    nrows = (it.y >= ip0 && it.y + nr <= ip1) ? nr : 0;
+  });
+}
+
 // Page ids one shared-page work-group stages in LDS (its chunk of pages),
 // and the bytes of one FP4 page in the payload and scale pools.
-constexpr int kSharedMaxChunk = 512;
+constexpr int kSharedMaxChunk = kMaxItemPages;
 constexpr int kPayBytes = 4096, kScBytes = 256;
 // Pages x rows one wave of a shared-page work-group scores at most.
 constexpr int kSharedPageRows = 64;
@@ -271,56 +324,65 @@ __device__ __forceinline__ void stage_shared_page(const SharedPageRegs<NPAY>& r,
   }
 }
 
+// LDS of a shared-page work-group: two page slots, the chunk's page ids and
+// the block's context lengths.
+template <int ROWS>
+struct SharedLds {
+  __attribute__((aligned(16))) uint8_t ring[2][kPayBytes + kScBytes];
+  int32_t pid[kSharedMaxChunk];
+  int32_t ctx[ROWS];
+};
+
+// The scalar arguments every shared-page item needs.
+struct SharedArgs {
+  const int32_t* block_table;
+  const int32_t* row_ctx;
+  const uint8_t* payload;
+  const uint8_t* scale;
+  int64_t num_pages;
+  int32_t bt_stride;
+  const uint8_t* q_fp4;
+  const uint8_t* q_scale;
+  const float* w;
+  float* logits;
+  int64_t logits_stride;
+};
+
+// One shared-page item: rows [row0, row0 + nrows) of request req (0 <
+// nrows <= NW*RW, rows inside the call's rows) and the pages [pb, pb +
+// n_max) of its block table (n_max <= kSharedMaxChunk), cut to the pages
+// the rows' contexts reach.  Work-group uniform; starts and ends with the
+// work-group in step (the caller's barriers order it against the previous
+// item's LDS use).
+// tid is the thread's index in the work-group.
 template <int NW, int RW, int NMT>
-__global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ indptr,
-    const int32_t* __restrict__ row_ctx, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ scale,
-    int64_t num_pages, int32_t bt_stride, const uint8_t* __restrict__ q_fp4, const uint8_t* __restrict__ q_scale,
-    const float* __restrict__ w, float* __restrict__ logits, int64_t logits_stride, int32_t chunk_pages,
-    int32_t n_rows) {
+__device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedArgs& a, int req, int row0,
+                                            int nrows, int pb, int n_max, int tid) {
   constexpr int NT = NW * 64;
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;
   constexpr int ROWS = NW * RW;
   constexpr int NPAY = 256 / NT;  // 16-byte payload pieces per thread and page
-  static_assert(NW == 1 || NW == 2 || NW == 4, "waves per work-group");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2][kPayBytes + kScBytes];
-  __shared__ int32_t pid_s[kSharedMaxChunk];
-  __shared__ int32_t ctx_s[ROWS];
-
-  // chunks rotated per request across the XCDs, as in mqa_logits_kernel
-  const int n_chunks = gridDim.x;
-  const int req = blockIdx.z;
-  int rot = req & 7;
-  if (rot >= n_chunks) rot %= n_chunks;
-  int chunk = (int)blockIdx.x + rot;
-  if (chunk >= n_chunks) chunk -= n_chunks;
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
 
-  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
-  const int row0 = ip0 + (int)blockIdx.y * ROWS;
-  const int nrows = max(0, min(ROWS, ip1 - row0));
-  if (nrows == 0) return;  // the whole work-group
   // a context length beyond the row or the table (a broken contract) is cut
   // to what both hold, so no store leaves the row
-  const int ctx_cap = (int)min(min((int64_t)bt_stride * 64, logits_stride), (int64_t)0x7FFFFFFF);
-  if (tid < ROWS) ctx_s[tid] = tid < nrows ? min(max(row_ctx[row0 + tid], 0), ctx_cap) : 0;
+  const int ctx_cap = (int)min(min((int64_t)a.bt_stride * 64, a.logits_stride), (int64_t)0x7FFFFFFF);
+  if (tid < ROWS) L.ctx[tid] = tid < nrows ? min(max(a.row_ctx[row0 + tid], 0), ctx_cap) : 0;
   __syncthreads();
   int gmax = 0;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) gmax = max(gmax, ctx_s[r]);
-  const int pb = chunk * chunk_pages;
-  const int n = min(chunk_pages, ((gmax + 63) >> 6) - pb);
+  for (int r = 0; r < ROWS; ++r) gmax = max(gmax, L.ctx[r]);
+  const int n = min(n_max, ((gmax + 63) >> 6) - pb);
   if (n <= 0) return;  // the whole work-group: no row needs these pages
   // page ids of the chunk; an id outside the pool (a broken table) reads
   // page 0, so every load stays in the pool
-  const int32_t* bt = block_table + (int64_t)req * bt_stride + pb;
+  const int32_t* bt = a.block_table + (int64_t)req * a.bt_stride + pb;
   for (int k = tid; k < n; k += NT) {
     const int32_t p = bt[k];
-    pid_s[k] = (p >= 0 && p < num_pages) ? p : 0;
+    L.pid[k] = (p >= 0 && p < a.num_pages) ? p : 0;
   }
 
   // the wave's rows, the block's rows spread evenly over the waves (a block
@@ -342,27 +404,33 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int64_t hrow = (int64_t)row * H + mt * 16 + li;
-      aq[r][mt] = *reinterpret_cast<const uint4*>(q_fp4 + hrow * 64 + lg * 16);
-      asc[r][mt >> 2] |= (uint32_t)q_scale[hrow * 4 + lg] << (8 * (mt & 3));
-      const float4 w4 = *reinterpret_cast<const float4*>(w + (int64_t)row * H + mt * 16 + lg * 4);
+      aq[r][mt] = *reinterpret_cast<const uint4*>(a.q_fp4 + hrow * 64 + lg * 16);
+      asc[r][mt >> 2] |= (uint32_t)a.q_scale[hrow * 4 + lg] << (8 * (mt & 3));
+      const float4 w4 = *reinterpret_cast<const float4*>(a.w + (int64_t)row * H + mt * 16 + lg * 4);
       wv[r][mt][0] = w4.x;
       wv[r][mt][1] = w4.y;
       wv[r][mt][2] = w4.z;
       wv[r][mt][3] = w4.w;
     }
-    rowp[r] = logits + (int64_t)row * logits_stride + (int64_t)pb * 64;
-    lim[r] = r < nr ? ctx_s[wave * per + r] - pb * 64 : 0;
+    rowp[r] = a.logits + (int64_t)row * a.logits_stride + (int64_t)pb * 64;
+    lim[r] = r < nr ? L.ctx[wave * per + r] - pb * 64 : 0;
   }
   __syncthreads();  // page ids staged
 
   // page bytes in flight: two register sets, used in turn
   SharedPageRegs<NPAY> set0, set1;
-  auto score = [&](const uint8_t* slot, int i) __attribute__((always_inline)) {
+  // a lane's B operand bytes and scale word within an LDS slot; the slot and
+  // the tile are compile-time offsets on top (immediate offsets of the LDS
+  // reads, so both slots share the lane's address registers)
+  const uint8_t* ring = &L.ring[0][0];
+  const uint32_t pay_off = lg * 1024 + li * 16, sc_off = kPayBytes + lg * 64 + li * 4;
+  auto score = [&](auto sc, int i) __attribute__((always_inline)) {
+    constexpr int slot = decltype(sc)::value * (kPayBytes + kScBytes);
     if (nr == 0) return;  // wave-uniform: a wave past the block's rows only loads
     Fp4Lds::Page pg;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pg.b[t] = *reinterpret_cast<const uint4*>(slot + lg * 1024 + (16 * t + li) * 16);
-    pg.s = *reinterpret_cast<const uint32_t*>(slot + kPayBytes + lg * 64 + li * 4);
+    for (int t = 0; t < 4; ++t) pg.b[t] = *reinterpret_cast<const uint4*>(ring + pay_off + slot + 256 * t);
+    pg.s = *reinterpret_cast<const uint32_t*>(ring + sc_off + slot);
     static_for<RW>([&](auto rc) __attribute__((always_inline)) {
       constexpr int r = decltype(rc)::value;
       if (r < nr) {
@@ -371,20 +439,70 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(
       }
     });
   };
-  fetch_shared_page<NT>(set0, payload, scale, pid_s[0], tid);
-  if (n > 1) fetch_shared_page<NT>(set1, payload, scale, pid_s[1], tid);
+  fetch_shared_page<NT>(set0, a.payload, a.scale, L.pid[0], tid);
+  if (n > 1) fetch_shared_page<NT>(set1, a.payload, a.scale, L.pid[1], tid);
   for (int i = 0; i < n; i += 2) {
-    stage_shared_page<NT>(set0, ring[0], tid);
+    stage_shared_page<NT>(set0, L.ring[0], tid);
     __syncthreads();
-    if (i + 2 < n) fetch_shared_page<NT>(set0, payload, scale, pid_s[i + 2], tid);
-    score(ring[0], i);
+    if (i + 2 < n) fetch_shared_page<NT>(set0, a.payload, a.scale, L.pid[i + 2], tid);
+    score(std::integral_constant<int, 0>{}, i);
     if (i + 1 < n) {
-      stage_shared_page<NT>(set1, ring[1], tid);
+      stage_shared_page<NT>(set1, L.ring[1], tid);
       __syncthreads();
-      if (i + 3 < n) fetch_shared_page<NT>(set1, payload, scale, pid_s[i + 3], tid);
-      score(ring[1], i + 1);
+      if (i + 3 < n) fetch_shared_page<NT>(set1, a.payload, a.scale, L.pid[i + 3], tid);
+      score(std::integral_constant<int, 1>{}, i + 1);
     }
   }
+}
+
+// Host-bounded grid: (page chunk, row block, request), each request's chunks
+// rotated across the XCDs as in mqa_logits_kernel.
+template <int NW, int RW, int NMT>
+__global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(SharedArgs a, const int32_t* __restrict__ indptr,
+                                                                    int32_t chunk_pages, int32_t n_rows) {
+  constexpr int ROWS = NW * RW;
+  __shared__ SharedLds<ROWS> L;
+  const int n_chunks = gridDim.x;
+  const int req = blockIdx.z;
+  int rot = req & 7;
+  if (rot >= n_chunks) rot %= n_chunks;
+  int chunk = (int)blockIdx.x + rot;
+  if (chunk >= n_chunks) chunk -= n_chunks;
+  // the request's rows, kept inside [0, n_rows) whatever indptr holds
+  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
+  const int row0 = ip0 + (int)blockIdx.y * ROWS;
+  const int nrows = max(0, min(ROWS, ip1 - row0));
+  if (nrows == 0) return;  // the whole work-group
+  shared_item<NW, RW, NMT>(L, a, req, row0, nrows, chunk * chunk_pages, chunk_pages, threadIdx.x);
+}
+
+// Scheduled: work-group i takes item i of the plan (request, up to NW*RW
+// rows, a page chunk), or leaves when the plan has fewer items.  The item
+// is checked against the call's requests and rows (a plan of another batch
+// never takes the kernel outside the buffers).
+template <int NW, int RW, int NMT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 && NMT <= 4 ? 4 : 1))) void
+mqa_logits_planned_kernel(SharedArgs a, const int32_t* __restrict__ indptr,
+                                                                     int32_t n_reqs, int32_t n_rows,
+                                                                     const int32_t* __restrict__ hdr,
+                                                                     const int4* __restrict__ items,
+                                                                     int32_t cap_items) {
+  constexpr int ROWS = NW * RW;
+  __shared__ SharedLds<ROWS> L;
+  const int n_items =
+      (hdr[kHdrRows] == ROWS && hdr[kHdrWaves] == NW) ? min(max(hdr[kHdrItems], 0), cap_items) : 0;
+  const int item = blockIdx.x;
+  if (item >= n_items) return;
+  const int4 iv = items[item];  // the same for the whole work-group: scalar registers
+  const int4 it = make_int4(__builtin_amdgcn_readfirstlane(iv.x), __builtin_amdgcn_readfirstlane(iv.y),
+                            __builtin_amdgcn_readfirstlane(iv.z), __builtin_amdgcn_readfirstlane(iv.w));
+  const int req = it.x, pb = it.z, nrows = it.w & 0xFF, n_max = it.w >> 8;
+  if (req < 0 || req >= n_reqs || nrows <= 0 || nrows > ROWS || pb < 0 || n_max <= 0 || n_max > kSharedMaxChunk ||
+      (int64_t)pb + n_max > a.bt_stride)
+    return;
+  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
+  if (it.y < ip0 || it.y + nrows > ip1) return;
+  shared_item<NW, RW, NMT>(L, a, req, it.y, nrows, pb, n_max, threadIdx.x);
 }
 
 // The arguments of one logits call, as the launchers pass them down.
@@ -427,9 +545,10 @@ static hipError_t launch_shared(const LogitsCall& c, int page_rows) {
   int64_t chunk_pages = std::min<int64_t>((pages + chunks - 1) / chunks, kSharedMaxChunk);
   chunks = (pages + chunk_pages - 1) / chunk_pages;
   if (chunks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const SharedArgs a{c.block_table, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
+                     c.q, c.q_scale, c.w, c.logits, c.logits_stride};
   return launch(mqa_logits_shared_kernel<NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)c.n_reqs),
-                dim3(NW * 64), 0, c.stream, c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages,
-                c.bt_stride, c.q, c.q_scale, c.w, c.logits, c.logits_stride, (int32_t)chunk_pages, c.n_rows);
+                dim3(NW * 64), 0, c.stream, a, c.indptr, (int32_t)chunk_pages, c.n_rows);
 }
 
 template <typename FMT, int RW, int NMT, int PPW, int D>
@@ -439,10 +558,10 @@ static hipError_t launch_rw(const LogitsCall& c) {
   const int64_t n_groups = (c.max_rows_per_req + RW - 1) / RW;
   if (n_chunks == 0 || n_groups == 0 || c.n_reqs == 0) return hipSuccess;
   if (n_chunks > 0x7FFFFFFFLL || n_groups > 65535 || c.n_reqs > 65535) return hipErrorInvalidConfiguration;
+  const WaveArgs a{c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
+                   c.q, c.q_scale, c.w, c.logits, c.logits_stride, c.n_rows};
   return launch(mqa_logits_kernel<FMT, RW, NMT, PPW, D>,
-                dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)c.n_reqs), dim3(256), 0, c.stream,
-                c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride, c.q, c.q_scale, c.w,
-                c.logits, c.logits_stride, c.n_rows);
+                dim3((unsigned)n_chunks, (unsigned)n_groups, (unsigned)c.n_reqs), dim3(256), 0, c.stream, a);
 }
 
 template <typename FMT, int NMT>
@@ -493,11 +612,11 @@ static hipError_t launch_fp4_shared(const LogitsCall& c, bool uniform) {
   return launch_shared<4, 2, NMT>(c, page_rows);
 }
 
-hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
-                             int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
-                             const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
-                             const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
-                             int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
+hipError_t launch_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                                     int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                     const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                                     const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                                     int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
   if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const LogitsCall c{q_fp4,       q_scale,   w,       indptr,    n_reqs,    (int32_t)n_rows, row_ctx,
                      block_table, bt_stride, payload, scale,     num_pages, logits,          logits_stride,
@@ -517,6 +636,151 @@ hipError_t launch_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const
     case 32: return launch_fp4_shared<2>(c, uniform);
     case 64: return launch_fp4_shared<4>(c, uniform);
     case 128: return launch_fp4_shared<8>(c, uniform);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---- the scheduled path: the plan (schedule.hip), then one work-group per item
+
+
+// The kernel and shape for a batch, from what the host knows: the average
+// rows per request and the head count (the same rule for the plan and the
+// run).  Under about three rows per request the per-wave kernel (rows per
+// wave = 1 or 2, each wave its own pages), else the shared-page kernel.
+PlanShape plan_shape(int64_t n_rows, int32_t n_reqs, int n_heads) {
+  const int64_t avg10 = n_reqs > 0 ? 10 * n_rows / n_reqs : 0;  // rows per request x 10
+  if (avg10 < 15) return PlanShape{0, 1};
+  if (avg10 < 30) return PlanShape{0, 2};
+  if (n_heads == 128) return avg10 >= 60 ? PlanShape{4, 8} : PlanShape{2, 4};
+  if (avg10 >= 70) return PlanShape{4, 8};
+  if (avg10 >= 45) return PlanShape{2, 6};
+  return PlanShape{2, 4};
+}
+
+// Pages of one per-wave item: the work-group's four waves, PPW pages each.
+template <typename FMT, int RW>
+constexpr int kWaveItemPages = 4 * (RW == 1 ? FMT::kPpw1 : FMT::kPpw2);
+
+static int wave_item_pages(const PlanShape& sh) {
+  return sh.rows == 1 ? kWaveItemPages<Fp4Split, 1> : kWaveItemPages<Fp4Split, 2>;
+}
+
+// The most items a plan of this shape makes for the batch sizes and the
+// context bound (the run's grid; work-groups past the plan's items leave).
+static int64_t plan_item_bound(const PlanShape& sh, int64_t n_rows, int32_t n_reqs, int64_t max_ctx) {
+  const PlanSizes sz = plan_sizes(n_rows, n_reqs, sh.rows);
+  return sz.blocks * plan_items_per_block(sh, (max_ctx + 63) / 64, wave_item_pages(sh), kItemTarget);
+}
+
+int64_t plan_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t max_ctx) {
+  int64_t bytes = 0;
+  for (int heads : {64, 128}) {  // the shapes a batch of these sizes can get
+    const PlanShape sh = plan_shape(n_rows, n_reqs, heads);
+    bytes = std::max(bytes, plan_bytes(sh, n_rows, n_reqs, max_ctx, wave_item_pages(sh), kItemTarget));
+  }
+  return bytes;
+}
+
+// Work-groups of a kernel the device holds at once.
+template <typename K>
+static int resident_groups(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 1024;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), threads, 0) !=
+      hipSuccess)
+    return 1024;
+  return cus * std::max(per_cu, 1);
+}
+
+// The work-groups a plan's kernel keeps resident (the plan sizes its short
+// chunks from it).
+template <int NMT>
+static int planned_resident(const PlanShape& sh) {
+  if (sh.waves == 0) return 0;
+  if (sh.waves == 4) return resident_groups(mqa_logits_planned_kernel<4, 2, NMT>, 256);
+  if constexpr (NMT != 8) {
+    if (sh.rows == 6) return resident_groups(mqa_logits_planned_kernel<2, 3, NMT>, 128);
+  }
+  return resident_groups(mqa_logits_planned_kernel<2, 2, NMT>, 128);
+}
+
+template <int NW, int RW, int NMT>
+static hipError_t launch_planned(const LogitsCall& c, const int32_t* ws, int64_t grid, int64_t cap_items,
+                                 const PlanSizes& sz) {
+  const SharedArgs a{c.block_table, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
+                     c.q, c.q_scale, c.w, c.logits, c.logits_stride};
+  return launch(mqa_logits_planned_kernel<NW, RW, NMT>, dim3((unsigned)grid), dim3(NW * 64), 0, c.stream, a,
+                c.indptr, c.n_reqs, c.n_rows, ws, reinterpret_cast<const int4*>(ws + sz.items_off),
+                (int32_t)cap_items);
+}
+
+template <int RW, int NMT>
+static hipError_t launch_wave_planned(const LogitsCall& c, const int32_t* ws, int64_t grid, int64_t cap_items,
+                                      const PlanSizes& sz) {
+  const WaveArgs a{c.block_table, c.indptr, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
+                   c.q, c.q_scale, c.w, c.logits, c.logits_stride, c.n_rows};
+  constexpr int PPW = RW == 1 ? Fp4Split::kPpw1 : Fp4Split::kPpw2;
+  constexpr int D = RW == 1 ? Fp4Split::kD1 : Fp4Split::kD2;
+  return launch(mqa_logits_wave_planned_kernel<Fp4Split, RW, NMT, PPW, D>, dim3((unsigned)grid), dim3(256), 0,
+                c.stream, a, ws, reinterpret_cast<const int4*>(ws + sz.items_off), c.n_reqs, (int32_t)cap_items);
+}
+
+template <int NMT>
+static hipError_t launch_planned_nmt(const LogitsCall& c, PlanShape sh, const int32_t* ws, int64_t grid,
+                                     int64_t cap_items, const PlanSizes& sz) {
+  if (sh.waves == 0) {
+    if (sh.rows == 1) return launch_wave_planned<1, NMT>(c, ws, grid, cap_items, sz);
+    return launch_wave_planned<2, NMT>(c, ws, grid, cap_items, sz);
+  }
+  if (sh.waves == 4) return launch_planned<4, 2, NMT>(c, ws, grid, cap_items, sz);
+  if constexpr (NMT != 8) {
+    if (sh.rows == 6) return launch_planned<2, 3, NMT>(c, ws, grid, cap_items, sz);
+  }
+  return launch_planned<2, 2, NMT>(c, ws, grid, cap_items, sz);
+}
+
+hipError_t launch_mqa_logits_plan(int64_t n_rows, int n_heads, const int32_t* indptr, int32_t n_reqs,
+                                  const int32_t* row_ctx, int64_t max_ctx, void* workspace, int64_t workspace_bytes,
+                                  hipStream_t stream) {
+  const PlanShape sh = plan_shape(n_rows, n_reqs, n_heads);
+  const PlanSizes sz = plan_sizes(n_rows, n_reqs, sh.rows);
+  const int64_t cap = plan_capacity(sz, workspace_bytes);
+  int resident = 0;
+  switch (n_heads) {
+    case 16: resident = planned_resident<1>(sh); break;
+    case 32: resident = planned_resident<2>(sh); break;
+    case 64: resident = planned_resident<4>(sh); break;
+    default: resident = planned_resident<8>(sh); break;
+  }
+  return launch_plan(indptr, n_reqs, n_rows, row_ctx, max_ctx, static_cast<int32_t*>(workspace), cap, sz, sh,
+                     sh.waves == 0 ? wave_item_pages(sh) : 0, kItemTarget, resident, stream);
+}
+
+hipError_t launch_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                                 int n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                                 const int32_t* block_table, int32_t bt_stride, const uint8_t* payload,
+                                 const uint8_t* scale, int64_t num_pages, float* logits, int64_t logits_stride,
+                                 void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (n_rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const PlanShape sh = plan_shape(n_rows, n_reqs, n_heads);
+  const PlanSizes sz = plan_sizes(n_rows, n_reqs, sh.rows);
+  const int64_t cap = plan_capacity(sz, workspace_bytes);
+  if (cap < sz.blocks || cap > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  // contexts are cut to the logits row and the block table in any case
+  const int64_t ctx_bound = std::min<int64_t>(logits_stride, (int64_t)bt_stride * 64);
+  const int64_t grid = std::min<int64_t>(plan_item_bound(sh, n_rows, n_reqs, ctx_bound), cap);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const LogitsCall c{q_fp4,       q_scale,   w,       indptr,    n_reqs,    (int32_t)n_rows, row_ctx,
+                     block_table, bt_stride, payload, scale,     num_pages, logits,          logits_stride,
+                     0,           0,         stream};
+  const int32_t* ws = static_cast<const int32_t*>(workspace);
+  switch (n_heads) {
+    case 16: return launch_planned_nmt<1>(c, sh, ws, grid, cap, sz);
+    case 32: return launch_planned_nmt<2>(c, sh, ws, grid, cap, sz);
+    case 64: return launch_planned_nmt<4>(c, sh, ws, grid, cap, sz);
+    case 128: return launch_planned_nmt<8>(c, sh, ws, grid, cap, sz);
     default: return hipErrorInvalidValue;
   }
 }

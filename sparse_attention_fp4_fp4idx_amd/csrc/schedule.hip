@@ -1,0 +1,266 @@
+// The plan kernel: the batch's work items for the scheduled logits kernels.
+//
+// One work-group of 1,024 threads (its registers and LDS do not depend on
+// the batch: the per-request list lives in the workspace, and so does the
+// per-block list beyond the first 4,096 blocks, whose working set stays in
+// registers):
+//  1. blocks per request: a request of R rows (its indptr range, clamped
+//     into [0, n_rows]) becomes ceil(R / rows) row blocks, its rows spread
+//     evenly over them; a block scan gives each request its first block.
+//  2. per block: the longest context among its rows (cut to the plan's
+//     bound) gives its pages P, and the block's work is P times the work of
+//     a page (for the shared-page kernel: staging it plus scoring the
+//     busiest wave's rows); the batch's work W is their sum.
+//  3. per block, its chunks.  Per-wave items have a fixed length (the work-
+//     group's four waves' pages).  Shared-page items: large chunks of about
+//     `target` units of work first, then the rest of the block in chunks a
+//     quarter as long; the share of pages in short chunks is the work of one
+//     round of the device's resident work-groups over W (at least the
+//     remainder of the large chunks).  Block scans of the two counts place
+//     every block's large items in one list and its short items in a second
+//     list that follows the first.
+//  4. the items, written in that order.
+// The logits kernel's work-groups take the items in list order, so the
+// hardware's dispatch keeps every CU busy while large items remain and the
+// list ends with short ones that fill the tail.  The item count never
+// exceeds the workspace's capacity: a block gets at most capacity / blocks
+// items (its chunks grow instead, and a per-wave block's pages past them are
+// not scored), which contexts within the workspace's bound never need.
+#include <algorithm>
+
+#include "launch.hpp"
+#include "schedule.hpp"
+#include "topk_core.hpp"
+
+namespace fp4idx {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanLdsReqs = 4096;  // request offsets searched in LDS up to this many requests
+constexpr int kPlanTiles = 4;       // tiles of blocks whose working set stays in registers
+
+// A block's plan: its request, first row and rows, its pages, and its large
+// and short chunks (length, count, first item of each kind).
+struct BlockPlan {
+  int b, r0, nr, P, Lb, nbig, Ls, nsmall, fb, fs;
+};
+
+// Exclusive prefix of v over the work-group; total gets the sum.  Ends with
+// the work-group in step (its scratch may be reused right away).
+__device__ __forceinline__ int plan_scan(int v, int lane, int wave, uint32_t* part, int& total) {
+  const int excl = (int)block_excl_scan<kPlanWaves>((uint32_t)v, lane, wave, part);
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) t += (int)part[i];
+  total = t;
+  __syncthreads();
+  return excl;
+}
+
+struct PlanParams {
+  const int32_t* indptr;
+  int32_t n_reqs;
+  int32_t n_rows;
+  const int32_t* row_ctx;
+  int32_t ctx_cap;
+  int32_t* ws;
+  int32_t cap_items;
+  int64_t req_off, blk_off, items_off;
+  int32_t max_blocks;
+  int32_t rows_per_block;
+  int32_t waves;      // 0: per-wave items
+  int32_t fixed;      // pages of a per-wave item
+  int32_t target;     // work of a large shared-page item
+  int32_t resident;   // work-groups the device holds at once
+};
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
+  __shared__ uint32_t part[kPlanWaves];
+  __shared__ int32_t first_lds[kPlanLdsReqs + 1];
+  __shared__ float s_work;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* req_first = p.ws + p.req_off;
+  int32_t* blk = p.ws + p.blk_off;
+  int4* items = reinterpret_cast<int4*>(p.ws + p.items_off);
+  const int rows_pb = p.rows_per_block;
+  auto rows_of = [&](int b, int& ip0, int& ip1) {
+    ip0 = min(max(p.indptr[b], 0), p.n_rows);
+    ip1 = min(max(p.indptr[b + 1], ip0), p.n_rows);
+  };
+  if (tid == 0) s_work = 0.0f;
+
+  // 1. row blocks per request, and each request's first block
+  int nb = 0;
+  for (int base = 0; base < p.n_reqs; base += kPlanThreads) {
+    const int b = base + tid;
+    int cnt = 0;
+    if (b < p.n_reqs) {
+      int ip0, ip1;
+      rows_of(b, ip0, ip1);
+      cnt = (ip1 - ip0 + rows_pb - 1) / rows_pb;
+    }
+    int tile = 0;
+    const int first = nb + plan_scan(cnt, lane, wave, part, tile);
+    if (b < p.n_reqs) {
+      req_first[b] = first;
+      if (b < kPlanLdsReqs) first_lds[b] = first;
+    }
+    nb += tile;
+  }
+  // more blocks than rows make only overlapping request ranges (a broken
+  // indptr): the blocks past the bound are not scheduled
+  nb = min(nb, p.max_blocks);
+  if (tid == 0) {
+    req_first[p.n_reqs] = nb;
+    if (p.n_reqs < kPlanLdsReqs) first_lds[p.n_reqs] = nb;
+  }
+  __syncthreads();
+  const bool in_lds = p.n_reqs < kPlanLdsReqs;
+  // the request holding block g: the last b with first[b] <= g (requests
+  // without rows share their successor's first block and are skipped)
+  auto request_of = [&](int g) {
+    int lo = 0, hi = p.n_reqs;  // first[lo] <= g < first[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      const int f = in_lds ? first_lds[mid] : req_first[mid];
+      if (f <= g) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  auto busiest_rows = [&](int nr) { return p.waves > 0 ? (nr + p.waves - 1) / p.waves : nr; };
+
+  // Per-block working set: in registers for the first kPlanTiles tiles of
+  // kPlanThreads blocks, in the workspace's per-block list beyond them.
+  BlockPlan reg[kPlanTiles];
+  // f(g, e) for every block g (g >= nb: a thread without a block, which
+  // still takes part in the scans); tiles in order, work-group uniform
+  auto visit = [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kPlanTiles; ++k)
+      if (k * kPlanThreads < nb) f(k * kPlanThreads + tid, reg[k]);
+    for (int base = kPlanTiles * kPlanThreads; base < nb; base += kPlanThreads) {
+      const int g = base + tid;
+      int32_t* ep = blk + (int64_t)kBlkWords * g;
+      BlockPlan e{};
+      if (g < nb) e = BlockPlan{ep[0], ep[1], ep[2], ep[3], ep[4], ep[5], ep[6], ep[7], ep[8], ep[9]};
+      f(g, e);
+      if (g < nb) {
+        ep[0] = e.b; ep[1] = e.r0; ep[2] = e.nr; ep[3] = e.P; ep[4] = e.Lb;
+        ep[5] = e.nbig; ep[6] = e.Ls; ep[7] = e.nsmall; ep[8] = e.fb; ep[9] = e.fs;
+      }
+    }
+  };
+
+  // 2. per block: request, rows, pages; the batch's work
+  float work = 0.0f;
+  visit([&](int g, BlockPlan& e) __attribute__((always_inline)) {
+    if (g >= nb) return;
+    const int b = request_of(g);
+    int ip0, ip1;
+    rows_of(b, ip0, ip1);
+    const int R = ip1 - ip0;
+    const int nblk = (R + rows_pb - 1) / rows_pb;
+    const int i = g - (in_lds ? first_lds[b] : req_first[b]);
+    int r0 = ip0, nr = 0, cmax = 0;
+    if (i >= 0 && i < nblk) {  // always, for the request the search finds
+      r0 = ip0 + (int)((int64_t)i * R / nblk);
+      const int r1 = ip0 + (int)((int64_t)(i + 1) * R / nblk);
+      nr = r1 - r0;
+      for (int r = r0; r < r1; ++r) cmax = max(cmax, min(max(p.row_ctx[r], 0), p.ctx_cap));
+    }
+    e.b = b;
+    e.r0 = r0;
+    e.nr = nr;
+    e.P = (cmax + 63) >> 6;
+    work += (float)e.P * (float)(kStagePageCost + busiest_rows(nr) * kRowPageCost);
+  });
+  atomicAdd(&s_work, work);
+  __syncthreads();
+  // share of each shared-page block's pages in short chunks
+  const float short_share =
+      p.waves > 0 ? fminf(1.0f, 0.01f * (float)kShortRoundsX100 * (float)p.resident * (float)p.target /
+                                    fmaxf(s_work, 1.0f))
+                  : 0.0f;
+
+  // 3. chunks per block; large items first, then the short ones
+  const int chunk_cap = nb > 0 ? max(1, p.cap_items / nb) : 1;
+  int n_big = 0, n_small = 0;
+  visit([&](int g, BlockPlan& e) __attribute__((always_inline)) {
+    int nbig = 0, nsmall = 0;
+    if (g < nb) {
+      int P = e.P;
+      int Lb = 1, Ls = 1;
+      if (P > 0) {
+        if (p.waves == 0) {
+          Lb = p.fixed;
+          nbig = min((P + Lb - 1) / Lb, chunk_cap);
+          P = min(P, nbig * Lb);  // pages past the workspace's bound are not scored
+        } else {
+          Lb = plan_big_pages(p.target, busiest_rows(e.nr));
+          Ls = plan_small_pages(Lb);
+          const int short_pages = min(P, (int)ceilf(short_share * (float)P));
+          nbig = (P - short_pages) / Lb;
+          const int rest = P - nbig * Lb;
+          nsmall = (rest + Ls - 1) / Ls;
+          if (nsmall > 0) Ls = (rest + nsmall - 1) / nsmall;  // even short chunks
+          if (nbig + nsmall > chunk_cap) {  // a workspace below the contexts' size: fewer, longer chunks
+            const int nch = min(chunk_cap, (P + Lb - 1) / Lb);
+            Lb = (P + nch - 1) / nch;
+            if (Lb > kMaxItemPages) {
+              Lb = kMaxItemPages;
+              P = nch * Lb;
+            }
+            nbig = (P + Lb - 1) / Lb;
+            nsmall = 0;
+          }
+        }
+      }
+      e.P = P;
+      e.Lb = Lb;
+      e.nbig = nbig;
+      e.Ls = Ls;
+      e.nsmall = nsmall;
+    }
+    int tb = 0, ts = 0;
+    e.fb = n_big + plan_scan(nbig, lane, wave, part, tb);
+    e.fs = n_small + plan_scan(nsmall, lane, wave, part, ts);
+    n_big += tb;
+    n_small += ts;
+  });
+
+  // 4. the items
+  visit([&](int g, BlockPlan& e) __attribute__((always_inline)) {
+    if (g >= nb) return;
+    for (int c = 0; c < e.nbig; ++c) {
+      const int p0 = c * e.Lb;
+      items[e.fb + c] = make_int4(e.b, e.r0, p0, e.nr | (min(e.Lb, e.P - p0) << 8));
+    }
+    const int s0 = e.nbig * e.Lb;
+    for (int c = 0; c < e.nsmall; ++c) {
+      const int p0 = s0 + c * e.Ls;
+      items[n_big + e.fs + c] = make_int4(e.b, e.r0, p0, e.nr | (min(e.Ls, e.P - p0) << 8));
+    }
+  });
+  if (tid == 0) {
+    p.ws[kHdrItems] = min(n_big + n_small, p.cap_items);
+    p.ws[1] = 0;
+    p.ws[2] = 0;
+    p.ws[kHdrCap] = p.cap_items;
+    p.ws[kHdrRows] = rows_pb;
+    p.ws[kHdrWaves] = p.waves;
+    p.ws[kHdrFixed] = p.fixed;
+  }
+}
+
+hipError_t launch_plan(const int32_t* indptr, int32_t n_reqs, int64_t n_rows, const int32_t* row_ctx,
+                       int64_t max_ctx, int32_t* ws, int64_t cap_items, const PlanSizes& sz, const PlanShape& sh,
+                       int fixed, int target, int resident, hipStream_t stream) {
+  if (n_rows > 0x7FFFFFFFLL || cap_items > 0x7FFFFFFFLL || cap_items < sz.blocks) return hipErrorInvalidConfiguration;
+  const PlanParams p{indptr, n_reqs, (int32_t)n_rows, row_ctx, (int32_t)std::min<int64_t>(max_ctx, 0x7FFFFFFFLL),
+                     ws, (int32_t)cap_items, sz.req_off, sz.blk_off, sz.items_off, (int32_t)sz.blocks, sh.rows,
+                     sh.waves, fixed, target, resident};
+  return launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+}
+
+}  // namespace fp4idx

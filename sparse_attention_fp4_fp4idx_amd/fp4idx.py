@@ -28,11 +28,13 @@ FP8_PAGE_BYTES = 8448
 MAX_TOPK = 2048
 FUSED_MAX_CTX = 32768
 
-_CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_topk",
+_CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_mqa_logits_plan",
+          "fp4idx_mqa_logits_run", "fp4idx_mqa_logits_bounded", "fp4idx_topk",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
           "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_mfma_valu",
           "fp4idx_peak_read")
-EXPORTS = _CALLS + ("fp4idx_time_next_call", "fp4idx_status_string", "fp4idx_version")
+EXPORTS = _CALLS + ("fp4idx_mqa_logits_workspace_bytes", "fp4idx_time_next_call", "fp4idx_status_string",
+                    "fp4idx_version")
 
 
 class Fp4idxError(RuntimeError):
@@ -57,7 +59,13 @@ def load():
     lib.fp4idx_pack_q.argtypes = [P, i64, i32, i64, P, P, i32, P, f32, P, P, P, P]
     lib.fp4idx_write_k_pack_q.argtypes = [P, i64, i64, P, P, P, f32, P, i32, P, P, i64,
                                           P, i64, i32, i64, P, P, f32, P, P, P, P]
-    lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
+    sz = ctypes.c_size_t
+    lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, sz, P]
+    lib.fp4idx_mqa_logits_run.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, sz, P]
+    lib.fp4idx_mqa_logits_plan.argtypes = [i64, i32, P, i32, P, i64, P, sz, P]
+    lib.fp4idx_mqa_logits_bounded.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
+    lib.fp4idx_mqa_logits_workspace_bytes.argtypes = [i64, i32, i64]
+    lib.fp4idx_mqa_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
     lib.fp4idx_peak_mfma_fp4.argtypes = [i32, P, P]
@@ -322,6 +330,7 @@ def _split_pool_pages(what, payload, scale) -> int:
 
 def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, max_rows_per_req,
                      max_ctx, logits, stream):
+    """Arguments of fp4idx_mqa_logits_bounded (host bounds max_rows_per_req, max_ctx)."""
     _check_logits_shapes("mqa_logits", q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, max_ctx, logits,
                          64, (4,))
     T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
@@ -345,23 +354,148 @@ def _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, pa
     return args, logits
 
 
+def fp4idx_mqa_logits_workspace_bytes(n_rows: int, n_reqs: int, max_ctx: int) -> int:
+    """Workspace bytes of fp4idx_mqa_logits / fp4idx_mqa_logits_plan for the batch sizes."""
+    return int(load().fp4idx_mqa_logits_workspace_bytes(int(n_rows), int(n_reqs), int(max_ctx)))
+
+
+def new_workspace(n_rows: int, n_reqs: int, max_ctx: int, device=None) -> torch.Tensor:
+    """A device workspace (uint8, 16-byte aligned) sized for the batch."""
+    n = max(16, fp4idx_mqa_logits_workspace_bytes(n_rows, n_reqs, max_ctx))
+    return torch.empty(n, dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def _workspace_arg(ws: torch.Tensor):
+    _need(ws.is_contiguous() and ws.dtype == torch.uint8, "mqa_logits", "workspace must be a contiguous uint8 tensor")
+    return [_ptr(ws, _U8, "workspace"), int(ws.numel())]
+
+
+def _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits, workspace,
+                  max_ctx, stream, what="mqa_logits"):
+    """Arguments of fp4idx_mqa_logits / fp4idx_mqa_logits_run.  Without
+    logits, an output of max_ctx columns is allocated; without a workspace,
+    one sized for contexts up to the output's width."""
+    if logits is None:
+        _need(max_ctx is not None, what, "give the logits buffer or max_ctx")
+        logits = torch.empty((int(q_fp4.shape[0]), max(1, int(max_ctx))), dtype=torch.float32, device=q_fp4.device)
+    width = int(logits.shape[1]) if logits.dim() == 2 else 0
+    _check_logits_shapes(what, q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, 0, logits, 64, (4,))
+    T, H = int(q_fp4.shape[0]), int(q_fp4.shape[1])
+    n_reqs = int(req_row_indptr.numel()) - 1
+    _need(block_table.stride(1) == 1, what, "block_table must have unit inner stride")
+    _need(logits.stride(-1) == 1, what, "logits must have unit inner stride")
+    for t, name in ((q_fp4, "q_fp4"), (q_scale, "q_scale"), (w, "w"), (req_row_indptr, "indptr"),
+                    (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale")):
+        _need(t.is_contiguous(), what, f"{name} must be contiguous")
+    num_pages = _split_pool_pages(what, payload, scale)
+    if workspace is None:
+        bound = min(width, int(block_table.shape[1]) * PAGE_TOKENS)
+        workspace = new_workspace(T, n_reqs, bound, q_fp4.device)
+    _need(workspace.is_contiguous() and workspace.dtype == torch.uint8, what,
+          "workspace must be a contiguous uint8 tensor")
+    args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
+            _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
+            _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
+            _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"), _pitch(logits)]
+    return args + _workspace_arg(workspace) + [_stream(stream)], logits, workspace
+
+
 def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor, req_row_indptr: torch.Tensor,
                       row_ctx: torch.Tensor, block_table: torch.Tensor, payload: torch.Tensor, scale: torch.Tensor,
-                      max_rows_per_req: int, max_ctx: int, logits: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """Paged FP4 logits [T, stride] fp32; only [0, ctx[t]) of each row is written."""
-    args, logits = _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
-                                    max_rows_per_req, max_ctx, logits, stream)
+                      logits: torch.Tensor = None, workspace: torch.Tensor = None, max_ctx: int = None,
+                      stream=None) -> torch.Tensor:
+    """Paged FP4 logits [T, stride] fp32 (only [0, ctx[t]) of each row is
+    written): the device schedule (plan) and the scheduled kernel (run) in
+    two launches.  workspace: a uint8 device tensor of
+    fp4idx_mqa_logits_workspace_bytes() bytes (allocated when omitted)."""
+    args, logits, _ = _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits,
+                                    workspace, max_ctx, stream)
     _run("fp4idx_mqa_logits", args)
     return logits
 
 
-def prepare_mqa_logits(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, max_rows_per_req,
-                       max_ctx, logits=None, stream=None):
+def prepare_mqa_logits(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits=None,
+                       workspace=None, max_ctx=None, stream=None):
     """fp4idx_mqa_logits with its arguments marshalled once: (Prepared, logits)."""
+    args, logits, workspace = _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                            logits, workspace, max_ctx, stream)
+    keep = (q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits, workspace)
+    return Prepared("fp4idx_mqa_logits", args, keep=keep), logits
+
+
+class LogitsPlan:
+    """The work schedule of one batch, kept in a device workspace for reuse.
+
+    The schedule depends only on the batch: the rows of each request
+    (req_row_indptr), their context lengths (row_ctx) and the head count.
+    build() issues fp4idx_mqa_logits_plan; run() issues fp4idx_mqa_logits_run
+    for any Q, weights, pool and block table of that batch, so one plan serves
+    every compressed-attention layer of a step and every replay of a captured
+    step (re-build when the batch changes; the tensors are read at build and
+    at run time, so in-place updates of row_ctx need a new build).  max_ctx
+    bounds the contexts the schedule covers (the logits width)."""
+
+    def __init__(self, n_heads: int, req_row_indptr: torch.Tensor, row_ctx: torch.Tensor, max_ctx: int,
+                 workspace: torch.Tensor = None, stream=None):
+        _need(req_row_indptr.dim() == 1 and req_row_indptr.numel() >= 1 and req_row_indptr.is_contiguous(),
+              "LogitsPlan", "req_row_indptr must be a contiguous [n_reqs + 1] tensor")
+        _need(row_ctx.dim() == 1 and row_ctx.is_contiguous(), "LogitsPlan", "row_ctx must be a contiguous [T] tensor")
+        self.n_heads = int(n_heads)
+        self.indptr, self.row_ctx, self.max_ctx = req_row_indptr, row_ctx, int(max_ctx)
+        self.n_rows, self.n_reqs = int(row_ctx.numel()), int(req_row_indptr.numel()) - 1
+        self.workspace = workspace if workspace is not None else new_workspace(
+            self.n_rows, self.n_reqs, self.max_ctx, row_ctx.device)
+        self._plan = Prepared("fp4idx_mqa_logits_plan", [
+            self.n_rows, self.n_heads, _ptr(req_row_indptr, _I32, "req_row_indptr"), self.n_reqs,
+            _ptr(row_ctx, _I32, "row_ctx"), self.max_ctx] + _workspace_arg(self.workspace) + [_stream(stream)],
+            keep=(req_row_indptr, row_ctx, self.workspace))
+
+    def build(self) -> "LogitsPlan":
+        self._plan()
+        return self
+
+    def prepare_build(self) -> Prepared:
+        return self._plan
+
+    def _run_args(self, q_fp4, q_scale, w, block_table, payload, scale, logits, stream):
+        _need(int(q_fp4.shape[0]) == self.n_rows and int(q_fp4.shape[1]) == self.n_heads, "LogitsPlan.run",
+              f"Q must be [{self.n_rows}, {self.n_heads}, 64] for this plan")
+        if logits is None:
+            logits = torch.empty((self.n_rows, max(1, self.max_ctx)), dtype=torch.float32, device=q_fp4.device)
+        args, logits, _ = _planned_args(q_fp4, q_scale, w, self.indptr, self.row_ctx, block_table, payload, scale,
+                                        logits, self.workspace, None, stream, what="mqa_logits_run")
+        return args, logits
+
+    def run(self, q_fp4, q_scale, w, block_table, payload, scale, logits=None, stream=None) -> torch.Tensor:
+        args, logits = self._run_args(q_fp4, q_scale, w, block_table, payload, scale, logits, stream)
+        _run("fp4idx_mqa_logits_run", args)
+        return logits
+
+    def prepare_run(self, q_fp4, q_scale, w, block_table, payload, scale, logits=None, stream=None):
+        """fp4idx_mqa_logits_run with its arguments marshalled once: (Prepared, logits)."""
+        args, logits = self._run_args(q_fp4, q_scale, w, block_table, payload, scale, logits, stream)
+        keep = (q_fp4, q_scale, w, self.indptr, self.row_ctx, block_table, payload, scale, logits, self.workspace)
+        return Prepared("fp4idx_mqa_logits_run", args, keep=keep), logits
+
+
+def fp4idx_mqa_logits_bounded(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor,
+                              req_row_indptr: torch.Tensor, row_ctx: torch.Tensor, block_table: torch.Tensor,
+                              payload: torch.Tensor, scale: torch.Tensor, max_rows_per_req: int, max_ctx: int,
+                              logits: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """The same logits without a workspace, the grid sized from host bounds."""
+    args, logits = _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                                    max_rows_per_req, max_ctx, logits, stream)
+    _run("fp4idx_mqa_logits_bounded", args)
+    return logits
+
+
+def prepare_mqa_logits_bounded(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
+                               max_rows_per_req, max_ctx, logits=None, stream=None):
+    """fp4idx_mqa_logits_bounded with its arguments marshalled once: (Prepared, logits)."""
     args, logits = _mqa_logits_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale,
                                     max_rows_per_req, max_ctx, logits, stream)
     keep = (q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits)
-    return Prepared("fp4idx_mqa_logits", args, keep=keep), logits
+    return Prepared("fp4idx_mqa_logits_bounded", args, keep=keep), logits
 
 
 def _mqa_logits_topk_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, k,
@@ -611,6 +745,8 @@ def prepare_mqa_logits_fp8(q_fp8, q_scale, w, req_row_indptr, row_ctx, block_tab
 write_k = fp4idx_write_k
 pack_q = fp4idx_pack_q
 mqa_logits = fp4idx_mqa_logits
+mqa_logits_bounded = fp4idx_mqa_logits_bounded
+mqa_logits_workspace_bytes = fp4idx_mqa_logits_workspace_bytes
 topk = fp4idx_topk
 write_k_pack_q = fp4idx_write_k_pack_q
 read_k = fp4idx_read_k

@@ -64,14 +64,14 @@ def test_host_validation_rejects_before_any_launch(F):
         assert lib.fp4idx_pack_q(fake, 2, h, 128 * 64, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     assert lib.fp4idx_pack_q(fake, 2, 64, 100, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     # logits: ctx bound beyond the block table or the logits row
-    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 4096, 4, 129,
-                                 None) == E
-    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 100, 4, 128,
-                                 None) == E
-    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128, 5, 128,
-                                 None) == E
-    assert lib.fp4idx_mqa_logits(fake, fake, fake, 4, 40, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128, 4, 128,
-                                 None) == E
+    assert lib.fp4idx_mqa_logits_bounded(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 4096,
+                                         4, 129, None) == E
+    assert lib.fp4idx_mqa_logits_bounded(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 100,
+                                         4, 128, None) == E
+    assert lib.fp4idx_mqa_logits_bounded(fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128,
+                                         5, 128, None) == E
+    assert lib.fp4idx_mqa_logits_bounded(fake, fake, fake, 4, 40, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128,
+                                         4, 128, None) == E
     # top-k: k out of range, ctx bound beyond the row
     for k in (0, -3, 2049):
         assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, 10, None) == E
@@ -90,8 +90,54 @@ def test_host_validation_rejects_before_any_launch(F):
     assert lib.fp4idx_topk(fake, 1, 100, fake, 0, fake, 10, None) == E
     # empty problems are a successful no-op
     assert lib.fp4idx_topk(None, 0, 100, None, 16, None, 10, None) == 0
-    assert lib.fp4idx_mqa_logits(None, None, None, 0, 64, None, 0, None, None, 0, None, None, 0, None, 0, 0, 0,
-                                 None) == 0
+    assert lib.fp4idx_mqa_logits_bounded(None, None, None, 0, 64, None, 0, None, None, 0, None, None, 0, None, 0, 0,
+                                         0, None) == 0
+
+
+def test_scheduled_logits_validate_workspace_and_arguments(F):
+    """fp4idx_mqa_logits / _plan / _run: a missing, unaligned or too small
+    workspace is FP4IDX_E_WORKSPACE; bad scalars FP4IDX_E_INVALID; an empty
+    batch is a no-op; the workspace size grows with rows, requests and
+    contexts and is 0 for an empty batch."""
+    lib = F.load()
+    E, EW = -1, -4
+    fake = ctypes.c_void_p(0x1000)
+    need = lib.fp4idx_mqa_logits_workspace_bytes(4, 1, 128)
+    assert need > 0
+    assert lib.fp4idx_mqa_logits_workspace_bytes(0, 1, 128) == 0
+    assert lib.fp4idx_mqa_logits_workspace_bytes(4, 0, 128) == 0
+    assert lib.fp4idx_mqa_logits_workspace_bytes(8, 1, 128) >= need
+    assert lib.fp4idx_mqa_logits_workspace_bytes(64, 64, 128) > need
+    assert lib.fp4idx_mqa_logits_workspace_bytes(4, 1, 4096) > need
+    assert lib.fp4idx_mqa_logits_workspace_bytes(4, 4, 128) > need
+    #          q     qs    w     T  H   ind   B  ctx   bt    bts pay   sc    P  out   ls   ws    wsb   stream
+    base = [fake, fake, fake, 4, 64, fake, 1, fake, fake, 2, fake, fake, 4, fake, 128, fake, need, None]
+
+    def call(fn, **kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return fn(*a)
+    for fn in (lib.fp4idx_mqa_logits, lib.fp4idx_mqa_logits_run):
+        assert call(fn, a15=None) == EW                       # no workspace
+        assert call(fn, a15=ctypes.c_void_p(0x1008)) == EW    # not 16-byte aligned
+        assert call(fn, a16=64) == EW                         # too small for the batch's row blocks
+        assert call(fn, a4=48) == E
+        assert call(fn, a3=-1) == E
+        assert call(fn, a12=0) == E                           # rows but no pool
+        assert call(fn, a0=None) == E
+        assert call(fn, a13=None) == E
+        assert call(fn, a0=ctypes.c_void_p(0x1004)) == E      # unaligned Q codes
+        assert call(fn, a3=0, a15=None) == 0                  # empty batch: nothing launched
+        assert call(fn, a6=0, a15=None) == 0
+    #             T  H   ind   B  ctx  max_ctx ws    wsb  stream
+    pbase = [4, 64, fake, 1, fake, 128, fake, need, None]
+    assert lib.fp4idx_mqa_logits_plan(*pbase[:6], None, need, None) == EW
+    assert lib.fp4idx_mqa_logits_plan(*pbase[:6], fake, 32, None) == EW
+    assert lib.fp4idx_mqa_logits_plan(4, 40, *pbase[2:]) == E
+    assert lib.fp4idx_mqa_logits_plan(4, 64, None, *pbase[3:]) == E
+    assert lib.fp4idx_mqa_logits_plan(4, 64, fake, 1, fake, -1, fake, need, None) == E
+    assert lib.fp4idx_mqa_logits_plan(0, 64, None, 1, None, 128, None, 0, None) == 0
 
 
 def test_fp8_calls_validate_like_their_fp4_twins(F):
@@ -212,8 +258,18 @@ def test_binding_checks_buffer_sizes_before_any_call(F):
 
     def logits(**kw):
         a = dict(d, **kw)
-        return lambda: F.mqa_logits(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pay"], a["sc"], 2, 200,
-                                    logits=a["out"])
+        return lambda: F.mqa_logits_bounded(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pay"], a["sc"],
+                                            2, 200, logits=a["out"])
+
+    def planned(**kw):
+        a = dict(d, **kw)
+        return lambda: F.mqa_logits(a["q"], a["qs"], a["w"], a["ind"], a["ctx"], a["bt"], a["pay"], a["sc"],
+                                    logits=a["out"], workspace=a.get("ws", torch.zeros(64, dtype=torch.uint8)))
+    _raises(F, planned(), "device tensor")
+    _raises(F, planned(ctx=torch.zeros(2, dtype=torch.int32)), "row_ctx")
+    _raises(F, planned(out=torch.zeros((2, 200))), "output")
+    _raises(F, planned(sc=torch.zeros(4 * 256, dtype=torch.uint8)), "pool sizes")
+    _raises(F, planned(ws=torch.zeros(64, dtype=torch.int32)), "workspace")
     _raises(F, logits(), "device tensor")
     _raises(F, logits(out=torch.zeros((2, 200))), "output")                 # fewer rows than T
     _raises(F, logits(out=torch.zeros((3, 150))), "output")                 # rows shorter than max_ctx

@@ -42,7 +42,7 @@ def _both(F, wl, qf, qs, w, pay, sc, k):
     args = (dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table), dev(pay),
             dev(sc))
     fused = F.mqa_logits_topk(*args, k, wl.max_rows_per_req, wl.max_ctx)
-    logits = F.mqa_logits(*args, wl.max_rows_per_req, wl.max_ctx)
+    logits = F.mqa_logits(*args, max_ctx=wl.max_ctx)
     two = F.topk(logits, args[4], k, wl.max_ctx)
     torch.cuda.synchronize()
     return fused.cpu().numpy(), two.cpu().numpy(), logits.cpu().numpy()

@@ -228,14 +228,26 @@ def test_pack_q_full_size_bit_exact(F, orc, cfg):
 
 # ---------------------------------------------------------------- logits
 
+def bits(x):
+    return np.nan_to_num(x, nan=7.0).view(np.uint32)
+
+
 def _gpu_logits(F, qf, qs, w, wl, payload, scale, stride=None, sentinel=np.nan):
+    """The logits through the scheduled call (fp4idx_mqa_logits: plan + run)
+    and through the host-bounded call, which must agree bit for bit
+    (untouched entries included); returns them."""
     T = qf.shape[0]
     stride = stride or max(1, wl.max_ctx)
+    args = (dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table), dev(payload),
+            dev(scale))
     out = torch.full((T, stride), float(sentinel), dtype=torch.float32, device=DEV)
-    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table),
-                 dev(payload), dev(scale), wl.max_rows_per_req, wl.max_ctx, logits=out)
+    F.mqa_logits(*args, logits=out)
+    ref = torch.full((T, stride), float(sentinel), dtype=torch.float32, device=DEV)
+    F.mqa_logits_bounded(*args, wl.max_rows_per_req, wl.max_ctx, logits=ref)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    got = out.cpu().numpy()
+    assert np.array_equal(bits(got), bits(ref.cpu().numpy())), "scheduled and host-bounded logits differ"
+    return got
 
 
 def _encoded_small(orc, wl):
@@ -300,7 +312,9 @@ def test_logits_same_bits_from_every_kernel(F, orc):
     kernel, one row per wave), as the same request next to a one-row request
     (a non-uniform batch: shared-page kernel, shorter chunks) and as the same
     request next to fifteen one-row requests (under three rows per request
-    on average: per-wave kernel, four rows per wave)."""
+    on average: per-wave kernel, four rows per wave); each batch through the
+    scheduled call and the host-bounded call (whose schedules and kernel
+    shapes differ again)."""
     rng = np.random.default_rng(17)
     ctx = 40_000  # 625 pages: many page chunks
     pages = (ctx + 63) // 64
@@ -308,29 +322,30 @@ def test_logits_same_bits_from_every_kernel(F, orc):
     qf, qs, w = _random_q(rng, 16)
     table = rng.permutation(pages + 3)[:pages].astype(np.int32)[None, :]
     row_ctx = (ctx - np.arange(16)[::-1] * 7).astype(np.int32)
-    out_many = torch.full((16, ctx), float("nan"), dtype=torch.float32, device=DEV)
-    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(np.array([0, 16], np.int32)), dev(row_ctx), dev(table), dev(pay),
-                 dev(sc), 16, ctx, logits=out_many)
-    out_one = torch.full((16, ctx), float("nan"), dtype=torch.float32, device=DEV)
-    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(np.arange(17, dtype=np.int32)), dev(row_ctx),
-                 dev(np.repeat(table, 16, axis=0)), dev(pay), dev(sc), 1, ctx, logits=out_one)
-    out_mixed = torch.full((17, ctx), float("nan"), dtype=torch.float32, device=DEV)
-    F.mqa_logits(dev(np.concatenate([qf, qf[:1]])), dev(np.concatenate([qs, qs[:1]])), dev(np.concatenate([w, w[:1]])),
-                 dev(np.array([0, 16, 17], np.int32)), dev(np.concatenate([row_ctx, row_ctx[:1]])),
-                 dev(np.repeat(table, 2, axis=0)), dev(pay), dev(sc), 16, ctx, logits=out_mixed)
-    out_sparse = torch.full((31, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    def both(q, qsc, wt, ind, cx, bt, mr):
+        """(scheduled, host-bounded) logits of one batch."""
+        T = q.shape[0]
+        o1 = torch.full((T, ctx), float("nan"), dtype=torch.float32, device=DEV)
+        o2 = torch.full((T, ctx), float("nan"), dtype=torch.float32, device=DEV)
+        a_ = (dev(q), dev(qsc), dev(wt), dev(ind), dev(cx), dev(bt), dev(pay), dev(sc))
+        F.mqa_logits(*a_, logits=o1)
+        F.mqa_logits_bounded(*a_, mr, ctx, logits=o2)
+        torch.cuda.synchronize()
+        return o1.cpu().numpy(), o2.cpu().numpy()
+    runs = [both(qf, qs, w, np.array([0, 16], np.int32), row_ctx, table, 16),
+            both(qf, qs, w, np.arange(17, dtype=np.int32), row_ctx, np.repeat(table, 16, axis=0), 1)]
+    m1, m2 = both(np.concatenate([qf, qf[:1]]), np.concatenate([qs, qs[:1]]), np.concatenate([w, w[:1]]),
+                  np.array([0, 16, 17], np.int32), np.concatenate([row_ctx, row_ctx[:1]]),
+                  np.repeat(table, 2, axis=0), 16)
+    runs.append((m1[:16], m2[:16]))
     pick = np.concatenate([np.arange(16), np.arange(15)])
-    F.mqa_logits(dev(qf[pick]), dev(qs[pick]), dev(w[pick]),
-                 dev(np.concatenate([[0], np.arange(16, 32)]).astype(np.int32)), dev(row_ctx[pick]),
-                 dev(np.repeat(table, 16, axis=0)), dev(pay), dev(sc), 16, ctx, logits=out_sparse)
-    torch.cuda.synchronize()
-    a, b, c = out_many.cpu().numpy(), out_one.cpu().numpy(), out_mixed.cpu().numpy()[:16]
-    d = out_sparse.cpu().numpy()
-    bits = lambda x: np.nan_to_num(x, nan=7.0).view(np.uint32)
-    assert np.array_equal(bits(a), bits(b))
-    assert np.array_equal(bits(a), bits(c))
-    assert np.array_equal(bits(a), bits(d[:16]))
-    assert np.array_equal(bits(a[:15]), bits(d[16:]))
+    s1, s2 = both(qf[pick], qs[pick], w[pick], np.concatenate([[0], np.arange(16, 32)]).astype(np.int32),
+                  row_ctx[pick], np.repeat(table, 16, axis=0), 16)
+    runs.append((s1[:16], s2[:16]))
+    a = runs[0][0]
+    for x, y in runs:
+        assert np.array_equal(bits(a), bits(x)) and np.array_equal(bits(a), bits(y))
+    assert np.array_equal(bits(a[:15]), bits(s1[16:])) and np.array_equal(bits(a[:15]), bits(s2[16:]))
     rows, toks = np.arange(16).repeat(40), (rng.random(640) * row_ctx.repeat(40)).astype(np.int64)
     f64, T, A = orc.logits_sampled(qf, qs, w, np.array([0, 16], np.int32), table, pay, sc, rows, toks)
     check_fp4(a[rows, toks], f64, T, A, "16-row request, 40,000 tokens (sampled)")
@@ -349,10 +364,14 @@ def test_logits_multi_row_broken_inputs_stay_in_bounds(F, orc):
     table = wl.block_table.copy()
     table[0, 2] = wl.num_pages + 5  # tokens 128..191 of request 0
     out = torch.full((wl.n_rows + 1, stride), float("nan"), dtype=torch.float32, device=DEV)
+    F.mqa_logits_bounded(dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(bad_ctx), dev(table), dev(pay),
+                         dev(sc), wl.max_rows_per_req, wl.max_ctx, logits=out[:wl.n_rows])
+    out2 = torch.full((wl.n_rows + 1, stride), float("nan"), dtype=torch.float32, device=DEV)
     F.mqa_logits(dev(qf), dev(qs), dev(w), dev(wl.req_row_indptr), dev(bad_ctx), dev(table), dev(pay), dev(sc),
-                 wl.max_rows_per_req, wl.max_ctx, logits=out[:wl.n_rows])
+                 logits=out2[:wl.n_rows])
     torch.cuda.synchronize()
     g = out.cpu().numpy()
+    assert np.array_equal(bits(g), bits(out2.cpu().numpy())), "scheduled and host-bounded logits differ"
     _, f64, T, A = orc.logits(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pay, sc,
                               logits_stride=stride, want_f64=True)
     keep = in_context(wl.row_ctx, stride)
@@ -376,14 +395,19 @@ def test_logits_broken_indptr_stays_in_bounds(F, orc):
                 np.array([4, 1, 6], np.int32)):
         for mr in (1, 5):   # per-wave kernel and multi-row kernels
             out = torch.full((T + 2, stride), float("nan"), dtype=torch.float32, device=DEV)
+            F.mqa_logits_bounded(dev(qf), dev(qs), dev(w), dev(ind), dev(wl.row_ctx), dev(wl.block_table), dev(pay),
+                                 dev(sc), mr, wl.max_ctx, logits=out[:T])
+            out2 = torch.full((T + 2, stride), float("nan"), dtype=torch.float32, device=DEV)
             F.mqa_logits(dev(qf), dev(qs), dev(w), dev(ind), dev(wl.row_ctx), dev(wl.block_table), dev(pay),
-                         dev(sc), mr, wl.max_ctx, logits=out[:T])
+                         dev(sc), logits=out2[:T])
             idx = torch.full((T + 2, 16), -77, dtype=torch.int32, device=DEV)
             F.mqa_logits_topk(dev(qf), dev(qs), dev(w), dev(ind), dev(wl.row_ctx), dev(wl.block_table), dev(pay),
                               dev(sc), 16, mr, wl.max_ctx, out_idx=idx[:T])
             torch.cuda.synchronize()
             g = out.cpu().numpy()
-            assert np.all(np.isnan(g[T:])), (ind, mr)
+            g2 = out2.cpu().numpy()
+            assert np.all(np.isnan(g[T:])) and np.all(np.isnan(g2[T:])), (ind, mr)
+            assert np.all(np.isnan(g2[:T, wl.max_ctx:])), (ind, mr)
             assert np.all(idx.cpu().numpy()[T:] == -77), (ind, mr)
             assert np.all(np.isnan(g[:T, wl.max_ctx:])), (ind, mr)
 
@@ -493,10 +517,14 @@ def test_pools_and_logits_past_2_gib(F, orc):
     bt = high[compact_bt].astype(np.int32)
     qf, qs, w = _random_q(rng, T)
     lg = torch.full((T, stride), float("nan"), dtype=torch.float32, device=DEV)
-    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(indptr), dev(ctx), dev(bt), pay, sc, 2, 256, logits=lg)
+    F.mqa_logits(dev(qf), dev(qs), dev(w), dev(indptr), dev(ctx), dev(bt), pay, sc, logits=lg)
     top = F.topk(lg, dev(ctx), 64, 256)
     torch.cuda.synchronize()
     g = lg[:, :300].cpu().numpy()
+    lg[:, :300] = float("nan")
+    F.mqa_logits_bounded(dev(qf), dev(qs), dev(w), dev(indptr), dev(ctx), dev(bt), pay, sc, 2, 256, logits=lg)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(g), bits(lg[:, :300].cpu().numpy())), "scheduled and host-bounded logits differ"
     del pay, sc
     _, f64, Tt, A = orc.logits(qf, qs, w, indptr, ctx, compact_bt, pay_o, sc_o, logits_stride=300, want_f64=True)
     check_rows(g, f64, Tt, A, ctx, "pools and logits past 2 GiB")
@@ -613,7 +641,7 @@ def test_chain_small_write_pack_logits_topk(F, orc):
     F.write_k(bf16(wl.k_new), dev(wl.pos_new), dev(wl.slot_new), bf16(wl.norm_w), wl.eps, bf16(tab), pay_g, sc_g)
     qf_g, qs_g, w_g = F.pack_q(bf16(wl.q), dev(wl.pos_q), bf16(tab), dev(wl.w), wl.w_scale)
     lg = F.mqa_logits(qf_g, qs_g, w_g, dev(wl.req_row_indptr), dev(wl.row_ctx), dev(wl.block_table), pay_g, sc_g,
-                      wl.max_rows_per_req, wl.max_ctx)
+                      max_ctx=wl.max_ctx)
     top_g = F.topk(lg, dev(wl.row_ctx), wl.topk, wl.max_ctx)
     torch.cuda.synchronize()
     assert np.array_equal(pay_g.cpu().numpy(), pay_o) and np.array_equal(sc_g.cpu().numpy(), sc_o)
@@ -686,7 +714,8 @@ def test_chain_graph_replays_match_eager(F):
                     qs=torch.empty((T, H, 4), dtype=torch.uint8, device=DEV),
                     wo=torch.empty((T, H), dtype=torch.float32, device=DEV),
                     lg=torch.full((T, wl.max_ctx), -7.0, dtype=torch.float32, device=DEV),
-                    top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV))
+                    top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV),
+                    ws=F.new_workspace(T, wl.n_reqs, wl.max_ctx))
 
     def chain(o, strm, side=None):
         kw = strm
@@ -702,7 +731,7 @@ def test_chain_graph_replays_match_eager(F):
             join.record(side)
             strm.wait_event(join)
         F.mqa_logits(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"],
-                     wl.max_rows_per_req, wl.max_ctx, logits=o["lg"], stream=strm)
+                     logits=o["lg"], workspace=o["ws"], stream=strm)
         F.topk(o["lg"], ins["ctx"], wl.topk, wl.max_ctx, out_idx=o["top"], stream=strm)
 
     ref = outs()
@@ -717,13 +746,15 @@ def test_chain_graph_replays_match_eager(F):
         with torch.cuda.graph(g, stream=cap):
             chain(o, torch.cuda.current_stream(), side if forked else None)
         for rep in range(4):
-            for n in ("pay", "sc", "qf", "qs", "wo", "top"):   # eager work between replays
+            for n in ("pay", "sc", "qf", "qs", "wo", "top", "ws"):   # eager work between replays
                 o[n].zero_()
             o["lg"].fill_(-7.0)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
             for n, v in want.items():
+                if n == "ws":
+                    continue
                 got = o[n].cpu()
                 if n in ("wo", "lg"):
                     assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (forked, rep, n)
@@ -737,9 +768,11 @@ def test_chain_graph_replays_follow_changed_inputs(F, orc):
     reuses a captured decode step: new K rows, positions and slots, new
     query rows, positions and weights, new row-to-request split, context
     lengths and block tables (within the captured row and context bounds).
-    Every replay equals an eager run of the same calls on the same values,
-    bit for bit, and the oracle: pool and Q bytes exact, logits within the
-    bar, top-k equal to the oracle's selection of the GPU logits."""
+    The logits call's device schedule is part of the captured graph, so
+    each replay plans the new batch.  Every replay equals an eager run of
+    the same calls on the same values, bit for bit, and the oracle: pool and
+    Q bytes exact, logits within the bar, top-k equal to the oracle's
+    selection of the GPU logits."""
     wl = W.small(seed=63, rows=(3, 1, 8), ctxs=(2500, 900, 4100), topk=512)
     tab_np = W.rope_table(wl.max_pos)
     tab = bf16(tab_np)
@@ -757,13 +790,14 @@ def test_chain_graph_replays_follow_changed_inputs(F, orc):
                     qs=torch.empty((T, H, 4), dtype=torch.uint8, device=DEV),
                     wo=torch.empty((T, H), dtype=torch.float32, device=DEV),
                     lg=torch.full((T, max_ctx), -7.0, dtype=torch.float32, device=DEV),
-                    top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV))
+                    top=torch.empty((T, wl.topk), dtype=torch.int32, device=DEV),
+                    ws=F.new_workspace(T, B, max_ctx))
 
     def chain(o, strm):
         F.write_k(ins["k"], ins["pos"], ins["slot"], ins["nw"], wl.eps, tab, o["pay"], o["sc"], stream=strm)
         F.pack_q(ins["q"], ins["pq"], tab, ins["w"], wl.w_scale, o["qf"], o["qs"], o["wo"], stream=strm)
-        F.mqa_logits(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"], max_rows,
-                     max_ctx, logits=o["lg"], stream=strm)
+        F.mqa_logits(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"],
+                     logits=o["lg"], workspace=o["ws"], stream=strm)
         F.topk(o["lg"], ins["ctx"], wl.topk, max_ctx, out_idx=o["top"], stream=strm)
 
     o = outs()
@@ -804,6 +838,11 @@ def test_chain_graph_replays_follow_changed_inputs(F, orc):
         torch.cuda.synchronize()
         for name in ("pay", "sc", "qf", "qs", "top"):
             assert torch.equal(o[name], e[name]), (rep, name)
+        lb = torch.full((T, max_ctx), -7.0, dtype=torch.float32, device=DEV)   # the host-bounded call agrees
+        F.mqa_logits_bounded(o["qf"], o["qs"], o["wo"], ins["ind"], ins["ctx"], ins["bt"], o["pay"], o["sc"],
+                             max_rows, max_ctx, logits=lb)
+        torch.cuda.synchronize()
+        assert torch.equal(o["lg"].view(torch.int32), lb.view(torch.int32)), rep
         for name in ("wo", "lg"):
             assert torch.equal(o[name].view(torch.int32), e[name].view(torch.int32)), (rep, name)
         # the oracle on the same values (its pool follows the same writes)
