@@ -11,7 +11,9 @@
  * Common conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller (device
  *     memory of the current HIP device).  The library allocates nothing and
- *     keeps no state between calls apart from a per-device architecture check.
+ *     keeps no state between calls apart from a per-device architecture check
+ *     and, for fp4idx_mqa_logits_noalloc alone, a fixed scratch array of
+ *     FP4IDX_SCRATCH_BYTES in each device's copy of its code object.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
  *     is asynchronous on that stream: no host synchronisation, no device reads
  *     on the host, so calls can be captured in a HIP graph.
@@ -45,6 +47,7 @@ extern "C" {
 #define FP4IDX_E_UNSUPPORTED (-2) /* current device is not gfx950            */
 #define FP4IDX_E_LAUNCH (-3)      /* a HIP runtime call or launch failed      */
 #define FP4IDX_E_WORKSPACE (-4)   /* workspace missing or too small           */
+#define FP4IDX_E_SCRATCH (-5)     /* batch too large for the built-in scratch */
 
 #define FP4IDX_HEAD_DIM 128
 #define FP4IDX_ROPE_DIM 64
@@ -54,6 +57,7 @@ extern "C" {
 #define FP4IDX_FP8_PAGE_BYTES 8448     /* [64][128] codes + [64] fp32 scales */
 #define FP4IDX_MAX_TOPK 2048
 #define FP4IDX_FUSED_MAX_CTX 32768     /* longest row of fp4idx_mqa_logits_topk */
+#define FP4IDX_SCRATCH_BYTES (16u << 20) /* per-device scratch of fp4idx_mqa_logits_noalloc */
 
 /*
  * Fused K writer.  [P2] Modifications / fp4_indexer_hip.py and compress.py:
@@ -234,6 +238,31 @@ int fp4idx_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, const fl
                           const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
                           int64_t num_pages, float* logits, int64_t logits_stride, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * fp4idx_mqa_logits for callers that cannot allocate device memory or pass
+ * a workspace (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the work schedule goes into the library's own scratch
+ * array of FP4IDX_SCRATCH_BYTES on the current device instead of a caller
+ * workspace.  Arguments, arithmetic and results as fp4idx_mqa_logits (bit
+ * for bit); no allocation, no hipMalloc or hipFree.
+ *
+ * Limit: the batch's schedule, fp4idx_mqa_logits_workspace_bytes(n_rows,
+ * n_reqs, min(logits_stride, bt_stride*64)) bytes, must fit in
+ * FP4IDX_SCRATCH_BYTES (e.g. 16,384 rows in 64 requests at 131,072 tokens
+ * need 8.3 MiB); a larger batch returns FP4IDX_E_SCRATCH and launches
+ * nothing.  Every call on one device shares that device's array, which keeps
+ * the last call's schedule (the plan writes every word the run reads, so
+ * nothing needs clearing): calls that overlap in time on one device (on
+ * different streams, or from several host threads without ordering) race
+ * and their logits are unspecified.  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress); FP4IDX_E_LAUNCH if that fails.
+ */
+int fp4idx_mqa_logits_noalloc(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                              int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                              const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                              int64_t logits_stride, void* stream);
 
 /*
  * The same logits without a workspace: the launch grid covers (request, row

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "fp4idx.h"
 #include "launch.hpp"
@@ -13,6 +14,13 @@
 namespace fp4idx {
 thread_local TimingEvents t_timing = {nullptr, nullptr};
 }
+
+// Scratch of fp4idx_mqa_logits_noalloc: a fixed array in every device's
+// copy of the code object, holding the work schedule of that call.  Host
+// code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// gives for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[FP4IDX_SCRATCH_BYTES];
 
 namespace {
 
@@ -61,6 +69,9 @@ const char* fp4idx_status_string(int status) {
     case FP4IDX_E_UNSUPPORTED: return "unsupported device (gfx950 required)";
     case FP4IDX_E_LAUNCH: return "HIP launch or runtime error";
     case FP4IDX_E_WORKSPACE: return "workspace missing or too small";
+    case FP4IDX_E_SCRATCH:
+      return "the batch's work schedule needs more than the library's built-in scratch "
+             "(FP4IDX_SCRATCH_BYTES); use fp4idx_mqa_logits with a workspace";
     default: return "unknown status";
   }
 }
@@ -127,6 +138,23 @@ int check_plan(int64_t n_rows, int32_t n_heads, const int32_t* indptr, int32_t n
   return FP4IDX_OK;
 }
 
+// Host checks of a scheduled logits call's buffers and scalars, apart from
+// its workspace.
+int check_planned_args(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                       int32_t n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
+                       const int32_t* block_table, int32_t bt_stride, const uint8_t* payload, const uint8_t* scale,
+                       int64_t num_pages, const float* logits, int64_t logits_stride) {
+  if (bt_stride < 0 || num_pages < 0 || logits_stride < 0) return FP4IDX_E_INVALID;
+  if (n_rows < 0 || n_reqs < 0 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
+  if (!indptr || !row_ctx) return FP4IDX_E_INVALID;
+  if (num_pages == 0 || !q_fp4 || !q_scale || !w || !block_table || !payload || !scale || !logits)
+    return FP4IDX_E_INVALID;
+  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16) || !aligned(scale, 4)) return FP4IDX_E_INVALID;
+  return FP4IDX_OK;
+}
+
 // Host checks of a scheduled logits call (its plan's checks, then the rest).
 int check_planned(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows, int32_t n_heads,
                   const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx, const int32_t* block_table,
@@ -135,10 +163,8 @@ int check_planned(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, 
   if (bt_stride < 0 || num_pages < 0 || logits_stride < 0) return FP4IDX_E_INVALID;
   const int rc = check_plan(n_rows, n_heads, indptr, n_reqs, row_ctx, 0, workspace, workspace_bytes);
   if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
-  if (num_pages == 0 || !q_fp4 || !q_scale || !w || !block_table || !payload || !scale || !logits)
-    return FP4IDX_E_INVALID;
-  if (!aligned(q_fp4, 16) || !aligned(w, 16) || !aligned(payload, 16) || !aligned(scale, 4)) return FP4IDX_E_INVALID;
-  return FP4IDX_OK;
+  return check_planned_args(q_fp4, q_scale, w, n_rows, n_heads, indptr, n_reqs, row_ctx, block_table, bt_stride,
+                            payload, scale, num_pages, logits, logits_stride);
 }
 
 // Plan and run in sequence on one stream.  Armed timing events stamp the
@@ -160,6 +186,27 @@ hipError_t planned_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const fl
                                       bt_stride, payload, scale, num_pages, logits, logits_stride, workspace,
                                       workspace_bytes, stream);
   return e;
+}
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's scratch address (FP4IDX_E_LAUNCH when the lookup fails).
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP4IDX_E_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return FP4IDX_E_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    const std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4IDX_E_LAUNCH;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP4IDX_OK;
 }
 
 }  // namespace
@@ -282,6 +329,29 @@ int fp4idx_mqa_logits(const uint8_t* q_fp4, const uint8_t* q_scale, const float*
   return launched(planned_logits(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, block_table,
                                  bt_stride, payload, scale, num_pages, logits, logits_stride, workspace,
                                  (int64_t)workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int fp4idx_mqa_logits_noalloc(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
+                              int32_t n_heads, const int32_t* req_row_indptr, int32_t n_reqs,
+                              const int32_t* row_ctx_len, const int32_t* block_table, int32_t bt_stride,
+                              const uint8_t* payload, const uint8_t* scale, int64_t num_pages, float* logits,
+                              int64_t logits_stride, void* stream) {
+  const TimingScope timing_scope;
+  const int rc = check_planned_args(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len,
+                                    block_table, bt_stride, payload, scale, num_pages, logits, logits_stride);
+  if (rc != FP4IDX_OK || n_rows == 0 || n_reqs == 0) return rc;
+  // the workspace fp4idx_mqa_logits would be given for this batch
+  const int64_t ctx_bound = std::min<int64_t>(logits_stride, (int64_t)bt_stride * FP4IDX_PAGE_TOKENS);
+  const int64_t need = fp4idx::plan_workspace_bytes(n_rows, n_reqs, ctx_bound);
+  if (need > (int64_t)FP4IDX_SCRATCH_BYTES) return FP4IDX_E_SCRATCH;
+  const int dev = check_device();
+  if (dev != FP4IDX_OK) return dev;
+  void* ws = nullptr;
+  const int sc = scratch_of_current_device(&ws);
+  if (sc != FP4IDX_OK) return sc;
+  return launched(planned_logits(q_fp4, q_scale, w, n_rows, n_heads, req_row_indptr, n_reqs, row_ctx_len, block_table,
+                                 bt_stride, payload, scale, num_pages, logits, logits_stride, ws, need,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,

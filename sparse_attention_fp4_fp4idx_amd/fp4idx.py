@@ -29,7 +29,7 @@ MAX_TOPK = 2048
 FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_mqa_logits_plan",
-          "fp4idx_mqa_logits_run", "fp4idx_mqa_logits_bounded", "fp4idx_topk",
+          "fp4idx_mqa_logits_run", "fp4idx_mqa_logits_bounded", "fp4idx_mqa_logits_noalloc", "fp4idx_topk",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
           "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_mfma_valu",
           "fp4idx_peak_read")
@@ -63,6 +63,7 @@ def load():
     lib.fp4idx_mqa_logits.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, sz, P]
     lib.fp4idx_mqa_logits_run.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P, sz, P]
     lib.fp4idx_mqa_logits_plan.argtypes = [i64, i32, P, i32, P, i64, P, sz, P]
+    lib.fp4idx_mqa_logits_noalloc.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, P]
     lib.fp4idx_mqa_logits_bounded.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_mqa_logits_workspace_bytes.argtypes = [i64, i32, i64]
     lib.fp4idx_mqa_logits_workspace_bytes.restype = ctypes.c_size_t
@@ -370,6 +371,9 @@ def _workspace_arg(ws: torch.Tensor):
     return [_ptr(ws, _U8, "workspace"), int(ws.numel())]
 
 
+_NO_WORKSPACE = object()  # _planned_args for the call that takes none
+
+
 def _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits, workspace,
                   max_ctx, stream, what="mqa_logits"):
     """Arguments of fp4idx_mqa_logits / fp4idx_mqa_logits_run.  Without
@@ -388,16 +392,20 @@ def _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, paylo
                     (row_ctx, "row_ctx"), (payload, "payload"), (scale, "scale")):
         _need(t.is_contiguous(), what, f"{name} must be contiguous")
     num_pages = _split_pool_pages(what, payload, scale)
-    if workspace is None:
-        bound = min(width, int(block_table.shape[1]) * PAGE_TOKENS)
-        workspace = new_workspace(T, n_reqs, bound, q_fp4.device)
-    _need(workspace.is_contiguous() and workspace.dtype == torch.uint8, what,
-          "workspace must be a contiguous uint8 tensor")
+    if workspace is _NO_WORKSPACE:
+        ws_args = [None, 0]
+    else:
+        if workspace is None:
+            bound = min(width, int(block_table.shape[1]) * PAGE_TOKENS)
+            workspace = new_workspace(T, n_reqs, bound, q_fp4.device)
+        _need(workspace.is_contiguous() and workspace.dtype == torch.uint8, what,
+              "workspace must be a contiguous uint8 tensor")
+        ws_args = _workspace_arg(workspace)
     args = [_ptr(q_fp4, _U8, "q_fp4"), _ptr(q_scale, _U8, "q_scale"), _ptr(w, _F32, "w"), T, H,
             _ptr(req_row_indptr, _I32, "req_row_indptr"), n_reqs, _ptr(row_ctx, _I32, "row_ctx"),
             _ptr(block_table, _I32, "block_table"), _pitch(block_table), _ptr(payload, _U8, "payload"),
             _ptr(scale, _U8, "scale"), num_pages, _ptr(logits, _F32, "logits"), _pitch(logits)]
-    return args + _workspace_arg(workspace) + [_stream(stream)], logits, workspace
+    return args + ws_args + [_stream(stream)], logits, workspace
 
 
 def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor, req_row_indptr: torch.Tensor,
@@ -411,6 +419,20 @@ def fp4idx_mqa_logits(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tenso
     args, logits, _ = _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits,
                                     workspace, max_ctx, stream)
     _run("fp4idx_mqa_logits", args)
+    return logits
+
+
+def fp4idx_mqa_logits_noalloc(q_fp4: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor,
+                              req_row_indptr: torch.Tensor, row_ctx: torch.Tensor, block_table: torch.Tensor,
+                              payload: torch.Tensor, scale: torch.Tensor, logits: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    """fp4idx_mqa_logits with the schedule in the library's per-device
+    scratch array (no workspace, no device allocation: the caller passes the
+    logits buffer).  Calls that overlap on one device race."""
+    _need(logits is not None, "mqa_logits_noalloc", "give the logits buffer (this call allocates nothing)")
+    args, logits, _ = _planned_args(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_table, payload, scale, logits,
+                                    _NO_WORKSPACE, None, stream, what="mqa_logits_noalloc")
+    _run("fp4idx_mqa_logits_noalloc", args[:-3] + args[-1:])
     return logits
 
 
@@ -746,6 +768,7 @@ write_k = fp4idx_write_k
 pack_q = fp4idx_pack_q
 mqa_logits = fp4idx_mqa_logits
 mqa_logits_bounded = fp4idx_mqa_logits_bounded
+mqa_logits_noalloc = fp4idx_mqa_logits_noalloc
 mqa_logits_workspace_bytes = fp4idx_mqa_logits_workspace_bytes
 topk = fp4idx_topk
 write_k_pack_q = fp4idx_write_k_pack_q
