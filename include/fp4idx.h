@@ -104,7 +104,7 @@ int fp4idx_write_k(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_row_strid
  *
  *   q_bf16   [n_rows, q_row_stride] bf16 bits; head h of row t is the 128
  *            elements at t*q_row_stride + h*128
- *   n_heads  16, 32, 64 or 128
+ *   n_heads  a multiple of 16, from 16 to 128
  *   pos      [n_rows] int32 RoPE position of each query row, 0 <= pos < max_pos;
  *            a row with pos outside that range is encoded as the zero vector
  *   w_in     [n_rows, n_heads] fp32 head weights
@@ -146,7 +146,7 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
  * with qhat, khat the dequantised FP4 vectors (e2m1 * 2^(byte-127)).
  *
  *   q_fp4, q_scale, w   as produced by fp4idx_pack_q ([n_rows, n_heads, ...]);
- *                       n_heads 16, 32, 64 or 128
+ *                       n_heads a multiple of 16, from 16 to 128
  *   req_row_indptr      [n_reqs+1] int32: rows of request b are
  *                       [indptr[b], indptr[b+1]); indptr[0] = 0, indptr[n_reqs] = n_rows,
  *                       non-decreasing (each bound is clamped into [0, n_rows] and
@@ -287,16 +287,27 @@ int fp4idx_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, cons
  * not in pool-slot order).
  *
  *   logits      [n_rows, logits_stride] fp32; row t uses [0, ctx[t]); finite values
- *   row_ctx_len [n_rows] int32, 0 <= ctx[t] <= max_ctx <= logits_stride (a
- *               value outside that range is cut into it; that row's result
- *               is then unspecified)
+ *   row_ctx_len [n_rows] int32, 0 <= ctx[t] <= logits_stride (a value
+ *               outside that range is cut into it; that row's result is then
+ *               unspecified)
  *   k           1 <= k <= FP4IDX_MAX_TOPK
  *   out_idx     [n_rows, k] int32 (out): the min(k, ctx[t]) positions with the
  *               largest values (ties: lower position first), ascending by
  *               position, then -1.  -0.0 and +0.0 compare equal.
+ * The kernel variant (register band, rows per work-group) is picked for rows
+ * of up to logits_stride values; fp4idx_topk_bounded takes a tighter bound.
  */
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
-                int32_t* out_idx, int64_t max_ctx, void* stream);
+                int32_t* out_idx, void* stream);
+
+/*
+ * fp4idx_topk with a host bound on the contexts: 0 <= ctx[t] <= max_ctx <=
+ * logits_stride (a larger ctx[t] is cut to max_ctx), so that logits rows
+ * wider than their contexts still get the variant sized for max_ctx.
+ * Results equal fp4idx_topk's whenever every ctx[t] <= max_ctx.
+ */
+int fp4idx_topk_bounded(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len,
+                        int32_t k, int32_t* out_idx, int64_t max_ctx, void* stream);
 
 /*
  * Fused logits + top-k: the top-k positions of every row without writing the
@@ -304,7 +315,7 @@ int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, cons
  * paged-MQA logits of [P2] Modifications (decode logits dispatch).
  *
  * Arguments as fp4idx_mqa_logits (without the logits buffer) plus k and
- * out_idx as fp4idx_topk; n_heads 16, 32 or 64; max_ctx <=
+ * out_idx as fp4idx_topk; n_heads 16, 32, 48 or 64; max_ctx <=
  * FP4IDX_FUSED_MAX_CTX (the row is held in LDS); max_rows_per_req >= 1 when
  * n_rows > 0.  out_idx [n_rows, k] int32 receives exactly what
  * fp4idx_mqa_logits followed by fp4idx_topk would write (same logits bit

@@ -47,6 +47,9 @@ int check_device() {
   return a == 1 ? FP4IDX_OK : FP4IDX_E_UNSUPPORTED;
 }
 
+// Index head counts: a multiple of 16 (one MFMA M tile) up to 128.
+inline bool valid_heads(int32_t n_heads) { return n_heads >= 16 && n_heads <= 128 && n_heads % 16 == 0; }
+
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 inline int launched(hipError_t e) { return e == hipSuccess ? FP4IDX_OK : FP4IDX_E_LAUNCH; }
@@ -99,7 +102,7 @@ int check_pack_q(const uint16_t* q_bf16, int64_t n_rows, int32_t n_heads, int64_
                  const uint16_t* cos_sin_bf16, int32_t max_pos, const float* w_in, const uint8_t* q_fp4,
                  const uint8_t* q_scale, const float* w_out) {
   if (n_rows < 0 || max_pos <= 0) return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (!valid_heads(n_heads)) return FP4IDX_E_INVALID;
   if (q_row_stride < (int64_t)n_heads * FP4IDX_HEAD_DIM || (q_row_stride % 8) != 0) return FP4IDX_E_INVALID;
   if (n_rows == 0) return FP4IDX_OK;
   if (!q_bf16 || !pos || !cos_sin_bf16 || !w_in || !q_fp4 || !q_scale || !w_out) return FP4IDX_E_INVALID;
@@ -115,7 +118,7 @@ int check_logits(int64_t n_rows, int32_t n_heads, int32_t n_reqs, int32_t bt_str
   if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || logits_stride < 0 || max_rows_per_req < 0 ||
       max_ctx < 0)
     return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (!valid_heads(n_heads)) return FP4IDX_E_INVALID;
   if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > logits_stride) return FP4IDX_E_INVALID;
   if (max_rows_per_req > n_rows || n_reqs > 65535 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0 || max_ctx == 0 || max_rows_per_req == 0) return FP4IDX_OK;
@@ -127,7 +130,7 @@ int check_logits(int64_t n_rows, int32_t n_heads, int32_t n_reqs, int32_t bt_str
 int check_plan(int64_t n_rows, int32_t n_heads, const int32_t* indptr, int32_t n_reqs, const int32_t* row_ctx,
                int64_t max_ctx, const void* workspace, size_t workspace_bytes) {
   if (n_rows < 0 || n_reqs < 0 || max_ctx < 0 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (!valid_heads(n_heads)) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
   if (!indptr || !row_ctx) return FP4IDX_E_INVALID;
   if (!workspace || !aligned(workspace, 16) || workspace_bytes > (size_t)INT64_MAX) return FP4IDX_E_WORKSPACE;
@@ -146,7 +149,7 @@ int check_planned_args(const uint8_t* q_fp4, const uint8_t* q_scale, const float
                        int64_t num_pages, const float* logits, int64_t logits_stride) {
   if (bt_stride < 0 || num_pages < 0 || logits_stride < 0) return FP4IDX_E_INVALID;
   if (n_rows < 0 || n_reqs < 0 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128) return FP4IDX_E_INVALID;
+  if (!valid_heads(n_heads)) return FP4IDX_E_INVALID;
   if (n_rows == 0 || n_reqs == 0) return FP4IDX_OK;
   if (!indptr || !row_ctx) return FP4IDX_E_INVALID;
   if (num_pages == 0 || !q_fp4 || !q_scale || !w || !block_table || !payload || !scale || !logits)
@@ -362,7 +365,7 @@ int fp4idx_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, const f
   const TimingScope timing_scope;
   if (n_rows < 0 || n_reqs < 0 || num_pages < 0 || bt_stride < 0 || max_rows_per_req < 0 || max_ctx < 0)
     return FP4IDX_E_INVALID;
-  if (n_heads != 16 && n_heads != 32 && n_heads != 64) return FP4IDX_E_INVALID;
+  if (!valid_heads(n_heads) || n_heads > 64) return FP4IDX_E_INVALID;
   if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;
   if (max_ctx > (int64_t)bt_stride * FP4IDX_PAGE_TOKENS || max_ctx > FP4IDX_FUSED_MAX_CTX) return FP4IDX_E_INVALID;
   if (max_rows_per_req > n_rows || n_reqs > 65535 || n_rows > 0x7FFFFFFF) return FP4IDX_E_INVALID;
@@ -428,7 +431,12 @@ int fp4idx_peak_read(const uint8_t* buf, int64_t bytes, uint32_t* sink, void* st
 }
 
 int fp4idx_topk(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len, int32_t k,
-                int32_t* out_idx, int64_t max_ctx, void* stream) {
+                int32_t* out_idx, void* stream) {
+  return fp4idx_topk_bounded(logits, n_rows, logits_stride, row_ctx_len, k, out_idx, logits_stride, stream);
+}
+
+int fp4idx_topk_bounded(const float* logits, int64_t n_rows, int64_t logits_stride, const int32_t* row_ctx_len,
+                        int32_t k, int32_t* out_idx, int64_t max_ctx, void* stream) {
   const TimingScope timing_scope;
   if (n_rows < 0 || logits_stride < 0 || max_ctx < 0 || max_ctx > logits_stride) return FP4IDX_E_INVALID;
   if (k < 1 || k > FP4IDX_MAX_TOPK) return FP4IDX_E_INVALID;

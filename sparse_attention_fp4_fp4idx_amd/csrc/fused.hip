@@ -154,19 +154,11 @@ hipError_t launch_mqa_logits_topk(const uint8_t* q_fp4, const uint8_t* q_scale, 
                                   const uint8_t* scale, int64_t num_pages, int32_t k, int32_t* out_idx,
                                   int32_t max_rows_per_req, int64_t max_ctx, hipStream_t stream) {
   if (max_ctx > kFusedMaxCtx || n_rows > 0x7FFFFFFFLL || n_reqs > 65535) return hipErrorInvalidConfiguration;
-  switch (n_heads) {
-    case 16:
-      return launch_fused_nmt<1>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
-    case 32:
-      return launch_fused_nmt<2>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
-    case 64:
-      return launch_fused_nmt<4>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride, payload, scale,
-                                 num_pages, k, out_idx, max_rows_per_req, max_ctx, (int32_t)n_rows, stream);
-    default:
-      return hipErrorInvalidValue;
-  }
+  return with_head_tiles<4>(n_heads, [&](auto nmt) {
+    return launch_fused_nmt<decltype(nmt)::value>(q_fp4, q_scale, w, indptr, n_reqs, row_ctx, block_table, bt_stride,
+                                                 payload, scale, num_pages, k, out_idx, max_rows_per_req, max_ctx,
+                                                 (int32_t)n_rows, stream);
+  });
 }
 
 }  // namespace fp4idx

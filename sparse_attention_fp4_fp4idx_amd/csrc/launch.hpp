@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "schedule.hpp"
 
 namespace fp4idx {
@@ -31,6 +33,32 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32
     hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, static_cast<KArgs>(args)...);
   }
   return hipGetLastError();
+}
+
+// f(std::integral_constant<int, NMT>{}) for the head count's 16-head M tiles,
+// NMT = n_heads / 16 (head counts 16, 32, ..., 16 * MAX_NMT); any other count
+// is hipErrorInvalidValue.
+template <int N, int MAX_NMT, typename F>
+inline hipError_t call_head_tiles(F& f) {
+  if constexpr (N <= MAX_NMT)
+    return f(std::integral_constant<int, N>{});
+  else
+    return hipErrorInvalidValue;
+}
+template <int MAX_NMT = 8, typename F>
+inline hipError_t with_head_tiles(int n_heads, F&& f) {
+  if (n_heads <= 0 || n_heads % 16 != 0) return hipErrorInvalidValue;
+  switch (n_heads / 16) {
+    case 1: return call_head_tiles<1, MAX_NMT>(f);
+    case 2: return call_head_tiles<2, MAX_NMT>(f);
+    case 3: return call_head_tiles<3, MAX_NMT>(f);
+    case 4: return call_head_tiles<4, MAX_NMT>(f);
+    case 5: return call_head_tiles<5, MAX_NMT>(f);
+    case 6: return call_head_tiles<6, MAX_NMT>(f);
+    case 7: return call_head_tiles<7, MAX_NMT>(f);
+    case 8: return call_head_tiles<8, MAX_NMT>(f);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_write_k(const uint16_t* k, int64_t n_tokens, int64_t k_row_stride, const int32_t* pos,

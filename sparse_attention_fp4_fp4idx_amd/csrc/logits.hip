@@ -566,7 +566,7 @@ static hipError_t launch_rw(const LogitsCall& c) {
 
 template <typename FMT, int NMT>
 static hipError_t launch_nmt(const LogitsCall& c) {
-  constexpr int cap = NMT == 8 ? FMT::kRowsCapWide : FMT::kRowsCap;
+  constexpr int cap = NMT > 4 ? FMT::kRowsCapWide : FMT::kRowsCap;
   const int r = c.max_rows_per_req;
   if (r <= 1) return launch_rw<FMT, 1, NMT, FMT::kPpw1, FMT::kD1>(c);
   if constexpr (cap <= 2) {
@@ -580,13 +580,7 @@ static hipError_t launch_nmt(const LogitsCall& c) {
 
 template <typename FMT>
 static hipError_t launch_heads(const LogitsCall& c, int n_heads) {
-  switch (n_heads) {
-    case 16: return launch_nmt<FMT, 1>(c);
-    case 32: return launch_nmt<FMT, 2>(c);
-    case 64: return launch_nmt<FMT, 4>(c);
-    case 128: return launch_nmt<FMT, 8>(c);
-    default: return hipErrorInvalidValue;
-  }
+  return with_head_tiles(n_heads, [&](auto nmt) { return launch_nmt<FMT, decltype(nmt)::value>(c); });
 }
 
 // FP4 batches of requests with three or more rows each on average: the
@@ -606,7 +600,7 @@ static hipError_t launch_fp4_shared(const LogitsCall& c, bool uniform) {
   const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 4;
   const int r = c.max_rows_per_req;
   if (!uniform || r <= 4) return launch_shared<2, 2, NMT>(c, page_rows);
-  if constexpr (NMT != 8) {
+  if constexpr (NMT <= 4) {
     if (r <= 6) return launch_shared<2, 3, NMT>(c, page_rows);
   }
   return launch_shared<4, 2, NMT>(c, page_rows);
@@ -631,13 +625,7 @@ hipError_t launch_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scal
   const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
   const int64_t avg_rows = n_reqs > 0 ? (n_rows + n_reqs - 1) / n_reqs : 0;
   if (max_rows_per_req <= 2 || avg_rows < 3) return launch_heads<Fp4Split>(c, n_heads);
-  switch (n_heads) {
-    case 16: return launch_fp4_shared<1>(c, uniform);
-    case 32: return launch_fp4_shared<2>(c, uniform);
-    case 64: return launch_fp4_shared<4>(c, uniform);
-    case 128: return launch_fp4_shared<8>(c, uniform);
-    default: return hipErrorInvalidValue;
-  }
+  return with_head_tiles(n_heads, [&](auto nmt) { return launch_fp4_shared<decltype(nmt)::value>(c, uniform); });
 }
 
 // ---- the scheduled path: the plan (schedule.hip), then one work-group per item
@@ -651,7 +639,7 @@ PlanShape plan_shape(int64_t n_rows, int32_t n_reqs, int n_heads) {
   const int64_t avg10 = n_reqs > 0 ? 10 * n_rows / n_reqs : 0;  // rows per request x 10
   if (avg10 < 15) return PlanShape{0, 1};
   if (avg10 < 30) return PlanShape{0, 2};
-  if (n_heads == 128) return avg10 >= 60 ? PlanShape{4, 8} : PlanShape{2, 4};
+  if (n_heads > 64) return avg10 >= 60 ? PlanShape{4, 8} : PlanShape{2, 4};
   if (avg10 >= 70) return PlanShape{4, 8};
   if (avg10 >= 45) return PlanShape{2, 6};
   return PlanShape{2, 4};
@@ -699,7 +687,7 @@ template <int NMT>
 static int planned_resident(const PlanShape& sh) {
   if (sh.waves == 0) return 0;
   if (sh.waves == 4) return resident_groups(mqa_logits_planned_kernel<4, 2, NMT>, 256);
-  if constexpr (NMT != 8) {
+  if constexpr (NMT <= 4) {
     if (sh.rows == 6) return resident_groups(mqa_logits_planned_kernel<2, 3, NMT>, 128);
   }
   return resident_groups(mqa_logits_planned_kernel<2, 2, NMT>, 128);
@@ -734,7 +722,7 @@ static hipError_t launch_planned_nmt(const LogitsCall& c, PlanShape sh, const in
     return launch_wave_planned<2, NMT>(c, ws, grid, cap_items, sz);
   }
   if (sh.waves == 4) return launch_planned<4, 2, NMT>(c, ws, grid, cap_items, sz);
-  if constexpr (NMT != 8) {
+  if constexpr (NMT <= 4) {
     if (sh.rows == 6) return launch_planned<2, 3, NMT>(c, ws, grid, cap_items, sz);
   }
   return launch_planned<2, 2, NMT>(c, ws, grid, cap_items, sz);
@@ -747,12 +735,11 @@ hipError_t launch_mqa_logits_plan(int64_t n_rows, int n_heads, const int32_t* in
   const PlanSizes sz = plan_sizes(n_rows, n_reqs, sh.rows);
   const int64_t cap = plan_capacity(sz, workspace_bytes);
   int resident = 0;
-  switch (n_heads) {
-    case 16: resident = planned_resident<1>(sh); break;
-    case 32: resident = planned_resident<2>(sh); break;
-    case 64: resident = planned_resident<4>(sh); break;
-    default: resident = planned_resident<8>(sh); break;
-  }
+  const hipError_t e = with_head_tiles(n_heads, [&](auto nmt) {
+    resident = planned_resident<decltype(nmt)::value>(sh);
+    return hipSuccess;
+  });
+  if (e != hipSuccess) return e;
   return launch_plan(indptr, n_reqs, n_rows, row_ctx, max_ctx, static_cast<int32_t*>(workspace), cap, sz, sh,
                      sh.waves == 0 ? wave_item_pages(sh) : 0, kItemTarget, resident, stream);
 }
@@ -776,13 +763,9 @@ hipError_t launch_mqa_logits_run(const uint8_t* q_fp4, const uint8_t* q_scale, c
                      block_table, bt_stride, payload, scale,     num_pages, logits,          logits_stride,
                      0,           0,         stream};
   const int32_t* ws = static_cast<const int32_t*>(workspace);
-  switch (n_heads) {
-    case 16: return launch_planned_nmt<1>(c, sh, ws, grid, cap, sz);
-    case 32: return launch_planned_nmt<2>(c, sh, ws, grid, cap, sz);
-    case 64: return launch_planned_nmt<4>(c, sh, ws, grid, cap, sz);
-    case 128: return launch_planned_nmt<8>(c, sh, ws, grid, cap, sz);
-    default: return hipErrorInvalidValue;
-  }
+  return with_head_tiles(n_heads, [&](auto nmt) {
+    return launch_planned_nmt<decltype(nmt)::value>(c, sh, ws, grid, cap, sz);
+  });
 }
 
 hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, const float* w, int64_t n_rows,

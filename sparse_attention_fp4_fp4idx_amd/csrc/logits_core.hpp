@@ -51,7 +51,7 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
 // [page][block][token] and its UE8M0 byte; A lane l = (head l%16, block l/16).
 struct Fp4Split {
   // Launch shapes (64 heads or fewer for the wave counts): rows per wave
-  // at most (kRowsCapWide at 128 heads), and per rows-per-wave class the
+  // at most (kRowsCapWide past 64 heads), and per rows-per-wave class the
   // resident waves per SIMD asked of the compiler, the pages per wave and
   // the pages in flight.
   static constexpr int kRowsCap = 4, kRowsCapWide = 4;
@@ -128,7 +128,7 @@ struct Fp4Lds {
 struct Fp8Fused {
   // launch shapes as for Fp4Split; 8-register operands and 36-register pages
   // need more registers per row and per page in flight
-  static constexpr int kRowsCap = 4, kRowsCapWide = 2;   // 3+ rows at 128 heads spill
+  static constexpr int kRowsCap = 4, kRowsCapWide = 2;   // 3+ rows past 64 heads spill
   static constexpr int kWaves1 = 2, kPpw1 = 4, kD1 = 4;
   static constexpr int kWaves2 = 1, kPpw2 = 4, kD2 = 4;
   static constexpr int kPpwMany = 8, kDMany = 4;

@@ -30,6 +30,7 @@ FUSED_MAX_CTX = 32768
 
 _CALLS = ("fp4idx_write_k", "fp4idx_pack_q", "fp4idx_write_k_pack_q", "fp4idx_mqa_logits", "fp4idx_mqa_logits_plan",
           "fp4idx_mqa_logits_run", "fp4idx_mqa_logits_bounded", "fp4idx_mqa_logits_noalloc", "fp4idx_topk",
+          "fp4idx_topk_bounded",
           "fp4idx_mqa_logits_topk", "fp4idx_read_k", "fp4idx_write_k_fp8", "fp4idx_pack_q_fp8", "fp4idx_write_k_pack_q_fp8",
           "fp4idx_mqa_logits_fp8", "fp4idx_peak_mfma_fp4", "fp4idx_peak_valu_fp32", "fp4idx_peak_mfma_valu",
           "fp4idx_peak_read")
@@ -67,7 +68,8 @@ def load():
     lib.fp4idx_mqa_logits_bounded.argtypes = [P, P, P, i64, i32, P, i32, P, P, i32, P, P, i64, P, i64, i32, i64, P]
     lib.fp4idx_mqa_logits_workspace_bytes.argtypes = [i64, i32, i64]
     lib.fp4idx_mqa_logits_workspace_bytes.restype = ctypes.c_size_t
-    lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, i64, P]
+    lib.fp4idx_topk.argtypes = [P, i64, i64, P, i32, P, P]
+    lib.fp4idx_topk_bounded.argtypes = [P, i64, i64, P, i32, P, i64, P]
     lib.fp4idx_read_k.argtypes = [P, P, i64, P, i64, P, i64, P]
     lib.fp4idx_peak_mfma_fp4.argtypes = [i32, P, P]
     lib.fp4idx_peak_valu_fp32.argtypes = [i32, P, P]
@@ -566,12 +568,15 @@ def prepare_mqa_logits_topk(q_fp4, q_scale, w, req_row_indptr, row_ctx, block_ta
 
 
 def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
+    """Arguments of fp4idx_topk (max_ctx None) or fp4idx_topk_bounded: (name, args, out_idx)."""
     _need(logits.dim() == 2, "topk", "logits must be [T, stride]")
     T = int(logits.shape[0])
     if logits.stride(-1) != 1:
         raise Fp4idxError("topk: logits must have unit inner stride")
     _need(row_ctx.numel() == T, "topk", f"row_ctx must hold one context length per row ({T})")
-    _need(0 <= int(max_ctx) <= logits.shape[1], "topk", f"max_ctx {max_ctx} exceeds the logits rows ({logits.shape[1]})")
+    if max_ctx is not None:
+        _need(0 <= int(max_ctx) <= logits.shape[1], "topk",
+              f"max_ctx {max_ctx} exceeds the logits rows ({logits.shape[1]})")
     if out_idx is not None:
         _shape(out_idx, (T, int(k)), "topk", "out_idx")
     if out_idx is None:
@@ -579,22 +584,31 @@ def _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream):
     if not out_idx.is_contiguous() or not row_ctx.is_contiguous():
         raise Fp4idxError("topk: out_idx and row_ctx must be contiguous")
     args = [_ptr(logits, _F32, "logits"), T, _pitch(logits), _ptr(row_ctx, _I32, "row_ctx"), int(k),
-            _ptr(out_idx, _I32, "out_idx"), int(max_ctx), _stream(stream)]
-    return args, out_idx
+            _ptr(out_idx, _I32, "out_idx")]
+    if max_ctx is None:
+        return "fp4idx_topk", args + [_stream(stream)], out_idx
+    return "fp4idx_topk_bounded", args + [int(max_ctx), _stream(stream)], out_idx
 
 
-def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int, out_idx: torch.Tensor = None,
-                stream=None) -> torch.Tensor:
-    """[T, k] int32: top-k positions per row, ascending, then -1."""
-    args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
-    _run("fp4idx_topk", args)
+def fp4idx_topk(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int = None,
+                out_idx: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """[T, k] int32: top-k positions per row, ascending, then -1.  With
+    max_ctx (a host bound on the contexts) fp4idx_topk_bounded runs."""
+    name, args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
+    _run(name, args)
     return out_idx
 
 
-def prepare_topk(logits, row_ctx, k, max_ctx, out_idx=None, stream=None):
-    """fp4idx_topk with its arguments marshalled once: (Prepared, out_idx)."""
-    args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
-    return Prepared("fp4idx_topk", args, keep=(logits, row_ctx, out_idx)), out_idx
+def fp4idx_topk_bounded(logits: torch.Tensor, row_ctx: torch.Tensor, k: int, max_ctx: int,
+                        out_idx: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """fp4idx_topk with the host bound max_ctx on the contexts."""
+    return fp4idx_topk(logits, row_ctx, k, max_ctx, out_idx, stream)
+
+
+def prepare_topk(logits, row_ctx, k, max_ctx=None, out_idx=None, stream=None):
+    """fp4idx_topk (or _bounded) with its arguments marshalled once: (Prepared, out_idx)."""
+    name, args, out_idx = _topk_args(logits, row_ctx, k, max_ctx, out_idx, stream)
+    return Prepared(name, args, keep=(logits, row_ctx, out_idx)), out_idx
 
 
 def fp4idx_read_k(payload: torch.Tensor, scale: torch.Tensor, slot: torch.Tensor, out: torch.Tensor = None,
@@ -771,6 +785,7 @@ mqa_logits_bounded = fp4idx_mqa_logits_bounded
 mqa_logits_noalloc = fp4idx_mqa_logits_noalloc
 mqa_logits_workspace_bytes = fp4idx_mqa_logits_workspace_bytes
 topk = fp4idx_topk
+topk_bounded = fp4idx_topk_bounded
 write_k_pack_q = fp4idx_write_k_pack_q
 read_k = fp4idx_read_k
 time_next_call = fp4idx_time_next_call

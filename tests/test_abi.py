@@ -60,7 +60,7 @@ def test_host_validation_rejects_before_any_launch(F):
     assert lib.fp4idx_write_k(fake, -1, 128, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1, None) == E
     assert lib.fp4idx_write_k(None, 0, 128, None, None, None, 1e-6, None, 10, None, None, 0, None) == 0
     # pack_q: unsupported head counts, short stride
-    for h in (0, 8, 48, 256):
+    for h in (0, 8, 40, 144, 256):
         assert lib.fp4idx_pack_q(fake, 2, h, 128 * 64, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     assert lib.fp4idx_pack_q(fake, 2, 64, 100, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     # logits: ctx bound beyond the block table or the logits row
@@ -74,22 +74,25 @@ def test_host_validation_rejects_before_any_launch(F):
                                          4, 128, None) == E
     # top-k: k out of range, ctx bound beyond the row
     for k in (0, -3, 2049):
-        assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, 10, None) == E
-    assert lib.fp4idx_topk(fake, 1, 100, fake, 16, fake, 101, None) == E
+        assert lib.fp4idx_topk(fake, 1, 100, fake, k, fake, None) == E
+        assert lib.fp4idx_topk_bounded(fake, 1, 100, fake, k, fake, 10, None) == E
+    assert lib.fp4idx_topk_bounded(fake, 1, 100, fake, 16, fake, 101, None) == E
+    assert lib.fp4idx_topk(fake, 1, -1, fake, 16, fake, None) == E
     # write_k_pack_q: each half is checked as its own call would check it
     wk = [fake, 5, 128, fake, fake, fake, 1e-6, fake, 10, fake, fake, 1]
     pq = [fake, 2, 64, 128 * 64, fake, fake, 1.0, fake, fake, fake]
     assert lib.fp4idx_write_k_pack_q(*wk[:2], 100, *wk[3:], *pq, None) == E          # K row stride
-    assert lib.fp4idx_write_k_pack_q(*wk, fake, 2, 48, *pq[3:], None) == E           # head count
+    assert lib.fp4idx_write_k_pack_q(*wk, fake, 2, 40, *pq[3:], None) == E           # head count
     assert lib.fp4idx_write_k_pack_q(*wk, None, 2, 64, *pq[3:], None) == E           # null Q
     assert lib.fp4idx_write_k_pack_q(None, 0, 128, None, None, None, 1e-6, None, 10, None, None, 0,
                                      None, 0, 64, 128 * 64, None, None, 1.0, None, None, None, None) == 0
     # timing events armed before a rejected call are dropped with it (no launch, events untouched)
     assert lib.fp4idx_time_next_call(None, None) == 0
     assert lib.fp4idx_time_next_call(fake, fake) == 0
-    assert lib.fp4idx_topk(fake, 1, 100, fake, 0, fake, 10, None) == E
+    assert lib.fp4idx_topk_bounded(fake, 1, 100, fake, 0, fake, 10, None) == E
     # empty problems are a successful no-op
-    assert lib.fp4idx_topk(None, 0, 100, None, 16, None, 10, None) == 0
+    assert lib.fp4idx_topk(None, 0, 100, None, 16, None, None) == 0
+    assert lib.fp4idx_topk_bounded(None, 0, 100, None, 16, None, 10, None) == 0
     assert lib.fp4idx_mqa_logits_bounded(None, None, None, 0, 64, None, 0, None, None, 0, None, None, 0, None, 0, 0,
                                          0, None) == 0
 
@@ -122,7 +125,8 @@ def test_scheduled_logits_validate_workspace_and_arguments(F):
         assert call(fn, a15=None) == EW                       # no workspace
         assert call(fn, a15=ctypes.c_void_p(0x1008)) == EW    # not 16-byte aligned
         assert call(fn, a16=64) == EW                         # too small for the batch's row blocks
-        assert call(fn, a4=48) == E
+        assert call(fn, a4=48 + 8) == E
+        assert call(fn, a4=144) == E
         assert call(fn, a3=-1) == E
         assert call(fn, a12=0) == E                           # rows but no pool
         assert call(fn, a0=None) == E
@@ -152,7 +156,7 @@ def test_fp8_calls_validate_like_their_fp4_twins(F):
     assert lib.fp4idx_write_k_fp8(fake, 5, 128, fake, fake, fake, -1.0, fake, 10, fake, 1, None) == E
     assert lib.fp4idx_write_k_fp8(None, 0, 128, None, None, None, 1e-6, None, 10, None, 0, None) == 0
     # pack_q_fp8: head counts, stride, unaligned code output
-    for h in (0, 8, 48, 256):
+    for h in (0, 8, 40, 144, 256):
         assert lib.fp4idx_pack_q_fp8(fake, 2, h, 128 * 64, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     assert lib.fp4idx_pack_q_fp8(fake, 2, 64, 100, fake, fake, 10, fake, 1.0, fake, fake, fake, None) == E
     assert lib.fp4idx_pack_q_fp8(fake, 2, 64, 128 * 64, fake, fake, 10, fake, 1.0, ctypes.c_void_p(0x1004), fake,
@@ -161,7 +165,7 @@ def test_fp8_calls_validate_like_their_fp4_twins(F):
     wk = [fake, 5, 128, fake, fake, fake, 1e-6, fake, 10, fake, 1]
     pq = [fake, 2, 64, 128 * 64, fake, fake, 1.0, fake, fake, fake]
     assert lib.fp4idx_write_k_pack_q_fp8(*wk[:2], 100, *wk[3:], *pq, None) == E
-    assert lib.fp4idx_write_k_pack_q_fp8(*wk, fake, 2, 48, *pq[3:], None) == E
+    assert lib.fp4idx_write_k_pack_q_fp8(*wk, fake, 2, 40, *pq[3:], None) == E
     assert lib.fp4idx_write_k_pack_q_fp8(None, 0, 128, None, None, None, 1e-6, None, 10, None, 0,
                                          None, 0, 64, 128 * 64, None, None, 1.0, None, None, None, None) == 0
     # logits_fp8: ctx bound beyond the table / the row, head count, unaligned scale, empty pool
@@ -192,7 +196,8 @@ def test_fused_logits_topk_validates_its_host_arguments(F):
         for i, v in kw.items():
             a[int(i[1:])] = v
         return lib.fp4idx_mqa_logits_topk(*a)
-    assert call(a4=128) == E            # 128 heads: not served by the fused call
+    assert call(a4=128) == E            # more than 64 heads: not served by the fused call
+    assert call(a4=80) == E
     assert call(a4=40) == E
     for k in (0, -1, 2049):
         assert call(a13=k) == E

@@ -139,7 +139,7 @@ def _same(a, b):
     return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-@pytest.mark.parametrize("heads", [64, 16, 32, 128])
+@pytest.mark.parametrize("heads", [64, 16, 32, 80, 128])
 def test_pack_q_fp8_bit_exact(F, orc, heads):
     rng = np.random.default_rng(130 + heads)
     T = 37
@@ -237,7 +237,7 @@ def _encoded_small(orc, wl):
     return qf, qs, w, pool
 
 
-@pytest.mark.parametrize("heads", [64, 16, 128])
+@pytest.mark.parametrize("heads", [64, 16, 128, 48, 112])
 def test_logits_fp8_small_mixed_all_scores(F, orc, heads):
     wl = W.small(heads=heads)
     qf, qs, w, pool = _encoded_small(orc, wl)

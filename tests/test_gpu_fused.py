@@ -57,7 +57,7 @@ def _encoded(orc, wl):
     return qf, qs, w, pay, sc
 
 
-@pytest.mark.parametrize("heads,k", [(64, 64), (16, 256), (32, 7), (64, 2048)])
+@pytest.mark.parametrize("heads,k", [(64, 64), (16, 256), (32, 7), (64, 2048), (48, 300)])
 def test_fused_equals_two_calls_small_mixed(F, orc, heads, k):
     """Single- and multi-row requests, ragged contexts, a zero-context row,
     rows shorter than k; the result against the two-call path, the oracle's

@@ -139,7 +139,7 @@ def _pack_both(F, orc, q, pos, tab, w, w_scale):
     return (qo, so, wo), (qg.cpu().numpy(), sg.cpu().numpy(), wg.cpu().numpy())
 
 
-@pytest.mark.parametrize("heads", [64, 16, 32, 128])
+@pytest.mark.parametrize("heads", [64, 16, 32, 48, 112, 128])
 def test_pack_q_small_bit_exact(F, orc, heads):
     rng = np.random.default_rng(22 + heads)
     T = 37
@@ -259,7 +259,7 @@ def _encoded_small(orc, wl):
     return qf, qs, w, pay, sc
 
 
-@pytest.mark.parametrize("heads", [64, 16, 128])
+@pytest.mark.parametrize("heads", [64, 16, 128, 48, 80, 96, 112])
 def test_logits_small_mixed_all_scores(F, orc, heads):
     wl = W.small(heads=heads)
     qf, qs, w, pay, sc = _encoded_small(orc, wl)
@@ -287,7 +287,9 @@ def test_logits_rows_per_request_variants(F, orc):
 
 @pytest.mark.parametrize("rows,heads", [((3, 3), 64), ((4, 4, 3), 64), ((5, 5), 64), ((8, 7), 64), ((10, 9), 64),
                                         ((12, 12), 64), ((13, 13), 64), ((16, 14), 32), ((4, 4), 128),
-                                        ((7, 7), 128), ((6, 5), 16), ((16, 1, 1), 64), ((14, 2, 5), 128)])
+                                        ((7, 7), 128), ((6, 5), 16), ((16, 1, 1), 64), ((14, 2, 5), 128),
+                                        ((6, 6), 48), ((8, 8), 48), ((5, 5), 80), ((9, 8), 96), ((4, 4), 112),
+                                        ((14, 2, 5), 112)])
 def test_logits_shared_page_kernel_every_shape(F, orc, rows, heads):
     """Batches with three or more rows per request on average go to the
     shared-page kernel; each rows-per-work-group shape it picks (near-uniform
@@ -537,9 +539,15 @@ def test_pools_and_logits_past_2_gib(F, orc):
 # ---------------------------------------------------------------- top-k
 
 def _gpu_topk(F, logits, ctx, k):
-    out = F.topk(dev(logits), dev(ctx), k, int(ctx.max(initial=0)))
+    """fp4idx_topk_bounded at the rows' longest context; fp4idx_topk (sized
+    by the logits row) must give the same indices."""
+    lg, cx = dev(logits), dev(ctx)
+    out = F.topk(lg, cx, k, int(ctx.max(initial=0)))
+    plain = F.topk(lg, cx, k)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    out = out.cpu().numpy()
+    assert np.array_equal(out, plain.cpu().numpy()), "fp4idx_topk and fp4idx_topk_bounded differ"
+    return out
 
 
 def test_topk_edges_and_ties_bit_exact(F, orc):

@@ -114,7 +114,7 @@ def test_plan_covers_every_row_page_exactly_once(F, case):
         indptr, ctx = wl.req_row_indptr, wl.row_ctx
     n_rows, n_reqs = int(indptr[-1]), indptr.size - 1
     max_ctx = int(ctx.max(initial=0)) + 1
-    for heads in (64, 128):
+    for heads in (64, 128, 96):
         plan = F.LogitsPlan(heads, dev(indptr), dev(ctx), max_ctx).build()
         torch.cuda.synchronize()
         n_items, rows_pb, waves = _check_schedule(plan.workspace, indptr, ctx, max_ctx, n_rows)

@@ -43,7 +43,7 @@ def test_noalloc_refuses_batches_past_its_scratch():
     small[0] = None                                     # null Q: the host checks still run first
     assert lib.fp4idx_mqa_logits_noalloc(*small) == E_INVALID
     small = list(args)
-    small[4] = 48                                       # head count
+    small[4] = 40                                       # head count (not a multiple of 16)
     assert lib.fp4idx_mqa_logits_noalloc(*small) == E_INVALID
     small = list(args)
     small[3] = 0                                        # empty batch: nothing launched
