@@ -50,6 +50,20 @@
 
 namespace fp4idx {
 
+// A logits store.  Non-temporal (FP4IDX_LOGITS_NT, the default): each score
+// is written once and read only by the next kernel, so streaming it past the
+// caches keeps them for the K pages that work-groups share.
+#ifndef FP4IDX_LOGITS_NT
+#define FP4IDX_LOGITS_NT 1
+#endif
+__device__ __forceinline__ void store_logit(float* p, float v) {
+#if FP4IDX_LOGITS_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
 // RW rows per wave, NMT = heads/16, PPW pages per wave, D pages in flight.
 // Few rows per wave (decode) means little work per wave: keep several waves
 // per SIMD resident so memory latency overlaps (four for FP4; two for FP8,
@@ -80,7 +94,11 @@ struct WaveArgs {
 // page_end) of its block table (page_end - page_begin <= PPW), and the rows
 // rows(row0, nrows) names once the wave's page ids are on their way (0 <=
 // nrows <= RW, rows inside [0, n_rows); nrows 0 leaves).  Wave-uniform.
-template <typename FMT, int RW, int NMT, int PPW, int D, typename Rows>
+// EARLY_Q: rows() needs no memory read (the scheduled kernel), so the Q
+// operands join round trip 1; otherwise (rows() reads indptr) they follow
+// the first pages, which keeps their registers free while the row range is
+// on its way.
+template <typename FMT, int RW, int NMT, int PPW, int D, bool EARLY_Q, typename Rows>
 __device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_begin, int page_end, Rows rows) {
   static_assert(RW >= 1 && RW <= 4, "rows per wave");
   static_assert(PPW % D == 0 && PPW <= 64, "pages per wave: a multiple of the prefetch depth, one id per lane");
@@ -98,25 +116,46 @@ __device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_b
   const int64_t num_pages = a.num_pages;
 
   // Memory round trip 1: the wave's page ids (one vector load, lane i reads
-  // entry i, clamped into the table) and the row range.  No branch depends
-  // on them before the next loads are issued: an empty row group loads page
-  // 0 and in-range rows, and leaves afterwards.
+  // entry i, clamped into the table), then, once rows() has the row range,
+  // the context lengths (lane r reads row r) and the stationary Q operands
+  // and weights, all in flight together.  No branch depends on them before
+  // the pages are requested: an empty row group loads in-range rows and
+  // leaves afterwards.
   const int32_t* bt = a.block_table + (int64_t)req * bt_stride;
   const int32_t my_pid = bt[min(page_begin + (lane % PPW), bt_stride - 1)];
   __builtin_amdgcn_sched_barrier(0);  // keep the load issued ahead of the row range
   int row0 = 0, nrows = 0;
   rows(row0, nrows);
   const int row_hi = max(0, min(row0 + nrows, a.n_rows) - 1);  // a valid row index to clamp to
-
-  // Round trip 2, all in flight together: the context lengths (lane r reads
-  // row r; requested first so they are not queued behind the page traffic),
-  // the first D pages (fetched before the context lengths say whether they
-  // are needed) and the stationary Q operands.
-  // (lane-dependent address: a vector load, so it is issued ahead of the
-  // page loads and, loads retiring in order, waiting for it does not wait
-  // for the pages)
   const int32_t my_ctx = a.row_ctx[min(row0 + (lane & 3), row_hi)];
-  __builtin_amdgcn_sched_barrier(0);  // issued before the exit test below
+  typename FMT::QOp aq[RW][NMT];
+  uint32_t asc[RW][NSC];
+  float wv[RW][NMT][4];
+  auto load_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int row = min(row0 + (r < nrows ? r : 0), row_hi);
+#pragma unroll
+      for (int c = 0; c < NSC; ++c) asc[r][c] = 0;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const int64_t hrow = (int64_t)row * H + mt * 16 + li;
+        aq[r][mt] = FMT::load_q(a.q_fp4, hrow, lg);
+        asc[r][mt >> 2] |= FMT::q_scale_byte(a.q_scale, hrow, lg) << (8 * (mt & 3));
+        const float4 w4 = *reinterpret_cast<const float4*>(a.w + (int64_t)row * H + mt * 16 + lg * 4);
+        const bool live = r < nrows;
+        wv[r][mt][0] = live ? w4.x : 0.f;
+        wv[r][mt][1] = live ? w4.y : 0.f;
+        wv[r][mt][2] = live ? w4.z : 0.f;
+        wv[r][mt][3] = live ? w4.w : 0.f;
+      }
+    }
+  };
+  if constexpr (EARLY_Q) load_rows();
+  __builtin_amdgcn_sched_barrier(0);  // all of round trip 1 issued before waiting for the page ids
+
+  // Round trip 2: the first D pages (fetched before the context lengths say
+  // whether they are needed).
   int32_t pid[D];  // the first D page ids; later ones are read from my_pid when they are loaded
 #pragma unroll
   for (int i = 0; i < D; ++i)
@@ -124,8 +163,8 @@ __device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_b
   // A wave whose first page id is outside [0, num_pages) has nothing to
   // store: the table only promises valid ids for pages some row needs, and
   // the wave's pages start past them (an empty row group has no ids at all).
-  // It leaves before loading anything, so it neither holds a slot nor queues
-  // page traffic ahead of the waves that have work.
+  // It leaves before loading any page, so it neither holds a slot nor
+  // queues page traffic ahead of the waves that have work.
   if (!(pid[0] >= 0 && pid[0] < num_pages)) return;
   // Branch-free from here, so all loads issue back to back: another id
   // outside the pool (past the request's pages) re-reads the first page and
@@ -138,28 +177,7 @@ __device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_b
     const int64_t pg = (pid[i] >= 0 && pid[i] < num_pages) ? pid[i] : pid[0];
     FMT::template load_page<kPageNT>(buf[i], a.payload, a.scale, pg, lane_pay, lane_sc);
   }
-
-  typename FMT::QOp aq[RW][NMT];
-  uint32_t asc[RW][NSC];
-  float wv[RW][NMT][4];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int row = min(row0 + (r < nrows ? r : 0), row_hi);
-#pragma unroll
-    for (int c = 0; c < NSC; ++c) asc[r][c] = 0;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const int64_t hrow = (int64_t)row * H + mt * 16 + li;
-      aq[r][mt] = FMT::load_q(a.q_fp4, hrow, lg);
-      asc[r][mt >> 2] |= FMT::q_scale_byte(a.q_scale, hrow, lg) << (8 * (mt & 3));
-      const float4 w4 = *reinterpret_cast<const float4*>(a.w + (int64_t)row * H + mt * 16 + lg * 4);
-      const bool live = r < nrows;
-      wv[r][mt][0] = live ? w4.x : 0.f;
-      wv[r][mt][1] = live ? w4.y : 0.f;
-      wv[r][mt][2] = live ? w4.z : 0.f;
-      wv[r][mt][3] = live ? w4.w : 0.f;
-    }
-  }
+  if constexpr (!EARLY_Q) load_rows();
 
   // a context length beyond the row or the table (a broken contract) is cut
   // to what both hold, so no store leaves the row
@@ -196,7 +214,7 @@ __device__ __forceinline__ void wave_item(const WaveArgs& a, int req, int page_b
         constexpr int r = decltype(rc)::value;
         if (r < nrows) {
           const float tot = row_page_logits<FMT, NMT, RW == 1>(aq[r], asc[r], wv[r], buf[i]);
-          if (lane + p * 64 < lim[r]) rowp[r][lane + p * 64] = tot;
+          if (lane + p * 64 < lim[r]) store_logit(rowp[r] + lane + p * 64, tot);
         }
       });
       const int pn = p + D;  // < PPW <= 64: lane pn of my_pid holds its id
@@ -229,7 +247,7 @@ mqa_logits_kernel(WaveArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int page_begin = (chunk * 4 + wave) * PPW;
   if (page_begin >= a.bt_stride) return;
-  wave_item<FMT, RW, NMT, PPW, D>(a, req, page_begin, page_begin + PPW, [&](int& row0, int& nrows) {
+  wave_item<FMT, RW, NMT, PPW, D, false>(a, req, page_begin, page_begin + PPW, [&](int& row0, int& nrows) {
     // the request's rows, kept inside [0, n_rows) whatever indptr holds
     const int ip0 = min(max(a.indptr[req], 0), a.n_rows), ip1 = min(max(a.indptr[req + 1], ip0), a.n_rows);
     row0 = ip0 + grp * RW;
@@ -244,10 +262,11 @@ template <typename FMT, int RW, int NMT, int PPW, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kMinWavesPerSimd<FMT, RW, NMT>))) void
 mqa_logits_wave_planned_kernel(WaveArgs a, const int32_t* __restrict__ hdr, const int4* __restrict__ items,
                                int32_t n_reqs, int32_t cap_items) {
-  const int n_items = (hdr[kHdrRows] == RW && hdr[kHdrWaves] == 0) ? min(max(hdr[kHdrItems], 0), cap_items) : 0;
   const int item = blockIdx.x;
+  // the item is read with the header (the grid never exceeds the capacity)
+  const int4 iv = items[min(item, cap_items - 1)];  // the same for the whole work-group: scalar registers
+  const int n_items = (hdr[kHdrRows] == RW && hdr[kHdrWaves] == 0) ? min(max(hdr[kHdrItems], 0), cap_items) : 0;
   if (item >= n_items) return;
-  const int4 iv = items[item];  // the same for the whole work-group: scalar registers
   const int4 it = make_int4(__builtin_amdgcn_readfirstlane(iv.x), __builtin_amdgcn_readfirstlane(iv.y),
                             __builtin_amdgcn_readfirstlane(iv.z), __builtin_amdgcn_readfirstlane(iv.w));
   const int req = it.x, pb = it.z, nr = it.w & 0xFF, npg = it.w >> 8;
@@ -256,10 +275,9 @@ mqa_logits_wave_planned_kernel(WaveArgs a, const int32_t* __restrict__ hdr, cons
   const int page_begin = pb + wave * PPW;
   const int page_end = min(page_begin + PPW, pb + npg);
   if (page_begin >= page_end || page_begin >= a.bt_stride) return;
-  wave_item<FMT, RW, NMT, PPW, D>(a, req, page_begin, page_end, [&](int& row0, int& nrows) {
-    const int ip0 = min(max(a.indptr[req], 0), a.n_rows), ip1 = min(max(a.indptr[req + 1], ip0), a.n_rows);
+  wave_item<FMT, RW, NMT, PPW, D, true>(a, req, page_begin, page_end, [&](int& row0, int& nrows) {
     row0 = it.y;
-    nrows = (it.y >= ip0 && it.y + nr <= ip1) ? nr : 0;
+    nrows = (it.y >= 0 && it.y + nr <= a.n_rows) ? nr : 0;  // rows inside the call's rows
   });
 }
 
@@ -354,10 +372,11 @@ struct SharedArgs {
 // the rows' contexts reach.  Work-group uniform; starts and ends with the
 // work-group in step (the caller's barriers order it against the previous
 // item's LDS use).
-// tid is the thread's index in the work-group.
+// tid is the thread's index in the work-group; rot picks which waves take a
+// block's extra rows.
 template <int NW, int RW, int NMT>
 __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedArgs& a, int req, int row0,
-                                            int nrows, int pb, int n_max, int tid) {
+                                            int nrows, int pb, int n_max, int tid, int rot) {
   constexpr int NT = NW * 64;
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;
@@ -367,35 +386,35 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
   const int lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
 
-  // a context length beyond the row or the table (a broken contract) is cut
-  // to what both hold, so no store leaves the row
+  // Round trip 1, all in flight together: the block's context lengths, the
+  // chunk's page ids (none past the table row) and the wave's Q operands and
+  // weights (its rows: the block's rows spread evenly over the waves, so a
+  // block short of ROWS rows leaves no wave with more than ceil(nrows / NW)).
+  // A context length beyond the row or the table (a broken contract) is cut
+  // to what both hold, so no store leaves the row; a page id outside the pool
+  // (a broken table) reads page 0, so every load stays in the pool.
   const int ctx_cap = (int)min(min((int64_t)a.bt_stride * 64, a.logits_stride), (int64_t)0x7FFFFFFF);
-  if (tid < ROWS) L.ctx[tid] = tid < nrows ? min(max(a.row_ctx[row0 + tid], 0), ctx_cap) : 0;
-  __syncthreads();
-  int gmax = 0;
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) gmax = max(gmax, L.ctx[r]);
-  const int n = min(n_max, ((gmax + 63) >> 6) - pb);
-  if (n <= 0) return;  // the whole work-group: no row needs these pages
-  // page ids of the chunk; an id outside the pool (a broken table) reads
-  // page 0, so every load stays in the pool
+  const int32_t my_ctx = tid < nrows ? a.row_ctx[row0 + tid] : 0;
   const int32_t* bt = a.block_table + (int64_t)req * a.bt_stride + pb;
-  for (int k = tid; k < n; k += NT) {
-    const int32_t p = bt[k];
-    L.pid[k] = (p >= 0 && p < a.num_pages) ? p : 0;
-  }
-
-  // the wave's rows, the block's rows spread evenly over the waves (a block
-  // short of ROWS rows leaves no wave with more than ceil(nrows / NW)): Q
-  // operands, scales and weights stay in registers
-  const int per = (nrows + NW - 1) / NW;  // <= RW
-  const int nr = max(0, min(per, nrows - wave * per));  // wave-uniform
-  const int wrow0 = row0 + wave * per;
+  const int n_ids = max(0, min(n_max, a.bt_stride - pb));
+  constexpr int NID = (kSharedMaxChunk + NT - 1) / NT;
+  int32_t ids[NID];
+#pragma unroll
+  for (int m = 0; m < NID; ++m) ids[m] = tid + NT * m < n_ids ? bt[tid + NT * m] : 0;
+  // The block's rows over the waves: every wave floor(nrows / NW) rows and
+  // the remainder one more each (at most RW), consecutive rows per wave.
+  // Which waves take the extra rows rotates with `rot`, so that across the
+  // work-groups of a launch no SIMD (a work-group's wave w runs on the same
+  // SIMD in every work-group) gets the busier waves more often than the
+  // others.  Results do not depend on which wave scores a row.
+  const int slot = (wave + rot) % NW;  // wave-uniform
+  const int base = nrows / NW, extra = nrows - base * NW;
+  const int nr = base + (slot < extra ? 1 : 0);  // wave-uniform, <= RW
+  const int first = slot * base + min(slot, extra);  // the wave's first row within the block
+  const int wrow0 = row0 + first;
   uint4 aq[RW][NMT];
   uint32_t asc[RW][NSC];
   float wv[RW][NMT][4];
-  float* rowp[RW];
-  int lim[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = r < nr ? wrow0 + r : row0;
@@ -412,10 +431,27 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
       wv[r][mt][2] = w4.z;
       wv[r][mt][3] = w4.w;
     }
-    rowp[r] = a.logits + (int64_t)row * a.logits_stride + (int64_t)pb * 64;
-    lim[r] = r < nr ? L.ctx[wave * per + r] - pb * 64 : 0;
   }
-  __syncthreads();  // page ids staged
+  if (tid < ROWS) L.ctx[tid] = min(max(my_ctx, 0), ctx_cap);
+#pragma unroll
+  for (int m = 0; m < NID; ++m) {
+    const int k = tid + NT * m;
+    if (k < n_ids) L.pid[k] = (ids[m] >= 0 && ids[m] < a.num_pages) ? ids[m] : 0;
+  }
+  __syncthreads();  // context lengths and page ids staged
+  int gmax = 0;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) gmax = max(gmax, L.ctx[r]);
+  const int n = min(n_ids, ((gmax + 63) >> 6) - pb);
+  if (n <= 0) return;  // the whole work-group: no row needs these pages
+  float* rowp[RW];
+  int lim[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r < nr ? wrow0 + r : row0;
+    rowp[r] = a.logits + (int64_t)row * a.logits_stride + (int64_t)pb * 64;
+    lim[r] = r < nr ? L.ctx[first + r] - pb * 64 : 0;
+  }
 
   // page bytes in flight: two register sets, used in turn
   SharedPageRegs<NPAY> set0, set1;
@@ -435,7 +471,7 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
       constexpr int r = decltype(rc)::value;
       if (r < nr) {
         const float tot = row_page_logits<Fp4Lds, NMT, false>(aq[r], asc[r], wv[r], pg);
-        if (lane + i * 64 < lim[r]) rowp[r][lane + i * 64] = tot;
+        if (lane + i * 64 < lim[r]) store_logit(rowp[r] + lane + i * 64, tot);
       }
     });
   };
@@ -473,7 +509,8 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(SharedArgs a
   const int row0 = ip0 + (int)blockIdx.y * ROWS;
   const int nrows = max(0, min(ROWS, ip1 - row0));
   if (nrows == 0) return;  // the whole work-group
-  shared_item<NW, RW, NMT>(L, a, req, row0, nrows, chunk * chunk_pages, chunk_pages, threadIdx.x);
+  shared_item<NW, RW, NMT>(L, a, req, row0, nrows, chunk * chunk_pages, chunk_pages, threadIdx.x,
+                           (int)(blockIdx.x + blockIdx.y));
 }
 
 // Scheduled: work-group i takes item i of the plan (request, up to NW*RW
@@ -482,27 +519,26 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(SharedArgs a
 // never takes the kernel outside the buffers).
 template <int NW, int RW, int NMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 && NMT <= 4 ? 4 : 1))) void
-mqa_logits_planned_kernel(SharedArgs a, const int32_t* __restrict__ indptr,
-                                                                     int32_t n_reqs, int32_t n_rows,
+mqa_logits_planned_kernel(SharedArgs a, int32_t n_reqs, int32_t n_rows,
                                                                      const int32_t* __restrict__ hdr,
                                                                      const int4* __restrict__ items,
                                                                      int32_t cap_items) {
   constexpr int ROWS = NW * RW;
   __shared__ SharedLds<ROWS> L;
+  const int item = blockIdx.x;
+  // the item is read with the header (the grid never exceeds the capacity)
+  const int4 iv = items[min(item, cap_items - 1)];  // the same for the whole work-group: scalar registers
   const int n_items =
       (hdr[kHdrRows] == ROWS && hdr[kHdrWaves] == NW) ? min(max(hdr[kHdrItems], 0), cap_items) : 0;
-  const int item = blockIdx.x;
   if (item >= n_items) return;
-  const int4 iv = items[item];  // the same for the whole work-group: scalar registers
   const int4 it = make_int4(__builtin_amdgcn_readfirstlane(iv.x), __builtin_amdgcn_readfirstlane(iv.y),
                             __builtin_amdgcn_readfirstlane(iv.z), __builtin_amdgcn_readfirstlane(iv.w));
   const int req = it.x, pb = it.z, nrows = it.w & 0xFF, n_max = it.w >> 8;
   if (req < 0 || req >= n_reqs || nrows <= 0 || nrows > ROWS || pb < 0 || n_max <= 0 || n_max > kSharedMaxChunk ||
       (int64_t)pb + n_max > a.bt_stride)
     return;
-  const int ip0 = min(max(indptr[req], 0), n_rows), ip1 = min(max(indptr[req + 1], ip0), n_rows);
-  if (it.y < ip0 || it.y + nrows > ip1) return;
-  shared_item<NW, RW, NMT>(L, a, req, it.y, nrows, pb, n_max, threadIdx.x);
+  if (it.y < 0 || it.y + nrows > n_rows) return;  // rows inside the call's rows
+  shared_item<NW, RW, NMT>(L, a, req, it.y, nrows, pb, n_max, threadIdx.x, item);
 }
 
 // The arguments of one logits call, as the launchers pass them down.
@@ -699,7 +735,7 @@ static hipError_t launch_planned(const LogitsCall& c, const int32_t* ws, int64_t
   const SharedArgs a{c.block_table, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
                      c.q, c.q_scale, c.w, c.logits, c.logits_stride};
   return launch(mqa_logits_planned_kernel<NW, RW, NMT>, dim3((unsigned)grid), dim3(NW * 64), 0, c.stream, a,
-                c.indptr, c.n_reqs, c.n_rows, ws, reinterpret_cast<const int4*>(ws + sz.items_off),
+                c.n_reqs, c.n_rows, ws, reinterpret_cast<const int4*>(ws + sz.items_off),
                 (int32_t)cap_items);
 }
 
