@@ -50,14 +50,18 @@
 
 namespace fp4idx {
 
-// A logits store.  Non-temporal (FP4IDX_LOGITS_NT, the default): each score
-// is written once and read only by the next kernel, so streaming it past the
-// caches keeps them for the K pages that work-groups share.
-#ifndef FP4IDX_LOGITS_NT
-#define FP4IDX_LOGITS_NT 1
+// A logits store.  Each score is written once and read only by the next
+// kernel.  FP4IDX_LOGITS_STORE 2 (the default): a relaxed device-scope
+// store, which writes through the XCD's L2, so the kernel ends without dirty
+// logits lines to write back (prefill: step 528 -> 518 us, and the top-k
+// reads them 5 % faster); 1: non-temporal; 0: plain.
+#ifndef FP4IDX_LOGITS_STORE
+#define FP4IDX_LOGITS_STORE 2
 #endif
 __device__ __forceinline__ void store_logit(float* p, float v) {
-#if FP4IDX_LOGITS_NT
+#if FP4IDX_LOGITS_STORE == 2
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#elif FP4IDX_LOGITS_STORE == 1
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;

@@ -38,6 +38,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanLdsReqs = 4096;  // request offsets searched in LDS up to this many requests
 constexpr int kPlanTiles = 4;       // tiles of blocks whose working set stays in registers
+constexpr int kPlanBlockRows = 8;   // most rows of a row block (the kernels' shapes)
 
 // A block's plan: its request, first row and rows, its pages, and its large
 // and short chunks (length, count, first item of each kind).
@@ -77,6 +78,7 @@ struct PlanParams {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   __shared__ uint32_t part[kPlanWaves];
   __shared__ int32_t first_lds[kPlanLdsReqs + 1];
+  __shared__ int32_t ip0_lds[kPlanLdsReqs], ip1_lds[kPlanLdsReqs];  // each request's clamped row range
   __shared__ float s_work;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* req_first = p.ws + p.req_off;
@@ -93,9 +95,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   int nb = 0;
   for (int base = 0; base < p.n_reqs; base += kPlanThreads) {
     const int b = base + tid;
-    int cnt = 0;
+    int cnt = 0, ip0 = 0, ip1 = 0;
     if (b < p.n_reqs) {
-      int ip0, ip1;
       rows_of(b, ip0, ip1);
       cnt = (ip1 - ip0 + rows_pb - 1) / rows_pb;
     }
@@ -103,7 +104,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     const int first = nb + plan_scan(cnt, lane, wave, part, tile);
     if (b < p.n_reqs) {
       req_first[b] = first;
-      if (b < kPlanLdsReqs) first_lds[b] = first;
+      if (b < kPlanLdsReqs) {
+        first_lds[b] = first;
+        ip0_lds[b] = ip0;
+        ip1_lds[b] = ip1;
+      }
     }
     nb += tile;
   }
@@ -158,7 +163,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     if (g >= nb) return;
     const int b = request_of(g);
     int ip0, ip1;
-    rows_of(b, ip0, ip1);
+    if (in_lds) {
+      ip0 = ip0_lds[b];
+      ip1 = ip1_lds[b];
+    } else {
+      rows_of(b, ip0, ip1);
+    }
     const int R = ip1 - ip0;
     const int nblk = (R + rows_pb - 1) / rows_pb;
     const int i = g - (in_lds ? first_lds[b] : req_first[b]);
@@ -167,7 +177,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
       r0 = ip0 + (int)((int64_t)i * R / nblk);
       const int r1 = ip0 + (int)((int64_t)(i + 1) * R / nblk);
       nr = r1 - r0;
-      for (int r = r0; r < r1; ++r) cmax = max(cmax, min(max(p.row_ctx[r], 0), p.ctx_cap));
+      // the block's context lengths, all in flight together (a block has at
+      // most kPlanBlockRows rows; the loop after it only guards the bound)
+      int c[kPlanBlockRows];
+#pragma unroll
+      for (int k = 0; k < kPlanBlockRows; ++k) c[k] = k < nr ? p.row_ctx[r0 + k] : 0;
+#pragma unroll
+      for (int k = 0; k < kPlanBlockRows; ++k) cmax = max(cmax, min(max(c[k], 0), p.ctx_cap));
+      for (int r = r0 + kPlanBlockRows; r < r1; ++r) cmax = max(cmax, min(max(p.row_ctx[r], 0), p.ctx_cap));
     }
     e.b = b;
     e.r0 = r0;
