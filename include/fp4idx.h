@@ -207,7 +207,10 @@ size_t fp4idx_mqa_logits_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t
  * busier a block's waves, the shorter its chunks), large ones first and
  * the last share of every block in chunks a quarter as long, so that the
  * item list, taken in order, ends with short items.  The items are
- * (request, row block, page chunk).  Context lengths are read here (cut to
+ * (request, row block, page chunk).  The list is cut into eight contiguous
+ * ranges, one per XCD, stored interleaved (the run's work-group i executes
+ * on XCD i mod 8), so a block's chunks share one XCD's L2; at most 16 empty
+ * items even out the ranges.  Context lengths are read here (cut to
  * max_ctx) and by the run.
  *
  * The schedule depends only on n_rows, n_heads, req_row_indptr, n_reqs and

@@ -697,7 +697,7 @@ static int wave_item_pages(const PlanShape& sh) {
 // context bound (the run's grid; work-groups past the plan's items leave).
 static int64_t plan_item_bound(const PlanShape& sh, int64_t n_rows, int32_t n_reqs, int64_t max_ctx) {
   const PlanSizes sz = plan_sizes(n_rows, n_reqs, sh.rows);
-  return sz.blocks * plan_items_per_block(sh, (max_ctx + 63) / 64, wave_item_pages(sh), kItemTarget);
+  return sz.blocks * plan_items_per_block(sh, (max_ctx + 63) / 64, wave_item_pages(sh), kItemTarget) + kXcdSlack;
 }
 
 int64_t plan_workspace_bytes(int64_t n_rows, int32_t n_reqs, int64_t max_ctx) {

@@ -2,8 +2,8 @@
 //
 // One work-group of 1,024 threads (its registers and LDS do not depend on
 // the batch: the per-request list lives in the workspace, and so does the
-// per-block list beyond the first 4,096 blocks, whose working set stays in
-// registers):
+// per-block list beyond the first 1,024 blocks; the first 1,024 blocks'
+// working set stays in registers):
 //  1. blocks per request: a request of R rows (its indptr range, clamped
 //     into [0, n_rows]) becomes ceil(R / rows) row blocks, its rows spread
 //     evenly over them; a block scan gives each request its first block.
@@ -37,7 +37,7 @@ namespace fp4idx {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanLdsReqs = 4096;  // request offsets searched in LDS up to this many requests
-constexpr int kPlanTiles = 4;       // tiles of blocks whose working set stays in registers
+constexpr int kPlanTiles = 1;       // tiles of blocks whose working set stays in registers
 constexpr int kPlanBlockRows = 8;   // most rows of a row block (the kernels' shapes)
 
 // A block's plan: its request, first row and rows, its pages, and its large
@@ -246,21 +246,70 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     n_small += ts;
   });
 
-  // 4. the items
+  // 4. the items.  Work-group i of the run goes to XCD i mod 8 (the
+  // hardware's round-robin dispatch), and each XCD has its own L2: so the
+  // large list is cut into eight contiguous ranges, one per XCD, and so is
+  // the short list, and XCD x's large items, then its short ones, go to
+  // indices x, x + 8, x + 16, ...  A row block's chunks are consecutive in
+  // the lists, so they share an XCD (and its cached Q rows and pages) except
+  // at a range boundary, and every XCD still gets large items first and
+  // short ones last.  Indices no XCD fills (the ranges differ by one item at
+  // most) get empty items.  A workspace without room for those (at most 16)
+  // keeps the lists in plain order, and so do per-wave items (each reads its
+  // own pages once; the shared Q row is a few KiB).
+  const bool spread = p.waves > 0 && (int64_t)n_big + n_small + kXcdSlack <= p.cap_items &&
+                      n_big + n_small < (1 << 27);  // so n * 8 + 7 fits in 32 bits
+  auto first_of = [](int n, int x) { return (n * x + 7) >> 3; };  // XCD x's first of n
+  // writes a block's `cnt` chunks, the list's items gi0 .. gi0 + cnt - 1 (of
+  // n, after `before` items of the XCD's earlier list): the XCD of the first
+  // from the list position, then stepping to the next XCD at each range end
+  auto put = [&](int gi0, int cnt, int n, bool small, auto&& item_of) __attribute__((always_inline)) {
+    if (cnt <= 0) return;
+    if (!spread) {
+      for (int c = 0; c < cnt; ++c) items[(small ? n_big : 0) + gi0 + c] = item_of(c);
+      return;
+    }
+    int x = 0;
+    while (x < 7 && first_of(n, x + 1) <= gi0) ++x;
+    int next = first_of(n, x + 1);
+    int base = first_of(n, x) - (small ? first_of(n_big, x + 1) - first_of(n_big, x) : 0);
+    for (int c = 0; c < cnt; ++c) {
+      const int gi = gi0 + c;
+      while (gi >= next) {  // the next XCD's range
+        ++x;
+        next = first_of(n, x + 1);
+        base = first_of(n, x) - (small ? first_of(n_big, x + 1) - first_of(n_big, x) : 0);
+      }
+      items[x + 8 * (gi - base)] = item_of(c);
+    }
+  };
   visit([&](int g, BlockPlan& e) __attribute__((always_inline)) {
     if (g >= nb) return;
-    for (int c = 0; c < e.nbig; ++c) {
+    put(e.fb, e.nbig, n_big, false, [&](int c) {
       const int p0 = c * e.Lb;
-      items[e.fb + c] = make_int4(e.b, e.r0, p0, e.nr | (min(e.Lb, e.P - p0) << 8));
-    }
+      return make_int4(e.b, e.r0, p0, e.nr | (min(e.Lb, e.P - p0) << 8));
+    });
     const int s0 = e.nbig * e.Lb;
-    for (int c = 0; c < e.nsmall; ++c) {
+    put(e.fs, e.nsmall, n_small, true, [&](int c) {
       const int p0 = s0 + c * e.Ls;
-      items[n_big + e.fs + c] = make_int4(e.b, e.r0, p0, e.nr | (min(e.Ls, e.P - p0) << 8));
-    }
+      return make_int4(e.b, e.r0, p0, e.nr | (min(e.Ls, e.P - p0) << 8));
+    });
   });
+  int n_items = n_big + n_small;
+  if (spread) {
+    int longest = 0;
+    for (int x = 0; x < 8; ++x)
+      longest = max(longest, first_of(n_big, x + 1) - first_of(n_big, x) + first_of(n_small, x + 1) -
+                                 first_of(n_small, x));
+    n_items = 8 * longest;
+    if (tid < 8) {  // the empty items of XCD tid
+      const int len = first_of(n_big, tid + 1) - first_of(n_big, tid) + first_of(n_small, tid + 1) -
+                      first_of(n_small, tid);
+      for (int pos = len; pos < longest; ++pos) items[tid + 8 * pos] = make_int4(0, 0, 0, 0);
+    }
+  }
   if (tid == 0) {
-    p.ws[kHdrItems] = min(n_big + n_small, p.cap_items);
+    p.ws[kHdrItems] = min(n_items, p.cap_items);
     p.ws[1] = 0;
     p.ws[2] = 0;
     p.ws[kHdrCap] = p.cap_items;

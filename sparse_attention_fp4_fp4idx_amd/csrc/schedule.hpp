@@ -21,7 +21,9 @@
 //              short chunk lengths and counts, the first large and the first
 //              short item)                       [most blocks x 10, padded]
 //   items: int4 {request, first row, first page, rows | pages << 8}, as many
-//          as the rest of the workspace holds
+//          as the rest of the workspace holds; in per-XCD order (item x + 8k
+//          is the k-th of XCD x's list), empty items (all zero) evening out
+//          the lists
 // Item: rows [row0, row0 + rows) of one request (rows <= the kernel's rows
 // per work-group) and pages [page0, page0 + pages) of its block table
 // (pages <= kMaxItemPages).
@@ -35,6 +37,10 @@ namespace fp4idx {
 constexpr int kHdrWords = 16;       // 64-byte header
 constexpr int kMaxItemPages = 512;  // page ids one work-group stages in LDS
 constexpr int kMinItemPages = 4;    // the shortest chunk the plan makes
+
+// Items a plan may add to a batch's chunks: the empty items that even out
+// the eight per-XCD lists (two per XCD at most).
+constexpr int kXcdSlack = 16;
 
 enum HdrWord { kHdrItems = 0, kHdrCap = 3, kHdrRows = 4, kHdrWaves = 5, kHdrFixed = 6 };
 constexpr int kBlkWords = 10;
@@ -122,7 +128,7 @@ inline int64_t plan_items_per_block(const PlanShape& sh, int64_t pages, int fixe
 inline int64_t plan_bytes(const PlanShape& sh, int64_t n_rows, int64_t n_reqs, int64_t max_ctx, int fixed,
                           int target) {
   const PlanSizes s = plan_sizes(n_rows, n_reqs, sh.rows);
-  return 4 * (s.items_off + 4 * s.blocks * plan_items_per_block(sh, (max_ctx + 63) / 64, fixed, target));
+  return 4 * (s.items_off + 4 * (s.blocks * plan_items_per_block(sh, (max_ctx + 63) / 64, fixed, target) + kXcdSlack));
 }
 
 }  // namespace fp4idx

@@ -4,7 +4,8 @@ _run) through the C ABI.
 The schedule is integer work: its items are read back from the workspace
 and checked exactly (every (row, page) a row's context reaches is scored by
 exactly one item, items stay inside their requests and the kernel's limits,
-the count inside the workspace).  The logits it drives are compared bit for
+the count inside the workspace, at most 16 empty items evening out the
+per-XCD lists).  The logits it drives are compared bit for
 bit with the host-bounded call and against the oracle's bar (tests/bars.py).
 Inputs come from the seeded generators; expected values from the oracle.
 """
@@ -67,7 +68,11 @@ def _check_schedule(ws, indptr, ctx, max_ctx, n_rows):
     items = w[items_off:items_off + 4 * n_items].reshape(n_items, 4)
     cover = {}
     req_of = np.searchsorted(indptr, np.arange(n_rows), side="right") - 1
+    empty = 0
     for req, row0, page0, packed in items.tolist():
+        if (req, row0, page0, packed) == (0, 0, 0, 0):   # evens out the per-XCD lists
+            empty += 1
+            continue
         nr, npg = packed & 0xFF, packed >> 8
         assert 0 <= req < n_reqs
         assert 1 <= nr <= rows_pb and 1 <= npg <= max_pages
@@ -81,6 +86,7 @@ def _check_schedule(ws, indptr, ctx, max_ctx, n_rows):
             assert cover.get((t, p), 0) == 1, (t, p, cover.get((t, p), 0), int(req_of[t]))
     # pages past a row's own context may be covered (its block's longest row reaches them), once at most
     assert all(v == 1 for v in cover.values())
+    assert empty <= 16, empty
     return n_items, rows_pb, waves
 
 
