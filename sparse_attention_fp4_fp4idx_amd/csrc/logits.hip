@@ -46,27 +46,13 @@
 
 #include "launch.hpp"
 #include "logits_core.hpp"
+#include "store.hpp"
 #include "schedule.hpp"
 
 namespace fp4idx {
 
-// A logits store.  Each score is written once and read only by the next
-// kernel.  FP4IDX_LOGITS_STORE 2 (the default): a relaxed device-scope
-// store, which writes through the XCD's L2, so the kernel ends without dirty
-// logits lines to write back (prefill: step 528 -> 518 us, and the top-k
-// reads them 5 % faster); 1: non-temporal; 0: plain.
-#ifndef FP4IDX_LOGITS_STORE
-#define FP4IDX_LOGITS_STORE 2
-#endif
-__device__ __forceinline__ void store_logit(float* p, float v) {
-#if FP4IDX_LOGITS_STORE == 2
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#elif FP4IDX_LOGITS_STORE == 1
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
+// A logits store: written once, read only by the next kernel (store.hpp).
+__device__ __forceinline__ void store_logit(float* p, float v) { store_through(p, v); }
 
 // RW rows per wave, NMT = heads/16, PPW pages per wave, D pages in flight.
 // Few rows per wave (decode) means little work per wave: keep several waves
