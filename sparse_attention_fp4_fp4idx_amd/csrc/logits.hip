@@ -663,6 +663,9 @@ hipError_t launch_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scal
 // wave = 1 or 2, each wave its own pages), else the shared-page kernel.
 PlanShape plan_shape(int64_t n_rows, int32_t n_reqs, int n_heads) {
   const int64_t avg10 = n_reqs > 0 ? 10 * n_rows / n_reqs : 0;  // rows per request x 10
+#ifdef FP4IDX_PLAN_SHAPE  // measurement builds: waves * 10 + rows per work-group (per wave when waves is 0)
+  if (avg10 >= 15) return PlanShape{FP4IDX_PLAN_SHAPE / 10, FP4IDX_PLAN_SHAPE % 10};
+#endif
   if (avg10 < 15) return PlanShape{0, 1};
   if (avg10 < 30) return PlanShape{0, 2};
   if (n_heads > 64) return avg10 >= 60 ? PlanShape{4, 8} : PlanShape{2, 4};
