@@ -183,7 +183,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // The logits of one query row for one page, token `lane` of the page in
 // lane `lane`: per 16-token tile NMT MFMAs, then the ReLU / weight epilogue
-// in two fixed-order chains (even / odd M-tiles), then the lane reduction.
+// in one fixed-order FMA chain, then the lane reduction.
 // Every (row, token) is formed by exactly this sequence whichever kernel
 // calls it, so the logits do not depend on the launch shape.  ONE_TILE keeps
 // a single tile's MFMA results live at a time (register budget for four
@@ -207,18 +207,14 @@ __device__ __forceinline__ float row_page_logits(const typename FMT::QOp (&aq)[N
         default: d[mt] = FMT::template mfma<3>(aq[mt], pg, t, asc[mt >> 2]); break;
       }
     }
-    // two fixed-order chains (even / odd M-tiles), then their sum
-    float acc0 = 0.f, acc1 = 0.f;
+    // one fixed-order chain over the M-tiles (the four tiles' chains are
+    // independent of each other)
+    float r = 0.f;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float rl = relu(d[mt][e]);
-        if (mt & 1) acc1 = __builtin_fmaf(wv[mt][e], rl, acc1);
-        else acc0 = __builtin_fmaf(wv[mt][e], rl, acc0);
-      }
+      for (int e = 0; e < 4; ++e) r = __builtin_fmaf(wv[mt][e], relu(d[mt][e]), r);
     }
-    const float r = acc0 + acc1;
     if constexpr (ONE_TILE) __builtin_amdgcn_sched_barrier(0);
     return r;
   };
