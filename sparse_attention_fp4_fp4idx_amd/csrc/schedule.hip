@@ -40,6 +40,7 @@ constexpr int kPlanLdsReqs = 4096;  // request offsets searched in LDS up to thi
 constexpr int kPlanTiles = 1;       // tiles of blocks whose working set stays in registers
 constexpr int kPlanBlockRows = 8;   // most rows of a row block (the kernels' shapes)
 constexpr int kPlanCoalescedBlocks = 128;  // batches of up to this many blocks write items coalesced
+constexpr int kPlanLdsRows = 4096;         // context lengths staged in LDS up to this many rows
 
 // A block's plan: its request, first row and rows, its pages, and its large
 // and short chunks (length, count, first item of each kind).
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   __shared__ int32_t first_lds[kPlanLdsReqs + 1];
   __shared__ int32_t ip0_lds[kPlanLdsReqs], ip1_lds[kPlanLdsReqs];  // each request's clamped row range
   __shared__ float s_work;
+  __shared__ int32_t ctx_lds[kPlanLdsRows];  // the rows' context lengths (batches of up to kPlanLdsRows rows)
   // per-block plans for the coalesced item writer (batches of up to
   // kPlanCoalescedBlocks row blocks): first large and short item, request,
   // first row, rows, pages, large and short chunk lengths
@@ -95,6 +97,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     ip1 = min(max(p.indptr[b + 1], ip0), p.n_rows);
   };
   if (tid == 0) s_work = 0.0f;
+  // Every row's context length (cut to the plan's bound), loaded in the
+  // same round trip as indptr when the batch has at most kPlanLdsRows rows
+  // (the blocks then read them from LDS); stored after pass 1's barriers.
+  const bool ctx_in_lds = p.n_rows <= kPlanLdsRows;
+  int32_t ctx_pre[kPlanLdsRows / kPlanThreads];
+  if (ctx_in_lds) {
+#pragma unroll
+    for (int k = 0; k < kPlanLdsRows / kPlanThreads; ++k) {
+      const int r = tid + k * kPlanThreads;
+      ctx_pre[k] = r < p.n_rows ? p.row_ctx[r] : 0;
+    }
+  }
 
   // 1. row blocks per request, and each request's first block
   int nb = 0;
@@ -116,6 +130,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
       }
     }
     nb += tile;
+  }
+  if (ctx_in_lds) {
+#pragma unroll
+    for (int k = 0; k < kPlanLdsRows / kPlanThreads; ++k) {
+      const int r = tid + k * kPlanThreads;
+      if (r < p.n_rows) ctx_lds[r] = min(max(ctx_pre[k], 0), p.ctx_cap);
+    }
   }
   // more blocks than rows make only overlapping request ranges (a broken
   // indptr): the blocks past the bound are not scheduled
@@ -184,12 +205,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
       nr = r1 - r0;
       // the block's context lengths, all in flight together (a block has at
       // most kPlanBlockRows rows; the loop after it only guards the bound)
-      int c[kPlanBlockRows];
+      if (ctx_in_lds) {
+        for (int r = r0; r < r1; ++r) cmax = max(cmax, ctx_lds[r]);
+      } else {
+        int c[kPlanBlockRows];
 #pragma unroll
-      for (int k = 0; k < kPlanBlockRows; ++k) c[k] = k < nr ? p.row_ctx[r0 + k] : 0;
+        for (int k = 0; k < kPlanBlockRows; ++k) c[k] = k < nr ? p.row_ctx[r0 + k] : 0;
 #pragma unroll
-      for (int k = 0; k < kPlanBlockRows; ++k) cmax = max(cmax, min(max(c[k], 0), p.ctx_cap));
-      for (int r = r0 + kPlanBlockRows; r < r1; ++r) cmax = max(cmax, min(max(p.row_ctx[r], 0), p.ctx_cap));
+        for (int k = 0; k < kPlanBlockRows; ++k) cmax = max(cmax, min(max(c[k], 0), p.ctx_cap));
+        for (int r = r0 + kPlanBlockRows; r < r1; ++r) cmax = max(cmax, min(max(p.row_ctx[r], 0), p.ctx_cap));
+      }
     }
     e.b = b;
     e.r0 = r0;
