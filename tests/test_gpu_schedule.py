@@ -65,38 +65,42 @@ def _check_schedule(ws, indptr, ctx, max_ctx, n_rows):
     max_pages = fixed if waves == 0 else MAX_ITEM_PAGES
     # the plan lays its lists out for the shape it picked
     _, items_off = layout(n_rows, n_reqs, rows_pb)
-    items = w[items_off:items_off + 4 * n_items].reshape(n_items, 4)
-    cover = {}
-    req_of = np.searchsorted(indptr, np.arange(n_rows), side="right") - 1
-    empty = 0
-    for req, row0, page0, packed in items.tolist():
-        if (req, row0, page0, packed) == (0, 0, 0, 0):   # evens out the per-XCD lists
-            empty += 1
-            continue
-        nr, npg = packed & 0xFF, packed >> 8
-        assert 0 <= req < n_reqs
-        assert 1 <= nr <= rows_pb and 1 <= npg <= max_pages
-        assert indptr[req] <= row0 and row0 + nr <= indptr[req + 1]
-        for t in range(row0, row0 + nr):
-            for p in range(page0, page0 + npg):
-                cover[(t, p)] = cover.get((t, p), 0) + 1
-    for t in range(n_rows):
-        need = (min(int(ctx[t]), max_ctx) + 63) // 64
-        for p in range(need):
-            assert cover.get((t, p), 0) == 1, (t, p, cover.get((t, p), 0), int(req_of[t]))
+    items = w[items_off:items_off + 4 * n_items].reshape(n_items, 4).astype(np.int64)
+    empty = np.all(items == 0, axis=1)            # evens out the per-XCD lists
+    assert int(empty.sum()) <= 16, int(empty.sum())
+    req, row0, page0, packed = items[~empty].T
+    nr, npg = packed & 0xFF, packed >> 8
+    assert np.all((req >= 0) & (req < n_reqs))
+    assert np.all((nr >= 1) & (nr <= rows_pb) & (npg >= 1) & (npg <= max_pages) & (page0 >= 0))
+    assert np.all((indptr[req] <= row0) & (row0 + nr <= indptr[req + 1]))
+    # coverage count per (row, page): +1 at an item's first page, -1 past its last, summed along pages
+    need = (np.minimum(ctx.astype(np.int64), max_ctx) + 63) // 64
+    width = int(max(int((page0 + npg).max(initial=0)), int(need.max(initial=0)))) + 1
+    rep = np.repeat(np.arange(req.size), nr)
+    rows = row0[rep] + (np.arange(rep.size) - np.repeat(np.cumsum(nr) - nr, nr))
+    diff = np.zeros((max(n_rows, 1), width + 1), np.int32)
+    np.add.at(diff, (rows, page0[rep]), 1)
+    np.add.at(diff, (rows, page0[rep] + npg[rep]), -1)
+    cover = np.cumsum(diff, axis=1)[:n_rows, :width]
+    needed = np.arange(width)[None, :] < need[:, None]
+    bad = np.argwhere(needed & (cover != 1))
+    assert bad.size == 0, (bad[:5].tolist(), cover[tuple(bad[0])] if bad.size else None)
     # pages past a row's own context may be covered (its block's longest row reaches them), once at most
-    assert all(v == 1 for v in cover.values())
-    assert empty <= 16, empty
+    assert cover.max(initial=0) <= 1
     return n_items, rows_pb, waves
 
 
 @pytest.mark.parametrize("case", ["small", "ragged", "empty_requests", "mixed48", "prefill", "decode256x6",
-                                  "decode64", "two_rows"])
+                                  "decode64", "two_rows", "many_requests", "many_blocks", "blocks_1100_two_rows"])
 def test_plan_covers_every_row_page_exactly_once(F, case):
     """The plan for batches of every kernel shape: near-uniform many rows
     (4 x 2), six rows (2 x 3), one to sixteen rows with contexts 8k-32k, a
     prefill of 4,096 rows, one and two rows per request (per-wave kernel),
-    requests without rows and rows without context."""
+    requests without rows and rows without context; and the plan's paths
+    for large batches: over 4,096 requests (the request search outside LDS)
+    and rows (context lengths read from memory), over 128 row blocks (one
+    thread per block writes its items) and over 1,024 (the per-block list
+    in the workspace)."""
     rng = np.random.default_rng(7)
     if case == "small":
         rows, ctxs = (1, 6, 16, 3), (130, 1000, 777, 0)
@@ -115,6 +119,15 @@ def test_plan_covers_every_row_page_exactly_once(F, case):
         R = rng.integers(1, 4, 40)
         indptr = np.concatenate([[0], np.cumsum(R)]).astype(np.int32)
         ctx = rng.integers(0, 9000, int(indptr[-1])).astype(np.int32)
+    elif case == "many_requests":   # 6,000 one-row requests (per-wave, one row per wave)
+        indptr = np.arange(6001, dtype=np.int32)
+        ctx = rng.integers(0, 3000, 6000).astype(np.int32)
+    elif case == "many_blocks":     # 2,000 requests of 8 rows: 16,000 rows, 2,000 blocks of 4 x 2
+        indptr = (8 * np.arange(2001)).astype(np.int32)
+        ctx = rng.integers(0, 2000, 16000).astype(np.int32)
+    elif case == "blocks_1100_two_rows":   # 1,100 requests of 2 rows (per-wave, two rows per wave)
+        indptr = (2 * np.arange(1101)).astype(np.int32)
+        ctx = rng.integers(1, 5000, 2200).astype(np.int32)
     else:
         wl = W.make({"mixed48": 4, "prefill": 3, "decode256x6": 2, "decode64": 1}[case], with_q=False)
         indptr, ctx = wl.req_row_indptr, wl.row_ctx
@@ -220,3 +233,39 @@ def test_planned_runs_interleaved_with_other_plans(F, orc):
                            logits=torch.full(ref.shape, float("nan"), device=DEV))
             torch.cuda.synchronize()
             assert np.array_equal(bits(got.cpu().numpy()), bits(ref)), rep
+
+
+@pytest.mark.parametrize("case", ["many_blocks", "many_requests"])
+def test_large_batch_logits_follow_the_plan(F, orc, case):
+    """Logits of batches on the plan's large-batch paths (2,000 requests of
+    8 rows: 2,000 shared-page blocks, the per-block list in the workspace;
+    6,000 one-row requests: the request search outside LDS), scheduled
+    against the host-bounded call bit for bit, and sampled scores against
+    the oracle's bar."""
+    rng = np.random.default_rng(91)
+    n_reqs, R = (2000, 8) if case == "many_blocks" else (6000, 1)
+    n_rows = n_reqs * R
+    indptr = (R * np.arange(n_reqs + 1)).astype(np.int32)
+    ctx = rng.integers(0, 1500, n_rows).astype(np.int32)
+    pages_per_req = 24                                         # 1,536 tokens of table per request
+    num_pages = n_reqs * pages_per_req
+    table = rng.permutation(num_pages).astype(np.int32).reshape(n_reqs, pages_per_req)
+    pay, sc = W.random_pool(rng, num_pages)
+    qf = rng.integers(0, 256, (n_rows, 64, 64)).astype(np.uint8)
+    qs = rng.integers(124, 129, (n_rows, 64, 4)).astype(np.uint8)
+    w = rng.uniform(0, 1, (n_rows, 64)).astype(np.float32)
+    width = pages_per_req * 64
+    a = (dev(qf), dev(qs), dev(w), dev(indptr), dev(ctx), dev(table), dev(pay), dev(sc))
+    say(case, "rows", n_rows, "requests", n_reqs)
+    got = F.mqa_logits(*a, logits=torch.full((n_rows, width), float("nan"), device=DEV))
+    ref = F.mqa_logits_bounded(*a, R, width, logits=torch.full((n_rows, width), float("nan"), device=DEV))
+    torch.cuda.synchronize()
+    g = got.cpu().numpy()
+    assert np.array_equal(bits(g), bits(ref.cpu().numpy()))
+    rows = rng.integers(0, n_rows, 3000)
+    rows = rows[ctx[rows] > 0]
+    toks = (rng.random(rows.size) * ctx[rows]).astype(np.int64)
+    f64, T, A = orc.logits_sampled(qf, qs, w, indptr, table, pay, sc, rows, toks)
+    check_fp4(g[rows, toks], f64, T, A, f"{case}: {n_rows} rows (sampled)")
+    cols = np.arange(width)[None, :]
+    assert np.all(np.isnan(g[cols >= ctx[:, None]]))
