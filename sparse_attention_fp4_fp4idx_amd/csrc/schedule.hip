@@ -19,10 +19,15 @@
 //     remainder of the large chunks).  Block scans of the two counts place
 //     every block's large items in one list and its short items in a second
 //     list that follows the first.
-//  4. the items, written in that order.
+//  4. the items: for the shared-page kernel each list cut into eight
+//     contiguous ranges, one per XCD, stored interleaved (item x + 8k is
+//     the k-th of XCD x's list; see below), for per-wave items in plain
+//     order; written coalesced (thread t builds items t, t + 1,024, ...)
+//     for up to 128 row blocks, else by one thread per block.
 // The logits kernel's work-groups take the items in list order, so the
 // hardware's dispatch keeps every CU busy while large items remain and the
-// list ends with short ones that fill the tail.  The item count never
+// list ends with short ones that fill the tail.  Context lengths of up to
+// 4,096 rows and the row ranges of up to 4,096 requests are staged in LDS.  The item count never
 // exceeds the workspace's capacity: a block gets at most capacity / blocks
 // items (its chunks grow instead, and a per-wave block's pages past them are
 // not scored), which contexts within the workspace's bound never need.
