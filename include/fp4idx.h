@@ -157,9 +157,10 @@ int fp4idx_write_k_pack_q(const uint16_t* k_bf16, int64_t n_tokens, int64_t k_ro
  *   block_table         [n_reqs, bt_stride] int32: token s of request b is in
  *                       page block_table[b*bt_stride + s/64], slot s%64.  Entries
  *                       for s/64 < ceil(max ctx of b's rows / 64) must be valid
- *                       page ids < num_pages (an invalid one is never read
- *                       from the pool; its tokens' logits are unspecified);
- *                       later entries are never read.
+ *                       page ids < num_pages (an invalid one never addresses
+ *                       the pool: a valid page is read in its place, and its
+ *                       tokens' logits are unspecified); later entries of
+ *                       the row may be read but are never used.
  *   logits              [n_rows, logits_stride] fp32 (out); only [0, ctx[t]) of
  *                       each row is written, the rest is left untouched.
  *   workspace           device memory of workspace_bytes bytes, 16-byte aligned,
