@@ -184,8 +184,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
-              "supported. The path shards by request or by context across GPUs; see DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported. Across GPUs "
+              "the path shards by request (no exchange) or, for long rows, by context (one all-gather of each "
+              "row's local top-k candidates before a final selection).", file=sys.stderr)
         sys.exit(2)
 
     import torch
