@@ -22,6 +22,15 @@ the same K steps, launched eagerly with the two encoders as separate
 kernels, where each kernel carries HIP events that its own dispatch stamps
 with its start and end times (fp4idx_time_next_call -> hipExtLaunchKernel).
 
+The first tens of milliseconds of a heavy step after idle run below the
+GPU's steady clock (its power management dips, then recovers over about a
+hundred prefill steps), and the W + K steps fall inside that transient.  So
+each workload's record also holds a `sustained` rate: the same K steps timed
+again after at least 60 ms of further untimed steps, and then K steps with
+the logits schedule built once and reused (one plan serves every
+compressed-attention layer of a step).  The JSON line's value is the K steps
+right after the W warm-up steps, the schedule built in every step.
+
 Roofline of a kernel: its algorithmic bytes at 8 TB/s and its FP4 MFMA flop
 at 10.1 PFLOP/s give a roofline time max(bytes / BW, flop / P); the fraction
 is that time over the measured time, and the bound is the larger term.  The
@@ -374,6 +383,7 @@ def main():
                     runners.append(g.replay)
                     sets[c]["graph"] = g
             else:
+                prepared = []
                 for c in range(copies):
                     s_ = sets[c]
                     pw, _ = (F.prepare_write_k_pack_q_fp8 if fp8 else F.prepare_write_k_pack_q)(
@@ -400,6 +410,7 @@ def main():
                         pl()
                         pt()
                     runners.append(run)
+                    prepared.append((pw, pt))
             for c in range(copies):
                 runners[c]()
             torch.cuda.synchronize()
@@ -411,6 +422,47 @@ def main():
                 runners[i % copies]()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - start
+
+            # Sustained rate: the GPU's power management slows the first tens of
+            # milliseconds of a heavy step after idle (a dip below, then a slow
+            # recovery to, its steady clock), so the same steps are timed again after
+            # at least 60 ms (at most 400 steps) of further untimed steps; then with
+            # the schedule built once per input copy and reused (one plan serves every
+            # layer of a step), timed in the same regime.
+            sustained = None
+            if args.launch == "prepared" and not fp8 and not fused:
+                n_more = int(min(400, max(args.steps, np.ceil(60.0 / max(elapsed * 1e3 / args.steps, 1e-3)))))
+                for i in range(n_more):
+                    runners[i % copies]()
+                torch.cuda.synchronize()
+                start = time.perf_counter()
+                for i in range(args.steps):
+                    runners[i % copies]()
+                torch.cuda.synchronize()
+                sustained = {"ms_per_step": (time.perf_counter() - start) * 1e3 / args.steps,
+                             "untimed_steps_before": args.warmup + copies + args.steps + n_more}
+                reused = []
+                for c in range(copies):
+                    s_ = sets[c]
+                    plan = F.LogitsPlan(H, indptr, ctx, wl.max_ctx, workspace=s_["ws"], stream=stream).build()
+                    pr, _ = plan.prepare_run(s_["q_code"], s_["q_scale"], s_["w_out"], bt, *pool_args(s_),
+                                             logits=s_["logits"], stream=stream)
+                    pw, pt = prepared[c]
+
+                    def run_reused(pw=pw, pr=pr, pt=pt):
+                        pw()
+                        pr()
+                        pt()
+                    reused.append(run_reused)
+                for c in range(copies):
+                    reused[c]()
+                torch.cuda.synchronize()
+                start = time.perf_counter()
+                for i in range(args.steps):
+                    reused[i % copies]()
+                torch.cuda.synchronize()
+                sustained["plan_reused_ms_per_step"] = (time.perf_counter() - start) * 1e3 / args.steps
+                del reused
 
             # kernel durations: the same K steps launched eagerly, each kernel carrying
             # HIP events its own dispatch stamps (no marker packets in between)
@@ -429,9 +481,9 @@ def main():
             per_kernel = {n: float(np.mean(v)) for n, v in times.items()}
             stats = {n: (float(np.median(v)), float(np.min(v))) for n, v in times.items()}
             del sets, runners
-            return elapsed * 1e3 / args.steps, per_kernel, copies, stats
+            return elapsed * 1e3 / args.steps, per_kernel, copies, stats, sustained
 
-        ms, pk, copies, stats = run_cache(False, dict(payload=payload, scale=scale))
+        ms, pk, copies, stats, sustained = run_cache(False, dict(payload=payload, scale=scale))
         alg = algorithmic(wl)
         kus = {n: v * 1e3 for n, v in pk.items()}
         bounded_us = kus.pop("mqa_logits_bounded")   # not part of the step
@@ -448,12 +500,26 @@ def main():
                            "roofline": roofline_of("write_k", alg, kus["write_k"], measured)},
                "unique_k_tokens": alg["unique_k_tokens"], "input_copies": copies,
                "logits_host_bounded_us": round(bounded_us, 2)}
+        if sustained is not None:
+            sm, rm = sustained["ms_per_step"], sustained["plan_reused_ms_per_step"]
+            rec["sustained"] = {
+                "ms_per_step": round(sm, 4), "scores_per_s": round(wl.scores / (sm * 1e-3), 1),
+                "plan_reused_ms_per_step": round(rm, 4), "plan_reused_scores_per_s": round(wl.scores / (rm * 1e-3), 1),
+                "untimed_steps_before": sustained["untimed_steps_before"],
+                "note": "the same K steps timed again after further untimed steps (at least 60 ms of them), past "
+                        "the power-management transient of the first steps after idle; then K steps with the "
+                        "schedule built once and reused (one plan serves every compressed-attention layer of a "
+                        "step). ms_per_step and value above are the K steps right after the W warm-up steps"}
         if dom != "mqa_logits":
             rec["logits_roofline"] = roofline_of("mqa_logits", alg, kus["mqa_logits"], measured,
                                                  measured_traffic(f"config{idx}:mqa_logits"))
         rec["topk_roofline"] = roofline_of("topk", alg, kus["topk"], measured)
         log(f"[bench] workload {idx}: {ms * 1e3:.1f} us/step, kernels " +
             ", ".join(f"{n} {v:.1f}" for n, v in kus.items()) + f" us ({time.time() - t0:.1f}s)")
+        if sustained is not None:
+            log(f"[bench] workload {idx}: sustained {sustained['ms_per_step'] * 1e3:.1f} us/step after "
+                f"{sustained['untimed_steps_before']} untimed steps, "
+                f"{sustained['plan_reused_ms_per_step'] * 1e3:.1f} us/step with the schedule reused")
 
         if headline:
             extras = {}
@@ -482,7 +548,7 @@ def main():
                                       t(wl.cached_slots[a:a + (1 << 20)]), norm_w, wl.eps, tab, pool8)
                     del kc
                 torch.cuda.synchronize()
-                ms8, pk8, copies8, _ = run_cache(True, dict(pool=pool8))
+                ms8, pk8, copies8, _, _ = run_cache(True, dict(pool=pool8))
                 del pool8
                 uk = alg["unique_k_tokens"]
                 l8 = 132 * uk + 4 * wl.scores + 8704 * T + 4 * ((uk + 63) // 64)
@@ -501,7 +567,7 @@ def main():
                 log(f"[bench] fp8 cache: {ms8 * 1e3:.1f} us/step, logits {pk8['mqa_logits'] * 1e3:.1f} us "
                     f"({time.time() - t0:.1f}s)")
             if not args.no_fused and wl.heads <= 64 and wl.max_ctx <= F.FUSED_MAX_CTX:
-                msf, pkf, copiesf, _ = run_cache(False, dict(payload=payload, scale=scale), fused=True)
+                msf, pkf, copiesf, _, _ = run_cache(False, dict(payload=payload, scale=scale), fused=True)
                 extras["fused_logits_topk"] = {
                     "ms_per_step": round(msf, 4), "scores_per_s": round(wl.scores / (msf * 1e-3), 1),
                     "kernels_us": {n: round(v * 1e3, 2) for n, v in pkf.items()},
@@ -599,7 +665,8 @@ def main():
         "roofline": dict(head["roofline"], measured_peaks=measured),
         "cpu_baseline": cpu,
         "extras": dict(head.get("extras", {}), configs=configs,
-                       headline_topk_roofline=head["topk_roofline"], headline_k_write=head["k_write"]),
+                       headline_topk_roofline=head["topk_roofline"], headline_k_write=head["k_write"],
+                       headline_sustained=head.get("sustained")),
     }
     print(json.dumps(out), flush=True)
 
