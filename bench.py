@@ -628,6 +628,20 @@ def main():
         secs /= reps
         # per sampled step: the K write pro rata to the sampled rows, the rest as measured
         cpu_s = secs[0] * (rows.size / T) + secs[1:].sum()
+        # the same sampled step once more on one host thread
+        n_thr = orc.get_threads()
+        orc.set_threads(1)
+        try:
+            c0 = time.perf_counter()
+            orc.write_k(wl.k_new, wl.pos_new, wl.slot_new, wl.norm_w, wl.eps, tabn, pay_np, sc_np)
+            c1 = time.perf_counter()
+            qf, qs, wo = orc.pack_q(wl.q[rows], wl.pos_q[rows], tabn, wl.w[rows], wl.w_scale)
+            lg = orc.logits(qf, qs, wo, ind, s_ctx, bts, pay_np, sc_np, logits_stride=wl.max_ctx)
+            orc.topk(np.nan_to_num(lg), s_ctx, k)
+            c2 = time.perf_counter()
+        finally:
+            orc.set_threads(n_thr)
+        one_s = (c1 - c0) * (rows.size / T) + (c2 - c1)
         cpu = {"value": round(s_scores / cpu_s, 1), "unit": "scores/s", "cores": orc.get_threads(), "kind": "oracle",
                "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
                "sample": f"{rows.size} of {T} rows spread evenly over the batch ({s_scores} scores, "
@@ -635,9 +649,11 @@ def main():
                          f"pack_q, logits and top-k of those rows on the oracle; value = sampled scores / "
                          f"mean time per run",
                "seconds_per_run": {n: round(float(v), 4)
-                                   for n, v in zip(("write_k", "pack_q", "mqa_logits", "topk"), secs)}}
-        log(f"[bench] cpu baseline: {cpu['value'] / 1e6:.2f} M scores/s on {cpu['cores']} threads "
-            f"({time.time() - t0:.1f}s)")
+                                   for n, v in zip(("write_k", "pack_q", "mqa_logits", "topk"), secs)},
+               "single_thread": {"value": round(s_scores / one_s, 1), "cores": 1,
+                                 "sample": "the same sampled step, run once on one host thread"}}
+        log(f"[bench] cpu baseline: {cpu['value'] / 1e6:.2f} M scores/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread']['value'] / 1e6:.2f} M on one ({time.time() - t0:.1f}s)")
         del pay_np, sc_np, lg
 
     out = {
