@@ -21,9 +21,9 @@
 //   2 KB contiguous, and a scale word), straight into the B operand.  D
 //   pages are in flight per wave; the page ids and Q are requested before
 //   the context lengths arrive so the prologue costs one memory latency less.
-//   FP4 batches whose requests all have about the same number (three or
-//   more) of rows use mqa_logits_shared_kernel instead: its waves split a
-//   block of rows and share each page through LDS (see that kernel).
+//   Batches with three or more rows per request on average (either cache)
+//   use mqa_logits_shared_kernel instead: its waves split a block of rows
+//   and share each page through LDS (see that kernel).
 //
 // MFMA mapping for FP4 (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands
 // e2m1; FP8 in Fp8Fused below):
@@ -278,65 +278,180 @@ constexpr int kPayBytes = 4096, kScBytes = 256;
 // Pages x rows one wave of a shared-page work-group scores at most.
 constexpr int kSharedPageRows = 64;
 
-// Requests with several rows (FP4 cache): a work-group of NW waves takes a
-// block of NW*RW rows of one request and a chunk of that request's pages;
-// each page is read from memory once per work-group and shared by its waves
-// through LDS, and each wave scores its RW rows.  Page i's bytes are loaded
-// into registers two pages ahead, written to LDS slot i&1 just before page
-// i is scored, and one barrier per page publishes the slot (the barrier
-// also proves every wave has finished page i-2, the slot's previous page).
-// Per lane and tile the B operand is a 16-byte LDS read in the pool's own
-// layout; the page's scale bytes are written transposed so one word read
-// gives a lane its four tiles' scales.  Each (row, token) goes through
-// row_page_logits exactly as in mqa_logits_kernel, so the logits are the
-// same bits whichever kernel computes them.
-// One FP4 page in flight in a shared-page work-group of NT threads: thread
-// t holds 16-byte payload pieces t, t + NT, ... (as one native vector, so the
-// pieces stay in registers) and, in the first wave, scale word t.
-template <int NPAY>
-struct SharedPageRegs {
-  typedef uint32_t Vec __attribute__((ext_vector_type(4 * NPAY)));
-  Vec p;
-  uint32_t s;
+// Requests with several rows: a work-group of NW waves takes a block of
+// NW*RW rows of one request and a chunk of that request's pages; each page
+// is read from memory once per work-group, in whole contiguous 16-byte
+// pieces, and shared by its waves through LDS, and each wave scores its RW
+// rows.  Page i's bytes are loaded into registers two pages ahead, written
+// to LDS slot i&1 just before page i is scored, and one barrier per page
+// publishes the slot (the barrier also proves every wave has finished page
+// i-2, the slot's previous page).  The slot layout is the cache format's
+// (Fp4Staged, Fp8Staged): a lane's B operand per tile is one (FP4) or two
+// (FP8) 16-byte LDS reads and its four tiles' scales one word.  Each (row,
+// token) goes through row_page_logits with the same operands as in
+// mqa_logits_kernel, so the logits are the same bits whichever kernel
+// computes them.
+// How a cache's pages travel through a shared-page work-group of NT threads:
+// Regs<NT> holds one page in flight (fetch: coalesced 16-byte loads, thread
+// t taking pieces t, t + NT, ...), stage() writes it to an LDS slot of
+// kSlotBytes, and read<SLOT>() gives a lane its B operands and scale word
+// for the page's four tiles from slot SLOT (a compile-time offset on top of
+// the lane's address registers).  Q and QSc load a row's A operands and
+// scale bytes as the per-wave kernel does; Op is the operand format that
+// row_page_logits scores with.
+//
+// FP4 (split pools): the slot holds the payload in pool order, so lane
+// (token li, block lg) finds its 16 bytes at lg*1024 + li*16 + t*256, and
+// the page's scale bytes transposed, so that one word gives a lane its four
+// tiles' scales (block j, token l, tile t at payload end + 64 j + 4 l + t).
+struct Fp4Staged {
+  static constexpr int kSlotBytes = kPayBytes + kScBytes;
+  typedef Fp4Split Q;
+  typedef Fp4Lds Op;
+  template <int NT>
+  struct Regs {
+    typedef uint32_t Vec __attribute__((ext_vector_type(4 * (kPayBytes / 16 / NT))));
+    Vec p;  // one native vector, so the pieces stay in registers
+    uint32_t s;
+  };
+  struct Lane {
+    uint32_t pay, sc;
+  };
+  static __device__ __forceinline__ Lane lane(int li, int lg) {
+    return Lane{(uint32_t)(lg * 1024 + li * 16), (uint32_t)(kPayBytes + lg * 64 + li * 4)};
+  }
+  template <int NT>
+  static __device__ __forceinline__ void fetch(Regs<NT>& r, const uint8_t* __restrict__ payload,
+                                               const uint8_t* __restrict__ scale, int64_t pid, int tid) {
+    const uint8_t* pp = payload + pid * kPayBytes;
+    static_for<kPayBytes / 16 / NT>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      const uint4 v = *reinterpret_cast<const uint4*>(pp + 16 * (tid + NT * m));
+      r.p[4 * m + 0] = v.x;
+      r.p[4 * m + 1] = v.y;
+      r.p[4 * m + 2] = v.z;
+      r.p[4 * m + 3] = v.w;
+    });
+    if (tid < 64) r.s = *reinterpret_cast<const uint32_t*>(scale + pid * kScBytes + 4 * tid);
+  }
+  // Scale word t holds block j = t/16, tokens 4*(t%16) + b; token 16*tile + l's
+  // byte goes to [j][l][tile].
+  template <int NT>
+  static __device__ __forceinline__ void stage(const Regs<NT>& r, uint8_t* slot, int tid) {
+    static_for<kPayBytes / 16 / NT>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      *reinterpret_cast<uint4*>(slot + 16 * (tid + NT * m)) =
+          make_uint4(r.p[4 * m + 0], r.p[4 * m + 1], r.p[4 * m + 2], r.p[4 * m + 3]);
+    });
+    if (tid < 64) {
+      uint8_t* d = slot + kPayBytes + (tid >> 4) * 64 + ((tid & 15) >> 2);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) d[(4 * (tid & 3) + b) * 4] = (uint8_t)(r.s >> (8 * b));
+    }
+  }
+  template <int SLOT>
+  static __device__ __forceinline__ Fp4Lds::Page read(const uint8_t* ring, const Lane& l) {
+    Fp4Lds::Page pg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pg.b[t] = *reinterpret_cast<const uint4*>(ring + l.pay + SLOT + 256 * t);
+    pg.s = *reinterpret_cast<const uint32_t*>(ring + l.sc + SLOT);
+    return pg;
+  }
 };
 
-template <int NT, int NPAY>
-__device__ __forceinline__ void fetch_shared_page(SharedPageRegs<NPAY>& r, const uint8_t* __restrict__ payload,
-                                                  const uint8_t* __restrict__ scale, int64_t pid, int tid) {
-  const uint8_t* pp = payload + pid * kPayBytes;
-  static_for<NPAY>([&](auto mc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value;
-    const uint4 v = *reinterpret_cast<const uint4*>(pp + 16 * (tid + NT * m));
-    r.p[4 * m + 0] = v.x;
-    r.p[4 * m + 1] = v.y;
-    r.p[4 * m + 2] = v.z;
-    r.p[4 * m + 3] = v.w;
-  });
-  if (tid < 64) r.s = *reinterpret_cast<const uint32_t*>(scale + pid * kScBytes + 4 * tid);
-}
-
-// registers -> an LDS slot.  Scale word t holds block j = t/16, tokens
-// 4*(t%16) + b; token 16*tile + l's byte goes to [j][l][tile], so a lane's
-// four tiles' scales are one word.
-template <int NT, int NPAY>
-__device__ __forceinline__ void stage_shared_page(const SharedPageRegs<NPAY>& r, uint8_t* slot, int tid) {
-  static_for<NPAY>([&](auto mc) __attribute__((always_inline)) {
-    constexpr int m = decltype(mc)::value;
-    *reinterpret_cast<uint4*>(slot + 16 * (tid + NT * m)) =
-        make_uint4(r.p[4 * m + 0], r.p[4 * m + 1], r.p[4 * m + 2], r.p[4 * m + 3]);
-  });
-  if (tid < 64) {
-    uint8_t* d = slot + kPayBytes + (tid >> 4) * 64 + ((tid & 15) >> 2);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) d[(4 * (tid & 3) + b) * 4] = (uint8_t)(r.s >> (8 * b));
+// An FP8 page staged in LDS: Fp8Fused's operands (lane (token li, K group lg)
+// holds code bytes 32 lg .. 32 lg + 31 of token 16 t + li in tile t) with
+// the same bytes in the same K slots, so every logit is computed by the same
+// operations.
+struct Fp8Lds {
+  struct Page {
+    v8i b[4];
+    uint32_t s;  // byte t: tile t's scale byte for the lane's token
+  };
+  typedef v8i QOp;
+  template <int OPA>
+  static __device__ __forceinline__ v4f mfma(const QOp& a, const Page& p, int t, uint32_t sa) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    switch (t) {  // t is a compile-time constant at every call
+      case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, p.b[0], z, 0, 0, OPA, (int)sa, 0, (int)p.s);
+      case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, p.b[1], z, 0, 0, OPA, (int)sa, 1, (int)p.s);
+      case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, p.b[2], z, 0, 0, OPA, (int)sa, 2, (int)p.s);
+      default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, p.b[3], z, 0, 0, OPA, (int)sa, 3, (int)p.s);
+    }
   }
-}
+};
+
+// FP8 (fused pool): the page's 8,192 code bytes (64 token rows of 128) are
+// fetched in pool order, 16 bytes per piece, and each piece is written to
+// where a lane reads it: piece c is token c/8, bytes 16 (c%8) .., i.e. half
+// h = c%2 of group lg = (c%8)/2 of token li = (c/8)%16 in tile t = c/128,
+// stored at t*2048 + h*1024 + 16 (16 lg + (li ^ (4 lg + 2 h))).  Within one
+// 16-byte column the 16 lanes of a group lg read one contiguous 256-byte
+// row (the xor permutes it), and the 16 consecutive pieces of two tokens
+// land in 16 different 16-byte bank groups (li ^ (4 lg + 2 h) runs over all
+// 16 values for li in {2i, 2i+1}), so neither the writes nor the reads
+// collide on a bank.  After the codes, word li byte t = the exponent byte of
+// token 16 t + li's fp32 scale (a power of two: the MFMA's E8M0 scale).
+struct Fp8Staged {
+  static constexpr int kCodeBytes = 8192, kPageBytes = 8448;
+  static constexpr int kSlotBytes = kCodeBytes + 64;
+  typedef Fp8Fused Q;
+  typedef Fp8Lds Op;
+  template <int NT>
+  struct Regs {
+    typedef uint32_t Vec __attribute__((ext_vector_type(4 * (kCodeBytes / 16 / NT))));
+    Vec c;  // one native vector, so the pieces stay in registers
+    uint32_t s;
+  };
+  struct Lane {
+    uint32_t h0, h1, sc;
+  };
+  static __device__ __forceinline__ Lane lane(int li, int lg) {
+    return Lane{(uint32_t)(16 * (16 * lg + (li ^ (4 * lg)))), (uint32_t)(1024 + 16 * (16 * lg + (li ^ (4 * lg + 2)))),
+                (uint32_t)(kCodeBytes + 4 * li)};
+  }
+  template <int NT>
+  static __device__ __forceinline__ void fetch(Regs<NT>& r, const uint8_t* __restrict__ pool, const uint8_t*,
+                                               int64_t pid, int tid) {
+    const uint8_t* pp = pool + pid * kPageBytes;
+    static_for<kCodeBytes / 16 / NT>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      const uint4 v = *reinterpret_cast<const uint4*>(pp + 16 * (tid + NT * m));
+      r.c[4 * m + 0] = v.x;
+      r.c[4 * m + 1] = v.y;
+      r.c[4 * m + 2] = v.z;
+      r.c[4 * m + 3] = v.w;
+    });
+    if (tid < 64) r.s = *reinterpret_cast<const uint32_t*>(pp + kCodeBytes + 4 * tid);
+  }
+  template <int NT>
+  static __device__ __forceinline__ void stage(const Regs<NT>& r, uint8_t* slot, int tid) {
+    static_for<kCodeBytes / 16 / NT>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      const int c = tid + NT * m;
+      const int li = (c >> 3) & 15, lg = (c >> 1) & 3, h = c & 1, t = c >> 7;
+      *reinterpret_cast<uint4*>(slot + t * 2048 + h * 1024 + 16 * (16 * lg + (li ^ (4 * lg + 2 * h)))) =
+          make_uint4(r.c[4 * m + 0], r.c[4 * m + 1], r.c[4 * m + 2], r.c[4 * m + 3]);
+    });
+    if (tid < 64) slot[kCodeBytes + 4 * (tid & 15) + (tid >> 4)] = (uint8_t)((r.s >> 23) & 0xFFu);
+  }
+  template <int SLOT>
+  static __device__ __forceinline__ Fp8Lds::Page read(const uint8_t* ring, const Lane& l) {
+    Fp8Lds::Page pg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      pg.b[t] = Fp8Fused::join(*reinterpret_cast<const uint4*>(ring + l.h0 + SLOT + 2048 * t),
+                               *reinterpret_cast<const uint4*>(ring + l.h1 + SLOT + 2048 * t));
+    pg.s = *reinterpret_cast<const uint32_t*>(ring + l.sc + SLOT);
+    return pg;
+  }
+};
 
 // LDS of a shared-page work-group: two page slots, the chunk's page ids and
 // the block's context lengths.
-template <int ROWS>
+template <typename SF, int ROWS>
 struct SharedLds {
-  __attribute__((aligned(16))) uint8_t ring[2][kPayBytes + kScBytes];
+  __attribute__((aligned(16))) uint8_t ring[2][SF::kSlotBytes];
   int32_t pid[kSharedMaxChunk];
   int32_t ctx[ROWS];
 };
@@ -349,8 +464,8 @@ struct SharedArgs {
   const uint8_t* scale;
   int64_t num_pages;
   int32_t bt_stride;
-  const uint8_t* q_fp4;
-  const uint8_t* q_scale;
+  const uint8_t* q;        // packed Q (FP4 codes or FP8 codes)
+  const uint8_t* q_scale;  // its scales (FP4: UE8M0 bytes; FP8: fp32 powers of two)
   const float* w;
   float* logits;
   int64_t logits_stride;
@@ -364,14 +479,13 @@ struct SharedArgs {
 // item's LDS use).
 // tid is the thread's index in the work-group; rot picks which waves take a
 // block's extra rows.
-template <int NW, int RW, int NMT>
-__device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedArgs& a, int req, int row0,
+template <typename SF, int NW, int RW, int NMT>
+__device__ __forceinline__ void shared_item(SharedLds<SF, NW * RW>& L, const SharedArgs& a, int req, int row0,
                                             int nrows, int pb, int n_max, int tid, int rot) {
   constexpr int NT = NW * 64;
   constexpr int H = NMT * 16;
   constexpr int NSC = (NMT + 3) / 4;
   constexpr int ROWS = NW * RW;
-  constexpr int NPAY = 256 / NT;  // 16-byte payload pieces per thread and page
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int li = lane & 15, lg = lane >> 4;
@@ -402,7 +516,7 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
   const int nr = base + (slot < extra ? 1 : 0);  // wave-uniform, <= RW
   const int first = slot * base + min(slot, extra);  // the wave's first row within the block
   const int wrow0 = row0 + first;
-  uint4 aq[RW][NMT];
+  typename SF::Op::QOp aq[RW][NMT];
   uint32_t asc[RW][NSC];
   float wv[RW][NMT][4];
 #pragma unroll
@@ -413,8 +527,8 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int64_t hrow = (int64_t)row * H + mt * 16 + li;
-      aq[r][mt] = *reinterpret_cast<const uint4*>(a.q_fp4 + hrow * 64 + lg * 16);
-      asc[r][mt >> 2] |= (uint32_t)a.q_scale[hrow * 4 + lg] << (8 * (mt & 3));
+      aq[r][mt] = SF::Q::load_q(a.q, hrow, lg);
+      asc[r][mt >> 2] |= SF::Q::q_scale_byte(a.q_scale, hrow, lg) << (8 * (mt & 3));
       const float4 w4 = *reinterpret_cast<const float4*>(a.w + (int64_t)row * H + mt * 16 + lg * 4);
       wv[r][mt][0] = w4.x;
       wv[r][mt][1] = w4.y;
@@ -444,38 +558,35 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
   }
 
   // page bytes in flight: two register sets, used in turn
-  SharedPageRegs<NPAY> set0, set1;
+  typename SF::template Regs<NT> set0, set1;
   // a lane's B operand bytes and scale word within an LDS slot; the slot and
   // the tile are compile-time offsets on top (immediate offsets of the LDS
   // reads, so both slots share the lane's address registers)
   const uint8_t* ring = &L.ring[0][0];
-  const uint32_t pay_off = lg * 1024 + li * 16, sc_off = kPayBytes + lg * 64 + li * 4;
+  const typename SF::Lane lo = SF::lane(li, lg);
   auto score = [&](auto sc, int i) __attribute__((always_inline)) {
-    constexpr int slot = decltype(sc)::value * (kPayBytes + kScBytes);
+    constexpr int slot = decltype(sc)::value * SF::kSlotBytes;
     if (nr == 0) return;  // wave-uniform: a wave past the block's rows only loads
-    Fp4Lds::Page pg;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) pg.b[t] = *reinterpret_cast<const uint4*>(ring + pay_off + slot + 256 * t);
-    pg.s = *reinterpret_cast<const uint32_t*>(ring + sc_off + slot);
+    const typename SF::Op::Page pg = SF::template read<slot>(ring, lo);
     static_for<RW>([&](auto rc) __attribute__((always_inline)) {
       constexpr int r = decltype(rc)::value;
       if (r < nr) {
-        const float tot = row_page_logits<Fp4Lds, NMT, false>(aq[r], asc[r], wv[r], pg);
+        const float tot = row_page_logits<typename SF::Op, NMT, false>(aq[r], asc[r], wv[r], pg);
         if (lane + i * 64 < lim[r]) store_logit(rowp[r] + lane + i * 64, tot);
       }
     });
   };
-  fetch_shared_page<NT>(set0, a.payload, a.scale, L.pid[0], tid);
-  if (n > 1) fetch_shared_page<NT>(set1, a.payload, a.scale, L.pid[1], tid);
+  SF::template fetch<NT>(set0, a.payload, a.scale, L.pid[0], tid);
+  if (n > 1) SF::template fetch<NT>(set1, a.payload, a.scale, L.pid[1], tid);
   for (int i = 0; i < n; i += 2) {
-    stage_shared_page<NT>(set0, L.ring[0], tid);
+    SF::template stage<NT>(set0, L.ring[0], tid);
     __syncthreads();
-    if (i + 2 < n) fetch_shared_page<NT>(set0, a.payload, a.scale, L.pid[i + 2], tid);
+    if (i + 2 < n) SF::template fetch<NT>(set0, a.payload, a.scale, L.pid[i + 2], tid);
     score(std::integral_constant<int, 0>{}, i);
     if (i + 1 < n) {
-      stage_shared_page<NT>(set1, L.ring[1], tid);
+      SF::template stage<NT>(set1, L.ring[1], tid);
       __syncthreads();
-      if (i + 3 < n) fetch_shared_page<NT>(set1, a.payload, a.scale, L.pid[i + 3], tid);
+      if (i + 3 < n) SF::template fetch<NT>(set1, a.payload, a.scale, L.pid[i + 3], tid);
       score(std::integral_constant<int, 1>{}, i + 1);
     }
   }
@@ -483,11 +594,11 @@ __device__ __forceinline__ void shared_item(SharedLds<NW * RW>& L, const SharedA
 
 // Host-bounded grid: (page chunk, row block, request), each request's chunks
 // rotated across the XCDs as in mqa_logits_kernel.
-template <int NW, int RW, int NMT>
+template <typename SF, int NW, int RW, int NMT>
 __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(SharedArgs a, const int32_t* __restrict__ indptr,
                                                                     int32_t chunk_pages, int32_t n_rows) {
   constexpr int ROWS = NW * RW;
-  __shared__ SharedLds<ROWS> L;
+  __shared__ SharedLds<SF, ROWS> L;
   const int n_chunks = gridDim.x;
   const int req = blockIdx.z;
   int rot = req & 7;
@@ -499,7 +610,7 @@ __global__ __launch_bounds__(NW * 64) void mqa_logits_shared_kernel(SharedArgs a
   const int row0 = ip0 + (int)blockIdx.y * ROWS;
   const int nrows = max(0, min(ROWS, ip1 - row0));
   if (nrows == 0) return;  // the whole work-group
-  shared_item<NW, RW, NMT>(L, a, req, row0, nrows, chunk * chunk_pages, chunk_pages, threadIdx.x,
+  shared_item<SF, NW, RW, NMT>(L, a, req, row0, nrows, chunk * chunk_pages, chunk_pages, threadIdx.x,
                            (int)(blockIdx.x + blockIdx.y));
 }
 
@@ -514,7 +625,7 @@ mqa_logits_planned_kernel(SharedArgs a, int32_t n_reqs, int32_t n_rows,
                                                                      const int4* __restrict__ items,
                                                                      int32_t cap_items) {
   constexpr int ROWS = NW * RW;
-  __shared__ SharedLds<ROWS> L;
+  __shared__ SharedLds<Fp4Staged, ROWS> L;
   const int item = blockIdx.x;
   // the item is read with the header (the grid never exceeds the capacity)
   const int4 iv = items[min(item, cap_items - 1)];  // the same for the whole work-group: scalar registers
@@ -528,7 +639,7 @@ mqa_logits_planned_kernel(SharedArgs a, int32_t n_reqs, int32_t n_rows,
       (int64_t)pb + n_max > a.bt_stride)
     return;
   if (it.y < 0 || it.y + nrows > n_rows) return;  // rows inside the call's rows
-  shared_item<NW, RW, NMT>(L, a, req, it.y, nrows, pb, n_max, threadIdx.x, item);
+  shared_item<Fp4Staged, NW, RW, NMT>(L, a, req, it.y, nrows, pb, n_max, threadIdx.x, item);
 }
 
 // The arguments of one logits call, as the launchers pass them down.
@@ -552,7 +663,7 @@ struct LogitsCall {
   hipStream_t stream;
 };
 
-template <int NW, int RW, int NMT>
+template <typename SF, int NW, int RW, int NMT>
 static hipError_t launch_shared(const LogitsCall& c, int page_rows) {
   constexpr int ROWS = NW * RW;
   const int64_t pages = (c.max_ctx + 63) / 64;
@@ -573,7 +684,7 @@ static hipError_t launch_shared(const LogitsCall& c, int page_rows) {
   if (chunks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const SharedArgs a{c.block_table, c.row_ctx, c.payload, c.scale, c.num_pages, c.bt_stride,
                      c.q, c.q_scale, c.w, c.logits, c.logits_stride};
-  return launch(mqa_logits_shared_kernel<NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)c.n_reqs),
+  return launch(mqa_logits_shared_kernel<SF, NW, RW, NMT>, dim3((unsigned)chunks, (unsigned)blocks, (unsigned)c.n_reqs),
                 dim3(NW * 64), 0, c.stream, a, c.indptr, (int32_t)chunk_pages, c.n_rows);
 }
 
@@ -625,11 +736,26 @@ template <int NMT>
 static hipError_t launch_fp4_shared(const LogitsCall& c, bool uniform) {
   const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 4;
   const int r = c.max_rows_per_req;
-  if (!uniform || r <= 4) return launch_shared<2, 2, NMT>(c, page_rows);
+  if (!uniform || r <= 4) return launch_shared<Fp4Staged, 2, 2, NMT>(c, page_rows);
   if constexpr (NMT <= 4) {
-    if (r <= 6) return launch_shared<2, 3, NMT>(c, page_rows);
+    if (r <= 6) return launch_shared<Fp4Staged, 2, 3, NMT>(c, page_rows);
   }
-  return launch_shared<4, 2, NMT>(c, page_rows);
+  return launch_shared<Fp4Staged, 4, 2, NMT>(c, page_rows);
+}
+
+// FP8 batches of requests with three or more rows each on average: the
+// shared-page kernel with the FP8 pages staged in LDS (Fp8Staged).  The
+// shapes follow the FP4 rule with the FP8 operands' register cost: NW waves
+// of RW rows (FP4IDX_FP8_SHARED_SHAPE = NW * 10 + RW in measurement builds).
+#ifndef FP4IDX_FP8_SHARED_SHAPE
+#define FP4IDX_FP8_SHARED_SHAPE 41
+#endif
+template <int NMT>
+static hipError_t launch_fp8_shared(const LogitsCall& c, bool uniform) {
+  const int page_rows = uniform ? kSharedPageRows : kSharedPageRows / 4;
+  constexpr int NW = FP4IDX_FP8_SHARED_SHAPE / 10, RW = NMT > 4 ? 1 : FP4IDX_FP8_SHARED_SHAPE % 10;
+  if (!uniform) return launch_shared<Fp8Staged, 2, 2 < RW ? 2 : RW, NMT>(c, page_rows);
+  return launch_shared<Fp8Staged, NW, RW, NMT>(c, page_rows);
 }
 
 hipError_t launch_mqa_logits_bounded(const uint8_t* q_fp4, const uint8_t* q_scale, const float* w, int64_t n_rows,
@@ -806,7 +932,12 @@ hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, con
   const LogitsCall c{q_fp8,       reinterpret_cast<const uint8_t*>(q_scale), w, indptr, n_reqs, (int32_t)n_rows,
                      row_ctx,     block_table, bt_stride, pool, pool, num_pages, logits, logits_stride,
                      max_rows_per_req, max_ctx, stream};
-  return launch_heads<Fp8Fused>(c, n_heads);
+  // as for the FP4 cache: the shared-page kernel from three rows per request
+  // on average (both kernels give the same bits)
+  const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
+  const int64_t avg_rows = n_reqs > 0 ? (n_rows + n_reqs - 1) / n_reqs : 0;
+  if (max_rows_per_req <= 2 || avg_rows < 3) return launch_heads<Fp8Fused>(c, n_heads);
+  return with_head_tiles(n_heads, [&](auto nmt) { return launch_fp8_shared<decltype(nmt)::value>(c, uniform); });
 }
 
 }  // namespace fp4idx

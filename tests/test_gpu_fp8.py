@@ -330,6 +330,56 @@ def test_logits_fp8_invariant_to_pages_and_batch(F, orc):
                           np.nan_to_num(alone, nan=7.0).view(np.uint32))
 
 
+def _bits(x):
+    return np.nan_to_num(x, nan=7.0).view(np.uint32)
+
+
+@pytest.mark.parametrize("heads", [64, 128, 32])
+def test_logits_fp8_same_bits_from_every_kernel(F, orc, heads):
+    """A 16-row request (shared-page kernel: the FP8 pages staged in LDS,
+    several page chunks) gives the same bits as its rows scored one per
+    request (per-wave kernel, one row per wave), as the same request next to
+    a one-row request (a non-uniform batch: shared-page kernel, two rows per
+    work-group, short chunks) and as the same request next to fifteen
+    one-row requests (under three rows per request on average: per-wave
+    kernel, several rows per wave); sampled scores against the oracle."""
+    rng = np.random.default_rng([23, heads])
+    ctx = 20_000 if heads == 64 else 5_000  # 313 pages: many page chunks
+    pages = (ctx + 63) // 64
+    pool = W.random_pool_fp8(rng, pages + 3)
+    qf, qs, w = W.random_q_fp8(rng, 16, heads=heads)
+    table = rng.permutation(pages + 3)[:pages].astype(np.int32)[None, :]
+    row_ctx = (ctx - np.arange(16)[::-1] * 7).astype(np.int32)
+    row_ctx[3] = 0
+
+    def run(q, qsc, wt, ind, cx, bt, mr):
+        o = torch.full((q.shape[0], ctx), float("nan"), dtype=torch.float32, device=DEV)
+        F.mqa_logits_fp8(dev(q), dev(qsc), dev(wt), dev(ind), dev(cx), dev(bt), dev(pool), mr, ctx, logits=o)
+        torch.cuda.synchronize()
+        return o.cpu().numpy()
+
+    say("fp8 kernels", heads, "heads")
+    a = run(qf, qs, w, np.array([0, 16], np.int32), row_ctx, table, 16)
+    one = run(qf, qs, w, np.arange(17, dtype=np.int32), row_ctx, np.repeat(table, 16, axis=0), 1)
+    m = run(np.concatenate([qf, qf[:1]]), np.concatenate([qs, qs[:1]]), np.concatenate([w, w[:1]]),
+            np.array([0, 16, 17], np.int32), np.concatenate([row_ctx, row_ctx[:1]]), np.repeat(table, 2, axis=0),
+            16)
+    pick = np.concatenate([np.arange(16), np.arange(15)])
+    few = run(qf[pick], qs[pick], w[pick], np.concatenate([[0], np.arange(16, 32)]).astype(np.int32), row_ctx[pick],
+              np.repeat(table, 16, axis=0), 16)
+    for x in (one, m[:16], few[:16]):
+        assert np.array_equal(_bits(a), _bits(x))
+    assert np.array_equal(_bits(a[:1]), _bits(m[16:])) and np.array_equal(_bits(a[:15]), _bits(few[16:]))
+    live = np.nonzero(row_ctx > 0)[0]
+    rows = live.repeat(40)
+    toks = (rng.random(rows.size) * row_ctx[rows]).astype(np.int64)
+    f64, T, A, B = orc.logits_fp8_sampled(qf, qs, w, np.array([0, 16], np.int32), table, pool, rows, toks,
+                                          want_b16=True)
+    check_fp8(a[rows, toks], f64, T, A, B, f"fp8 16-row request, {heads} heads (sampled)")
+    cols = np.arange(ctx)[None, :]
+    assert np.all(np.isnan(a[cols >= row_ctx[:, None]])) and not np.any(np.isnan(a[cols < row_ctx[:, None]]))
+
+
 def test_logits_fp8_context_past_the_row_is_cut(F, orc):
     """A device context length beyond the logits row (a broken contract) is
     cut by the kernel to the row: the next row's entries stay untouched."""

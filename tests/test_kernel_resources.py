@@ -66,15 +66,16 @@ def test_register_budgets_the_launch_shapes_rely_on():
     waves) shares a CU with a second row only at <= 128 registers per lane
     (four waves per SIMD), and the shared-page logits kernel's 4 x 2 shape was
     picked for four waves per SIMD as well (and its scheduled form, which
-runs the same body on the plan's items)."""
+    runs the same body on the plan's items), as was the FP8 shared-page
+    kernel's 4 x 1 shape."""
     if not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
     srcs = [s for s in build.sources() if os.path.basename(s) in ("topk.hip", "logits.hip")]
     with tempfile.TemporaryDirectory() as d:
         regs = dict(kv for s in srcs for kv in _vgprs(_assemble(s, d)))
     want = {n: r for n, r in regs.items()
-            if "topk_reg_kernelILi512E" in n or "mqa_logits_shared_kernelILi4ELi2ELi4E" in n
-            or "mqa_logits_planned_kernelILi4ELi2ELi4E" in n}
-    assert len(want) >= 7, sorted(regs)
+            if "topk_reg_kernelILi512E" in n or "mqa_logits_shared_kernelINS_9Fp4StagedELi4ELi2ELi4E" in n
+            or "mqa_logits_planned_kernelILi4ELi2ELi4E" in n or "mqa_logits_shared_kernelINS_9Fp8StagedELi4ELi1ELi4E" in n}
+    assert len(want) >= 8, sorted(regs)
     over = {n: r for n, r in want.items() if r > 128}
     assert not over, over
