@@ -932,10 +932,25 @@ hipError_t launch_mqa_logits_fp8(const uint8_t* q_fp8, const float* q_scale, con
   const LogitsCall c{q_fp8,       reinterpret_cast<const uint8_t*>(q_scale), w, indptr, n_reqs, (int32_t)n_rows,
                      row_ctx,     block_table, bt_stride, pool, pool, num_pages, logits, logits_stride,
                      max_rows_per_req, max_ctx, stream};
-  // as for the FP4 cache: the shared-page kernel from three rows per request
-  // on average (both kernels give the same bits)
+  // Pages are staged through LDS whenever the batch allows: an FP8 token's
+  // 128 code bytes are one row of the page, so a lane's direct operand loads
+  // (Fp8Fused) read half lines of sixteen rows per instruction, while staging
+  // reads the page in whole lines (decode batch 64: 32.4 -> 23.0 us).  One or
+  // two rows per request: one-wave work-groups, each staging its own pages;
+  // three or more on average: the shared-page shapes above; in between (a few
+  // long requests among one-row ones) the per-wave kernel, several rows per
+  // wave.  Every kernel gives the same bits.
   const bool uniform = 4 * n_rows >= 3 * (int64_t)max_rows_per_req * n_reqs;
   const int64_t avg_rows = n_reqs > 0 ? (n_rows + n_reqs - 1) / n_reqs : 0;
+#ifndef FP4IDX_FP8_WAVE_STAGED  // 0 in measurement builds: the per-wave kernel for one or two rows
+#define FP4IDX_FP8_WAVE_STAGED 1
+#endif
+  if (FP4IDX_FP8_WAVE_STAGED && max_rows_per_req <= 2)
+    return with_head_tiles(n_heads, [&](auto nmt) {
+      constexpr int NMT = decltype(nmt)::value;
+      if (max_rows_per_req <= 1) return launch_shared<Fp8Staged, 1, 1, NMT>(c, kSharedPageRows);
+      return launch_shared<Fp8Staged, 1, 2, NMT>(c, kSharedPageRows);
+    });
   if (max_rows_per_req <= 2 || avg_rows < 3) return launch_heads<Fp8Fused>(c, n_heads);
   return with_head_tiles(n_heads, [&](auto nmt) { return launch_fp8_shared<decltype(nmt)::value>(c, uniform); });
 }

@@ -338,11 +338,12 @@ def _bits(x):
 def test_logits_fp8_same_bits_from_every_kernel(F, orc, heads):
     """A 16-row request (shared-page kernel: the FP8 pages staged in LDS,
     several page chunks) gives the same bits as its rows scored one per
-    request (per-wave kernel, one row per wave), as the same request next to
-    a one-row request (a non-uniform batch: shared-page kernel, two rows per
-    work-group, short chunks) and as the same request next to fifteen
-    one-row requests (under three rows per request on average: per-wave
-    kernel, several rows per wave); sampled scores against the oracle."""
+    request (one-wave work-groups staging their own pages), as the same
+    request next to a one-row request (a non-uniform batch: shared-page
+    kernel, two rows per work-group, short chunks) and as the same request
+    next to fifteen one-row requests (under three rows per request on
+    average: per-wave kernel with direct operand loads, several rows per
+    wave); sampled scores against the oracle."""
     rng = np.random.default_rng([23, heads])
     ctx = 20_000 if heads == 64 else 5_000  # 313 pages: many page chunks
     pages = (ctx + 63) // 64
