@@ -65,6 +65,20 @@ __device__ __forceinline__ int plan_scan(int v, int lane, int wave, uint32_t* pa
   return excl;
 }
 
+// Sum of v over the 64 lanes in a fixed order (result uniform): DPP within
+// each 16-lane row, then the four rows' sums in turn.
+__device__ __forceinline__ float plan_wave_sum(float v) {
+  v += __uint_as_float(dppu<kQpXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dppu<kQpXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dppu<kRowHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dppu<kRowMirror>(__float_as_uint(v)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 struct PlanParams {
   const int32_t* indptr;
   int32_t n_reqs;
@@ -86,7 +100,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
   __shared__ uint32_t part[kPlanWaves];
   __shared__ int32_t first_lds[kPlanLdsReqs + 1];
   __shared__ int32_t ip0_lds[kPlanLdsReqs], ip1_lds[kPlanLdsReqs];  // each request's clamped row range
-  __shared__ float s_work;
+  __shared__ float s_wsum[kPlanWaves];  // the waves' sums of their blocks' work
   __shared__ int32_t ctx_lds[kPlanLdsRows];  // the rows' context lengths (batches of up to kPlanLdsRows rows)
   // per-block plans for the coalesced item writer (batches of up to
   // kPlanCoalescedBlocks row blocks): first large and short item, request,
@@ -101,7 +115,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     ip0 = min(max(p.indptr[b], 0), p.n_rows);
     ip1 = min(max(p.indptr[b + 1], ip0), p.n_rows);
   };
-  if (tid == 0) s_work = 0.0f;
   // Every row's context length (cut to the plan's bound), loaded in the
   // same round trip as indptr when the batch has at most kPlanLdsRows rows
   // (the blocks then read them from LDS); stored after pass 1's barriers.
@@ -227,13 +240,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     e.P = (cmax + 63) >> 6;
     work += (float)e.P * (float)(kStagePageCost + busiest_rows(nr) * kRowPageCost);
   });
-  atomicAdd(&s_work, work);
-  __syncthreads();
-  // share of each shared-page block's pages in short chunks
-  const float short_share =
-      p.waves > 0 ? fminf(1.0f, 0.01f * (float)kShortRoundsX100 * (float)p.resident * (float)p.target /
-                                    fmaxf(s_work, 1.0f))
-                  : 0.0f;
+  // share of each shared-page block's pages in short chunks, from the
+  // batch's work summed in a fixed order (within each wave, then the waves
+  // in turn), so that one batch always gets the same plan; per-wave items
+  // (work-group uniform) have no short ones
+  float short_share = 0.0f;
+  if (p.waves > 0) {
+    const float wsum = plan_wave_sum(work);
+    if (lane == 0) s_wsum[wave] = wsum;
+    __syncthreads();
+    float total = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPlanWaves; ++i) total += s_wsum[i];
+    short_share = fminf(1.0f, 0.01f * (float)kShortRoundsX100 * (float)p.resident * (float)p.target /
+                                  fmaxf(total, 1.0f));
+  }
 
   // 3. chunks per block; large items first, then the short ones
   const int chunk_cap = nb > 0 ? max(1, p.cap_items / nb) : 1;
@@ -276,7 +297,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     }
     int tb = 0, ts = 0;
     e.fb = n_big + plan_scan(nbig, lane, wave, part, tb);
-    e.fs = n_small + plan_scan(nsmall, lane, wave, part, ts);
+    e.fs = n_small + (p.waves > 0 ? plan_scan(nsmall, lane, wave, part, ts) : 0);  // per-wave items: no short ones
     n_big += tb;
     n_small += ts;
   });
