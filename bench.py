@@ -73,8 +73,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _strip_c_comments(text: str) -> str:
+    """C/C++ source without its comments (string and character literals kept
+    whole): each comment replaced by one space, trailing spaces and blank
+    lines dropped."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).split("\n") if line.strip())
+
+
 def kernel_source_hash() -> str:
-    """Digest of everything the kernels are compiled from (HIP sources, headers, build flags)."""
+    """Digest of everything the kernels are compiled from (HIP sources and
+    headers without their comments, build flags): the key of the stored
+    counter readings, which a change of the compiled code makes stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_fp4_fp4idx_amd", "csrc")
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
@@ -82,7 +111,10 @@ def kernel_source_hash() -> str:
     for f in files:
         if os.path.isfile(f):
             h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+            data = open(f, "rb").read()
+            if f.endswith((".hip", ".hpp", ".h")):
+                data = _strip_c_comments(data.decode()).encode()
+            h.update(data)
     return h.hexdigest()[:16]
 
 

@@ -17,13 +17,16 @@
 //   Every wave keeps its rows' packed Q (the MFMA A operand) and head weights
 //   in registers and streams K pages: per 16-token tile each lane loads 16
 //   payload bytes (one 128-bit load; the 64 lanes read 4 runs of 256 B) and
-//   one scale byte (FP8: 32 code bytes in two 128-bit loads, the 16 tokens'
-//   2 KB contiguous, and a scale word), straight into the B operand.  D
-//   pages are in flight per wave; the page ids and Q are requested before
-//   the context lengths arrive so the prologue costs one memory latency less.
+//   one scale byte (Fp8Fused: 32 code bytes in two 128-bit loads, and a
+//   scale word), straight into the B operand.  D pages are in flight per
+//   wave; the page ids and Q are requested before the context lengths
+//   arrive so the prologue costs one memory latency less.
 //   Batches with three or more rows per request on average (either cache)
 //   use mqa_logits_shared_kernel instead: its waves split a block of rows
-//   and share each page through LDS (see that kernel).
+//   and share each page through LDS (see that kernel); FP8 batches of one or
+//   two rows per request use it too, with one-wave work-groups, because an
+//   FP8 token's code bytes are one 128-byte row and direct operand loads
+//   would read half lines.
 //
 // MFMA mapping for FP4 (V_MFMA_SCALE_F32_16X16X128_F8F6F4, both operands
 // e2m1; FP8 in Fp8Fused below):
@@ -35,8 +38,8 @@
 //   the page layout feeds the MFMA without any shuffle.
 //   D (16 x 16, fp32): lane l holds token l%16, heads 4*(l/16)+i, i = 0..3.
 // Epilogue per lane and row: for each of the page's 4 tiles, p_t = sum over
-// the row's M-tiles and i of w * ReLU(d) (two fixed-order chains: even and
-// odd M-tiles), then the four lane groups of the four tiles are summed
+// the row's M-tiles and i of w * ReLU(d) (one fixed-order FMA chain), then
+// the four lane groups of the four tiles are summed
 // together with two permlane swap steps that leave tile t's total for token
 // l%16 in lane 16*t + l%16, i.e. the page's 64 logits in lane order, stored
 // as one 256-byte row segment.
