@@ -19,8 +19,9 @@
 //     before it in (value descending, position ascending) order; its bit joins
 //     the masks.  Otherwise exact key-space rounds find the K-th largest value
 //     T and the masks hold value > T and the first ties of value == T.
-//  3. Ordered compaction: thread t owns the 32 positions of mask word t, one
-//     block scan of the popcounts gives its output offset.
+//  3. Ordered compaction: thread t owns the J consecutive positions J t ..
+//     J t + J - 1 of the bit masks, one block scan of the popcounts gives
+//     its output offset.
 // Longer rows (topk_long_kernel) re-read the logits in each pass, with four
 // waves per row and ballot-based compaction.
 #include "launch.hpp"
