@@ -261,6 +261,22 @@ def test_logits_fp8_rows_per_request_variants(F, orc):
         assert np.all(np.isnan(gpu[~in_context(wl.row_ctx, gpu.shape[1])]))
 
 
+@pytest.mark.parametrize("heads,rows", [(16, (1, 1, 1)), (48, (2, 1, 2)), (80, (1, 1)), (128, (2, 2, 1)),
+                                       (112, (1, 2))])
+def test_logits_fp8_one_wave_staging_every_head_count(F, orc, heads, rows):
+    """One or two rows per request: one-wave work-groups that stage their
+    own FP8 pages through LDS, at every M-tile count; ragged contexts (a
+    partial last page, a zero-context row, a context under one page)."""
+    ctxs = tuple((70, 0, 700, 130, 1)[: len(rows)])
+    wl = W.small(seed=heads + sum(rows), rows=rows, ctxs=ctxs, heads=heads)
+    qf, qs, w, pool = _encoded_small(orc, wl)
+    gpu = _gpu_logits(F, qf, qs, w, wl, pool)
+    _, f64, T, A, B = orc.logits_fp8(qf, qs, w, wl.req_row_indptr, wl.row_ctx, wl.block_table, pool,
+                                     logits_stride=gpu.shape[1], want_f64=True, want_b16=True)
+    check_rows(gpu, f64, T, A, B, wl.row_ctx, f"fp8 one-wave staging, {heads} heads, rows {rows}")
+    assert np.all(np.isnan(gpu[~in_context(wl.row_ctx, gpu.shape[1])]))
+
+
 def test_logits_fp8_128_heads_many_rows(F, orc):
     """128 heads with more than two rows per request (the row cap for the
     wide FP8 operands)."""
