@@ -208,6 +208,37 @@ def test_one_plan_serves_every_layer(F, orc):
     assert torch.equal(plan.workspace, built)
 
 
+@pytest.mark.parametrize("rows,ctxs", [((3, 8, 1, 12), (5000, 2200, 700, 4100)),   # shared-page items
+                                       ((1,) * 40, tuple(1000 + 613 * i for i in range(40))),  # per-wave
+                                       ((9, 16, 5, 2, 14, 7), (30000, 9000, 17000, 4000, 26000, 12000))])
+def test_a_batch_always_gets_the_same_plan(F, rows, ctxs):
+    """Building the plan of one batch again, into fresh and into reused
+    workspaces, gives the same workspace bytes every time: the batch's work
+    (which sizes the short items) is summed in a fixed order, so nothing in
+    the plan depends on the order the device happens to run its threads."""
+    wl = W.small(seed=sum(rows), rows=rows, ctxs=ctxs)
+    ind, ctx = dev(wl.req_row_indptr), dev(wl.row_ctx)
+
+    def defined(ws):
+        """What a plan defines: the header's words, the per-request list and
+        the items up to the item count (the per-block list is the plan's
+        own scratch, and the rest of a fresh workspace is never written)."""
+        w = ws.cpu().numpy().view(np.int32)
+        _, items_off = layout(wl.n_rows, wl.n_reqs, int(w[4]))
+        req = w[HDR_WORDS:HDR_WORDS + wl.n_reqs + 1]
+        return np.concatenate([w[:7], req, w[items_off:items_off + 4 * int(w[0])]])
+
+    first = F.LogitsPlan(64, ind, ctx, wl.max_ctx).build()
+    torch.cuda.synchronize()
+    ref = defined(first.workspace)
+    _check_schedule(first.workspace, wl.req_row_indptr, wl.row_ctx, wl.max_ctx, wl.n_rows)
+    say("plan", rows[:6], "items", int(ref[0]))
+    for rep in range(8):
+        again = F.LogitsPlan(64, ind, ctx, wl.max_ctx).build() if rep % 2 else first.build()
+        torch.cuda.synchronize()
+        assert np.array_equal(defined(again.workspace), ref), rep
+
+
 def test_planned_runs_interleaved_with_other_plans(F, orc):
     """Two batches, each with its own workspace, planned and run alternately
     on one stream (a serving loop with two batches in flight): each run uses
